@@ -1,0 +1,133 @@
+"""Oracle for the W1.58A8 ternary matrix product (Python side).
+
+TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the benchmark's
+CPU-baseline leg may import this package.  It wraps the plain C oracle in
+``oracle.c`` (scalar loops, no HIP) with numpy arrays and shares no code with
+the GPU library.  The functions follow the pages cited in ``oracle.h``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+CFLAGS = ["-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fPIC",
+          "-shared", "-pthread"]
+
+
+def build(force: bool = True) -> str:
+    """Compile oracle.c into liboracle.so with gcc (no HIP involved)."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp"
+        subprocess.check_call(["gcc", *CFLAGS, _SRC, "-o", tmp, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build()
+        L = ctypes.CDLL(_LIB)
+        i64, i32, p = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p
+        L.oracle_ternarize_absmean.argtypes = [p, i64, i64, p, p]
+        L.oracle_ternarize_absmean.restype = i32
+        L.oracle_pack_i2s.argtypes = [p, i64, i64, p]
+        L.oracle_pack_i2s.restype = i64
+        L.oracle_unpack_i2s.argtypes = [p, i64, i64, p]
+        L.oracle_unpack_i2s.restype = i64
+        L.oracle_quant_act.argtypes = [p, i64, i64, p, p]
+        L.oracle_quant_act.restype = i32
+        L.oracle_gemm.argtypes = [p, ctypes.c_float, i64, i64, i64, p, p, p, p,
+                                  i32]
+        L.oracle_gemm.restype = i32
+        _lib = L
+    return _lib
+
+
+def _ptr(a: np.ndarray) -> int:
+    return a.ctypes.data
+
+
+def _c(a, dtype) -> np.ndarray:
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+def ternarize_absmean(w):
+    """O1: fp32 [n, k] -> (int8 trits [n, k], fp32 scale)."""
+    w = _c(w, np.float32)
+    n, k = w.shape
+    t = np.empty((n, k), np.int8)
+    s = np.zeros(1, np.float32)
+    lib().oracle_ternarize_absmean(_ptr(w), n, k, _ptr(t), _ptr(s))
+    return t, np.float32(s[0])
+
+
+def pack_i2s(t):
+    """O2: int8 trits [n, k] -> (uint8 packed [n, k/4], invalid count)."""
+    t = _c(t, np.int8)
+    n, k = t.shape
+    if k % 16:
+        raise ValueError("k must be a multiple of 16")
+    out = np.empty((n, k // 4), np.uint8)
+    bad = lib().oracle_pack_i2s(_ptr(t), n, k, _ptr(out))
+    return out, int(bad)
+
+
+def unpack_i2s(packed, k: int):
+    """O2 inverse: uint8 [n, k/4] -> (int8 trits [n, k], invalid count)."""
+    packed = _c(packed, np.uint8)
+    n = packed.shape[0]
+    if packed.shape[1] * 4 != k:
+        raise ValueError("packed row length does not match k")
+    t = np.empty((n, k), np.int8)
+    bad = lib().oracle_unpack_i2s(_ptr(packed), n, k, _ptr(t))
+    return t, int(bad)
+
+
+def quant_act(x):
+    """O3: fp32 [m, k] -> (int8 q [m, k], fp32 s_a [m])."""
+    x = _c(x, np.float32)
+    if x.ndim == 1:
+        x = x[None, :]
+    m, k = x.shape
+    q = np.empty((m, k), np.int8)
+    s = np.empty(m, np.float32)
+    lib().oracle_quant_act(_ptr(x), m, k, _ptr(q), _ptr(s))
+    return q, s
+
+
+def gemm(packed, s_w, k: int, q, s_a, nthreads: int = 1, rows=None):
+    """O4 + O5: (int32 acc [m, n], float64 y [m, n]).
+
+    ``rows`` = (r0, r1) restricts the product to output rows r0..r1-1 of the
+    packed matrix (used to compute samples at full sizes)."""
+    packed = _c(packed, np.uint8)
+    q = _c(q, np.int8)
+    if q.ndim == 1:
+        q = q[None, :]
+    s_a = _c(np.atleast_1d(s_a), np.float32)
+    if rows is not None:
+        packed = np.ascontiguousarray(packed[rows[0]:rows[1]])
+    n = packed.shape[0]
+    m = q.shape[0]
+    if packed.shape[1] * 4 != k or q.shape[1] != k or s_a.shape[0] != m:
+        raise ValueError("shape mismatch")
+    acc = np.empty((m, n), np.int32)
+    y = np.empty((m, n), np.float64)
+    rc = lib().oracle_gemm(_ptr(packed), float(np.float32(s_w)), n, k, m,
+                           _ptr(q), _ptr(s_a), _ptr(acc), _ptr(y),
+                           int(nthreads))
+    if rc != 0:
+        raise ValueError(f"oracle_gemm failed with {rc}")
+    return acc, y

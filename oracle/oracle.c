@@ -1,0 +1,174 @@
+/*
+ * Oracle for the W1.58A8 ternary matrix product (plain C, scalar loops).
+ * TEST INFRASTRUCTURE ONLY: called by the tests, the smoke check and the
+ * benchmark's CPU-baseline leg.  It shares no code with the HIP library.
+ * Every function states the passage it follows; the header lists the readings
+ * taken where the pages are silent.
+ *
+ * Build: gcc -O2 -std=c11 -ffp-contract=off -fno-fast-math -shared -fPIC
+ *        -pthread (no FMA contraction, IEEE single precision for float).
+ */
+#include "oracle.h"
+
+#include <math.h>
+#include <pthread.h>
+#include <stdlib.h>
+
+/* --- O1: absmean ternarization ------------------------------------------
+ * bitnet.cpp CPU tutorial (m.qwbw.cn), §3.2: the converter projects all
+ * weights onto {-1, 0, +1} by absmean quantization: divide by the mean
+ * absolute value and round to the nearest of the three values. */
+int oracle_ternarize_absmean(const float* w, int64_t n, int64_t k, int8_t* t,
+                             float* s_w) {
+  const int64_t count = n * k;
+  double sum = 0.0;
+  for (int64_t i = 0; i < count; ++i) sum += fabs((double)w[i]);
+  const float gamma = (float)(sum / (double)count);
+  *s_w = gamma;
+  for (int64_t i = 0; i < count; ++i) {
+    if (gamma == 0.0f) {
+      t[i] = 0;
+      continue;
+    }
+    const float scaled = w[i] / gamma;       /* fp32 divide */
+    float r = nearbyintf(scaled);            /* round half to even */
+    if (r > 1.0f) r = 1.0f;
+    if (r < -1.0f) r = -1.0f;
+    t[i] = (int8_t)r;
+  }
+  return 0;
+}
+
+/* --- O2: 2-bit packing ---------------------------------------------------
+ * bitnet.cpp CPU tutorial, §1.1: each ternary weight is stored in 2 bits.
+ * "BitNet 1 位 LLM 独立推理引擎" (conversion paragraph): this generic 2-bit
+ * format is I2_S.  The byte layout is this library's reading (header). */
+static int64_t byte_of(int64_t k) { return 4 * (k / 16) + (k % 4); }
+static int shift_of(int64_t k) { return (int)(2 * ((k % 16) / 4)); }
+
+int64_t oracle_pack_i2s(const int8_t* t, int64_t n, int64_t k,
+                        uint8_t* packed) {
+  const int64_t row_bytes = k / 4;
+  int64_t invalid = 0;
+  for (int64_t i = 0; i < n * row_bytes; ++i) packed[i] = 0;
+  for (int64_t r = 0; r < n; ++r) {
+    for (int64_t c = 0; c < k; ++c) {
+      const int8_t v = t[r * k + c];
+      unsigned code;
+      if (v == -1) code = 0;
+      else if (v == 0) code = 1;
+      else if (v == 1) code = 2;
+      else { code = 3; ++invalid; }
+      packed[r * row_bytes + byte_of(c)] |= (uint8_t)(code << shift_of(c));
+    }
+  }
+  return invalid;
+}
+
+int64_t oracle_unpack_i2s(const uint8_t* packed, int64_t n, int64_t k,
+                          int8_t* t) {
+  const int64_t row_bytes = k / 4;
+  int64_t invalid = 0;
+  for (int64_t r = 0; r < n; ++r) {
+    for (int64_t c = 0; c < k; ++c) {
+      const unsigned code =
+          (packed[r * row_bytes + byte_of(c)] >> shift_of(c)) & 3u;
+      if (code == 3) { ++invalid; t[r * k + c] = 2; }
+      else t[r * k + c] = (int8_t)((int)code - 1);
+    }
+  }
+  return invalid;
+}
+
+/* --- O3: per-token absmax int8 quantization ------------------------------
+ * "BitNet-rs" page, section "技术实现细节": activations are quantized to 8
+ * bits.  Per token, the largest magnitude maps to 127 and every element is
+ * scaled by the same factor and rounded (readings in the header). */
+int oracle_quant_act(const float* x, int64_t m, int64_t k, int8_t* q,
+                     float* s_a) {
+  for (int64_t i = 0; i < m; ++i) {
+    const float* row = x + i * k;
+    float amax = 0.0f;
+    for (int64_t c = 0; c < k; ++c) {
+      const float mag = fabsf(row[c]);
+      if (mag > amax) amax = mag;
+    }
+    const float a = amax > 1e-5f ? amax : 1e-5f;
+    const float inv = 127.0f / a;            /* fp32, correctly rounded */
+    for (int64_t c = 0; c < k; ++c) {
+      const float p = row[c] * inv;          /* fp32 product */
+      float r = nearbyintf(p);               /* round half to even */
+      if (r > 127.0f) r = 127.0f;
+      if (r < -127.0f) r = -127.0f;
+      q[i * k + c] = (int8_t)r;
+    }
+    s_a[i] = a / 127.0f;
+  }
+  return 0;
+}
+
+/* --- O4 + O5: exact integer contraction, then the rescale ----------------
+ * bitnet.cpp CPU tutorial, §1.1: with weights in {-1, 0, +1} every product
+ * is the activation, its negation or nothing, so the matrix product is a
+ * sign test plus accumulation.  The output is that integer times the weight
+ * scale times the token's activation scale. */
+typedef struct {
+  const uint8_t* packed;
+  float s_w;
+  int64_t n, k, m;
+  const int8_t* q;
+  const float* s_a;
+  int32_t* acc;
+  double* y;
+  int64_t r0, r1;
+  int status;
+} gemm_job;
+
+static void* gemm_rows(void* arg) {
+  gemm_job* j = (gemm_job*)arg;
+  const int64_t row_bytes = j->k / 4;
+  for (int64_t r = j->r0; r < j->r1; ++r) {
+    for (int64_t i = 0; i < j->m; ++i) {
+      int64_t sum = 0;
+      for (int64_t c = 0; c < j->k; ++c) {
+        const unsigned code =
+            (j->packed[r * row_bytes + byte_of(c)] >> shift_of(c)) & 3u;
+        if (code == 3) { j->status = -2; return NULL; }
+        const int64_t trit = (int64_t)code - 1;
+        sum += trit * (int64_t)j->q[i * j->k + c];
+      }
+      if (sum > INT32_MAX || sum < INT32_MIN) { j->status = -1; return NULL; }
+      if (j->acc) j->acc[i * j->n + r] = (int32_t)sum;
+      if (j->y)
+        j->y[i * j->n + r] = (double)sum * (double)j->s_w * (double)j->s_a[i];
+    }
+  }
+  return NULL;
+}
+
+int oracle_gemm(const uint8_t* packed, float s_w, int64_t n, int64_t k,
+                int64_t m, const int8_t* q, const float* s_a, int32_t* acc,
+                double* y, int nthreads) {
+  if (nthreads < 1) nthreads = 1;
+  if (nthreads > n) nthreads = n > 0 ? (int)n : 1;
+  gemm_job* jobs = (gemm_job*)calloc((size_t)nthreads, sizeof(gemm_job));
+  pthread_t* tids = (pthread_t*)calloc((size_t)nthreads, sizeof(pthread_t));
+  for (int t = 0; t < nthreads; ++t) {
+    gemm_job* j = &jobs[t];
+    j->packed = packed; j->s_w = s_w; j->n = n; j->k = k; j->m = m;
+    j->q = q; j->s_a = s_a; j->acc = acc; j->y = y;
+    j->r0 = n * t / nthreads;
+    j->r1 = n * (t + 1) / nthreads;
+    j->status = 0;
+    if (t > 0) pthread_create(&tids[t], NULL, gemm_rows, j);
+  }
+  gemm_rows(&jobs[0]);
+  int status = jobs[0].status;
+  for (int t = 1; t < nthreads; ++t) {
+    pthread_join(tids[t], NULL);
+    if (jobs[t].status != 0) status = jobs[t].status;
+  }
+  free(jobs);
+  free(tids);
+  return status;
+}

@@ -1,0 +1,70 @@
+/*
+ * Oracle for the W1.58A8 ternary matrix product: a plain, slow, obviously
+ * correct CPU implementation.  TEST INFRASTRUCTURE ONLY: it is used by the
+ * tests, by the smoke check and by the benchmark's CPU-baseline leg, never by
+ * the product path.  It shares no code with the HIP library.
+ *
+ * Sources (web pages; cited by title and section):
+ *  - "1bit-systems：在AMD Strix Halo上实现纯Rust本地三值权重LLM推理",
+ *    section "三值量化：1.58-bit的魔法": weights take one of -1, 0, +1.
+ *  - bitnet.cpp CPU tutorial (m.qwbw.cn/news/64613), §1.1: ternary weights,
+ *    stored 2 bits each in practice; a multiply by -1/0/+1 is negate/skip/copy,
+ *    so the product is a sign test plus accumulation.
+ *  - same tutorial, §3.2: conversion projects every weight onto the ternary
+ *    set by absmean quantization.
+ *  - "BitNet-rs：Rust实现的高效1比特大语言模型推理引擎", section
+ *    "技术实现细节": activations are quantized to 8 bits.
+ *  - "BitNet 1 位 LLM 独立推理引擎：位串行 GEMM 内核与 LUT 优化工程实践",
+ *    body paragraph on conversion: the generic 2-bit format is called I2_S.
+ * The pages fix no bit layout, rounding rule or scale formula; the readings
+ * used here (code = trit + 1, the word-interleaved 2-bit layout, round half to
+ * even, clamp to +-127, amax floor 1e-5, x * (127 / amax)) are listed with the
+ * reasons in the design notes of this repository.
+ */
+#ifndef BT_ORACLE_H
+#define BT_ORACLE_H
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* O1: absmean ternarization of an fp32 [n, k] tensor.
+ * gamma = (float)(sum |w| / (n k)) with the sum in double; t = clamp(rne(w /
+ * gamma), -1, 1) with an fp32 divide; *s_w = gamma.  gamma == 0 gives t = 0.
+ * Returns 0. */
+int oracle_ternarize_absmean(const float* w, int64_t n, int64_t k, int8_t* t,
+                             float* s_w);
+
+/* O2: pack trits [n, k] (k % 16 == 0) into n * k / 4 bytes.
+ * Code c = t + 1 in {0, 1, 2}.  Row r occupies bytes [r k/4, (r+1) k/4).
+ * Weight k of a row sits in byte 4 (k / 16) + (k % 4) of the row, at bit
+ * 2 ((k % 16) / 4).  Returns the number of entries outside {-1, 0, 1}; such
+ * entries are stored as code 3 (the one code that no trit maps to). */
+int64_t oracle_pack_i2s(const int8_t* t, int64_t n, int64_t k, uint8_t* packed);
+
+/* O2 inverse: unpack to trits.  Code 3 is invalid: it is written as the
+ * value 2 (not a trit) and counted; returns the count. */
+int64_t oracle_unpack_i2s(const uint8_t* packed, int64_t n, int64_t k,
+                          int8_t* t);
+
+/* O3: per-row (per token) absmax quantization of fp32 x [m, k] to int8.
+ * amax = max |x|, a = max(amax, 1e-5f), inv = 127.0f / a (fp32),
+ * q = clamp(rne(x * inv), -127, 127) (fp32 product), s_a = a / 127.0f. */
+int oracle_quant_act(const float* x, int64_t m, int64_t k, int8_t* q,
+                     float* s_a);
+
+/* O4 + O5: acc[i, r] = sum_k trit(r, k) * q[i, k], exact (int64 sum, checked
+ * to fit int32); y[i, r] = acc * s_w * s_a[i] evaluated in double.
+ * packed is [n, k/4] in the O2 layout, q is [m, k], acc and y are [m, n]
+ * (either may be NULL).  Output rows are split over `nthreads` threads in
+ * contiguous slices; each output is computed by the same plain loop.
+ * Returns 0, -1 if an accumulator left int32, -2 on an invalid code. */
+int oracle_gemm(const uint8_t* packed, float s_w, int64_t n, int64_t k,
+                int64_t m, const int8_t* q, const float* s_a, int32_t* acc,
+                double* y, int nthreads);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,0 +1,368 @@
+"""Pins for the CPU oracle: hand-worked examples, closed forms, brute force
+and invariants.  None of these re-types the oracle's formulas; each checks a
+property that a dropped term, a wrong sign or index, or a transposed operand
+would break.  CPU only."""
+import itertools
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def read_golden(name):
+    out = {}
+    rows = []
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            if ":" in line:
+                key, val = line.split(":", 1)
+                out[key.strip()] = val.split()
+            else:
+                rows.append(line.split())
+    return out, rows
+
+
+# ------------------------------------------------------------------ O1
+def test_absmean_worked_example(orc):
+    g, _ = read_golden("absmean_example.txt")
+    w = np.array([[float(v) for v in g["w"]]], np.float32)
+    t, s = orc.ternarize_absmean(w)
+    assert s == np.float32(float(g["gamma"][0]))
+    assert t.tolist() == [[int(v) for v in g["t"]]]
+
+
+def _brute_ternarize(w):
+    """argmin over {-1, 0, 1} of |w/gamma - t| with ties to the even value
+    (0 for +-0.5); values beyond +-1.5 saturate."""
+    flat = w.astype(np.float64).ravel()
+    gamma = np.float32(math.fsum(abs(v) for v in flat) / flat.size)
+    out = []
+    for v in w.ravel():
+        if gamma == 0:
+            out.append(0)
+            continue
+        r = float(np.float32(v) / gamma)  # fp32 divide decides the trit
+        best = None
+        for cand in (0, -1, 1):  # 0 first: it wins exact ties at +-0.5
+            d = abs(Fraction(r) - cand)
+            if best is None or d < best[0]:
+                best = (d, cand)
+        out.append(best[1])
+    return np.array(out, np.int8).reshape(w.shape), gamma
+
+
+def test_absmean_brute_force(orc):
+    rng = np.random.default_rng(11)
+    for shape in [(1, 8), (3, 16), (7, 33)]:
+        # multiples of 2^-10 in a small range: the double sum is exact
+        w = (rng.integers(-900, 901, size=shape) / 1024.0).astype(np.float32)
+        t, s = orc.ternarize_absmean(w)
+        tb, sb = _brute_ternarize(w)
+        assert s == sb
+        np.testing.assert_array_equal(t, tb)
+
+
+def test_absmean_idempotent_on_scaled_trits(orc):
+    rng = np.random.default_rng(12)
+    for s in [0.02, 0.5, 3.0, 1e-3]:
+        t = rng.integers(-1, 2, size=(5, 64), dtype=np.int8)
+        t[0, 0] = 1
+        w = (np.float32(s) * t).astype(np.float32)
+        t2, gamma = orc.ternarize_absmean(w)
+        np.testing.assert_array_equal(t2, t)
+        # gamma is s times the fraction of nonzero entries, not s itself
+        frac = np.count_nonzero(t) / t.size
+        assert gamma == pytest.approx(s * frac, rel=1e-6)
+
+
+def test_absmean_odd_and_power_of_two(orc):
+    rng = np.random.default_rng(13)
+    w = rng.standard_normal((9, 48)).astype(np.float32)
+    t, s = orc.ternarize_absmean(w)
+    tn, sn = orc.ternarize_absmean(-w)
+    np.testing.assert_array_equal(tn, -t)
+    assert sn == s
+    for j in (-3, 5):
+        tj, sj = orc.ternarize_absmean(w * np.float32(2.0 ** j))
+        np.testing.assert_array_equal(tj, t)
+        assert sj == s * np.float32(2.0 ** j)
+    assert set(np.unique(t)) <= {-1, 0, 1}
+
+
+def test_absmean_all_zero(orc):
+    t, s = orc.ternarize_absmean(np.zeros((2, 16), np.float32))
+    assert s == 0 and not t.any()
+
+
+# ------------------------------------------------------------------ O2
+def test_pack_closed_forms(orc):
+    for trit, byte in [(0, 0x55), (1, 0xAA), (-1, 0x00)]:
+        p, bad = orc.pack_i2s(np.full((3, 64), trit, np.int8))
+        assert bad == 0 and p.shape == (3, 16)
+        assert (p == byte).all()
+
+
+def test_pack_single_plus_one_golden(orc):
+    _, rows = read_golden("pack_single_plus_one.txt")
+    assert len(rows) >= 16
+    for k, bidx, val in rows:
+        t = np.zeros((1, 64), np.int8)
+        t[0, int(k)] = 1
+        p, _ = orc.pack_i2s(t)
+        expect = np.full(16, 0x55, np.uint8)
+        expect[int(bidx)] = int(val, 16)
+        np.testing.assert_array_equal(p[0], expect, err_msg=f"k={k}")
+
+
+def test_pack_round_trip_all_81_bytes(orc):
+    # positions 0, 4, 8, 12 share byte 0 of the row (one field each)
+    seen = set()
+    for combo in itertools.product((-1, 0, 1), repeat=4):
+        t = np.zeros((1, 16), np.int8)
+        t[0, [0, 4, 8, 12]] = combo
+        p, bad = orc.pack_i2s(t)
+        assert bad == 0
+        seen.add(int(p[0, 0]))
+        back, bad2 = orc.unpack_i2s(p, 16)
+        assert bad2 == 0
+        np.testing.assert_array_equal(back, t)
+    assert len(seen) == 81
+    # no valid byte holds the invalid code 3 in any 2-bit field
+    for b in seen:
+        assert all(((b >> s) & 3) != 3 for s in (0, 2, 4, 6))
+
+
+def test_pack_round_trip_random(orc):
+    rng = np.random.default_rng(14)
+    t = rng.integers(-1, 2, size=(37, 320), dtype=np.int8)
+    p, bad = orc.pack_i2s(t)
+    assert bad == 0 and p.shape == (37, 80)
+    back, bad2 = orc.unpack_i2s(p, 320)
+    assert bad2 == 0
+    np.testing.assert_array_equal(back, t)
+
+
+def test_pack_invalid_counted(orc):
+    t = np.zeros((2, 16), np.int8)
+    t[0, 3] = 2
+    t[1, 7] = -2
+    t[1, 9] = 5
+    _, bad = orc.pack_i2s(t)
+    assert bad == 3
+    _, bad_unpack = orc.unpack_i2s(np.full((1, 4), 0xFF, np.uint8), 16)
+    assert bad_unpack == 16
+
+
+def test_pack_size_matches_two_bits_per_weight(orc):
+    # bitnet.cpp CPU tutorial §1.1: a 1B-parameter model's weights take about
+    # 250 MB at 2 bits each; the packed size is n*k/4 bytes.
+    t = np.zeros((8, 1024), np.int8)
+    p, _ = orc.pack_i2s(t)
+    assert p.nbytes * 4 == t.size
+    assert 10 ** 9 // 4 == 250_000_000
+
+
+# ------------------------------------------------------------------ O3
+def test_quant_tie_table(orc):
+    g, _ = read_golden("quant_ties.txt")
+    x = np.array([[float(v) for v in g["x"]]], np.float32)
+    q, s = orc.quant_act(x)
+    assert q[0].tolist() == [int(v) for v in g["q"]]
+    assert s[0] == np.float32(float(g["s_a"][0]))
+
+
+def _brute_quant_row(x):
+    """q = argmin over integers in [-127, 127] of |x * inv - q| (fp32 product
+    decides), ties to even; exact rational distances."""
+    amax = max(abs(float(v)) for v in x)
+    a = np.float32(max(amax, float(np.float32(1e-5))))
+    inv = np.float32(127.0) / a
+    out = []
+    for v in x:
+        p = Fraction(float(np.float32(v) * inv))
+        lo = math.floor(p)
+        cands = [c for c in (lo, lo + 1) if -127 <= c <= 127]
+        if not cands:
+            cands = [max(-127, min(127, lo))]
+        best = min(cands, key=lambda c: (abs(p - c), c % 2))
+        out.append(best)
+    return np.array(out, np.int8), np.float32(a / np.float32(127.0))
+
+
+def test_quant_brute_force(orc):
+    rng = np.random.default_rng(15)
+    x = rng.standard_normal((4, 96)).astype(np.float32)
+    x[1] *= 30
+    x[2, ::7] *= 20
+    x[3] = np.round(x[3] * 4) / 4  # many exact .5 ties after scaling
+    q, s = orc.quant_act(x)
+    for i in range(x.shape[0]):
+        qb, sb = _brute_quant_row(x[i])
+        np.testing.assert_array_equal(q[i], qb)
+        assert s[i] == sb
+
+
+def test_quant_invariants(orc):
+    rng = np.random.default_rng(16)
+    x = rng.standard_normal((6, 128)).astype(np.float32)
+    q, s = orc.quant_act(x)
+    # the element of largest magnitude maps to +-127
+    for i in range(6):
+        j = np.argmax(np.abs(x[i]))
+        assert abs(int(q[i, j])) == 127
+    assert q.min() >= -127
+    # odd symmetry
+    qn, sn = orc.quant_act(-x)
+    np.testing.assert_array_equal(qn, -q)
+    np.testing.assert_array_equal(sn, s)
+    # power-of-two scaling leaves q unchanged and scales s_a exactly
+    for j in (-4, 7):
+        qj, sj = orc.quant_act(x * np.float32(2.0 ** j))
+        np.testing.assert_array_equal(qj, q)
+        np.testing.assert_array_equal(sj, s * np.float32(2.0 ** j))
+
+
+def test_quant_zero_and_tiny_rows(orc):
+    x = np.zeros((2, 64), np.float32)
+    x[1, 5] = 1e-30
+    q, s = orc.quant_act(x)
+    assert not q.any()
+    assert s[0] == s[1] == np.float32(np.float32(1e-5) / np.float32(127))
+
+
+# ------------------------------------------------------------------ O4
+def test_gemm_matches_numpy_int64(orc):
+    rng = np.random.default_rng(17)
+    for n, k, m in [(5, 64, 1), (33, 128, 3), (17, 256, 8), (3, 1024, 2)]:
+        t = rng.integers(-1, 2, size=(n, k), dtype=np.int8)
+        q = rng.integers(-127, 128, size=(m, k), dtype=np.int8)
+        p, _ = orc.pack_i2s(t)
+        acc, _ = orc.gemm(p, 1.0, k, q, np.ones(m, np.float32))
+        ref = q.astype(np.int64) @ t.astype(np.int64).T
+        np.testing.assert_array_equal(acc, ref)
+
+
+def test_gemm_brute_force_all_rows_of_four(orc):
+    rows = np.array(list(itertools.product((-1, 0, 1), repeat=4)), np.int8)
+    t = np.zeros((81, 16), np.int8)
+    t[:, :4] = rows
+    qs = np.zeros((3, 16), np.int8)
+    qs[0, :4] = [127, 2, -4, 0]
+    qs[1, :4] = [-127, -127, 127, 1]
+    qs[2, :4] = [5, -3, 7, -11]
+    p, _ = orc.pack_i2s(t)
+    acc, _ = orc.gemm(p, 1.0, 16, qs, np.ones(3, np.float32))
+    for i in range(3):
+        for r in range(81):
+            s = 0
+            for c in range(4):
+                s += int(rows[r][c]) * int(qs[i][c])
+            assert acc[i, r] == s
+
+
+def test_gemm_closed_forms(orc):
+    rng = np.random.default_rng(18)
+    k = 192
+    q = rng.integers(-127, 128, size=(2, k), dtype=np.int8)
+    t = np.zeros((3 + k, k), np.int8)
+    t[1] = 1
+    t[2] = -1
+    for c in range(k):
+        t[3 + c, c] = 1  # one-hot rows
+    p, _ = orc.pack_i2s(t)
+    acc, _ = orc.gemm(p, 1.0, k, q, np.ones(2, np.float32))
+    qs = q.astype(np.int64).sum(axis=1)
+    assert (acc[:, 0] == 0).all()
+    np.testing.assert_array_equal(acc[:, 1], qs)
+    np.testing.assert_array_equal(acc[:, 2], -qs)
+    np.testing.assert_array_equal(acc[:, 3:], q)
+
+
+def test_gemm_invariants(orc):
+    rng = np.random.default_rng(19)
+    n, k, m = 11, 320, 4
+    t = rng.integers(-1, 2, size=(n, k), dtype=np.int8)
+    q = rng.integers(-127, 128, size=(m, k), dtype=np.int8)
+    ones = np.ones(m, np.float32)
+    acc, _ = orc.gemm(orc.pack_i2s(t)[0], 1.0, k, q, ones)
+    accn, _ = orc.gemm(orc.pack_i2s(-t)[0], 1.0, k, q, ones)
+    np.testing.assert_array_equal(accn, -acc)
+    perm = rng.permutation(k)
+    accp, _ = orc.gemm(orc.pack_i2s(t[:, perm])[0], 1.0, k, q[:, perm], ones)
+    np.testing.assert_array_equal(accp, acc)
+    # additivity while the sum stays ternary: split t into disjoint supports
+    mask = rng.random((n, k)) < 0.5
+    t1 = np.where(mask, t, 0).astype(np.int8)
+    t2 = np.where(mask, 0, t).astype(np.int8)
+    a1, _ = orc.gemm(orc.pack_i2s(t1)[0], 1.0, k, q, ones)
+    a2, _ = orc.gemm(orc.pack_i2s(t2)[0], 1.0, k, q, ones)
+    np.testing.assert_array_equal(a1 + a2, acc)
+
+
+def test_gemm_threads_and_row_ranges_agree(orc):
+    rng = np.random.default_rng(20)
+    n, k, m = 57, 256, 3
+    t = rng.integers(-1, 2, size=(n, k), dtype=np.int8)
+    q = rng.integers(-127, 128, size=(m, k), dtype=np.int8)
+    s_a = np.array([0.5, 0.25, 2.0], np.float32)
+    p, _ = orc.pack_i2s(t)
+    a1, y1 = orc.gemm(p, 0.125, k, q, s_a, nthreads=1)
+    a7, y7 = orc.gemm(p, 0.125, k, q, s_a, nthreads=7)
+    np.testing.assert_array_equal(a1, a7)
+    np.testing.assert_array_equal(y1, y7)
+    ar, yr = orc.gemm(p, 0.125, k, q, s_a, rows=(10, 20))
+    np.testing.assert_array_equal(ar, a1[:, 10:20])
+
+
+def test_gemm_extreme_accumulator(orc):
+    k = 65536
+    t = np.ones((1, k), np.int8)
+    q = np.full((1, k), 127, np.int8)
+    acc, _ = orc.gemm(orc.pack_i2s(t)[0], 1.0, k, q, np.ones(1, np.float32))
+    assert acc[0, 0] == 127 * k
+
+
+# ------------------------------------------------------------------ O5
+def test_pipeline_worked_example(orc):
+    g, _ = read_golden("pipeline_example.txt")
+    t4 = np.array([[int(v) for v in g["T0"]], [int(v) for v in g["T1"]]],
+                  np.int8)
+    for k in (4 * 4, 64):
+        t = np.zeros((2, k), np.int8)
+        t[:, :4] = t4
+        x = np.zeros((1, k), np.float32)
+        x[0, :4] = [float(v) for v in g["x"]]
+        q, s_a = orc.quant_act(x)
+        assert q[0, :4].tolist() == [int(v) for v in g["q"]]
+        assert s_a[0] == float(g["s_a"][0])
+        acc, y = orc.gemm(orc.pack_i2s(t)[0], float(g["s_w"][0]), k, q, s_a)
+        assert acc[0].tolist() == [int(v) for v in g["acc"]]
+        assert y[0].tolist() == [float(v) for v in g["y"]]
+
+
+def test_rescale_close_to_exact_product(orc):
+    """y (double) is within a few double roundings of the exact rational
+    product acc * s_w * s_a."""
+    rng = np.random.default_rng(21)
+    n, k, m = 9, 128, 3
+    t = rng.integers(-1, 2, size=(n, k), dtype=np.int8)
+    x = rng.standard_normal((m, k)).astype(np.float32)
+    q, s_a = orc.quant_act(x)
+    s_w = np.float32(0.0317)
+    acc, y = orc.gemm(orc.pack_i2s(t)[0], s_w, k, q, s_a)
+    for i in range(m):
+        for r in range(n):
+            exact = Fraction(int(acc[i, r])) * Fraction(float(s_w)) * \
+                Fraction(float(s_a[i]))
+            if exact == 0:
+                assert y[i, r] == 0
+            else:
+                err = abs((Fraction(float(y[i, r])) - exact) / exact)
+                assert err < Fraction(1, 2 ** 50)
