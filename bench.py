@@ -1,0 +1,298 @@
+#!/usr/bin/env python3
+"""Benchmark of the ternary W1.58A8 hot path on one MI355X.
+
+A step is one pass of the per-token path over a whole synthetic weight set:
+per-token int8 quantization of every projection's activations (bt_quant_act,
+one launch per distinct input length) and every ternary product with its
+rescale (one grouped launch, bt_gemm_grouped).  Packing is the offline
+conversion step and runs before timing.  Inputs are resident in HBM when the
+timed region starts.
+
+Default workload: the 2B-shaped decode set at M=1 (30 layers x 7 projections,
+0.52 GB of packed weights, larger than the 256 MB Infinity Cache).  Prints
+one JSON line (rank 0, one GPU).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import glob
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workloads as wl  # noqa: E402
+
+METRIC = "W1.58A8 GEMV HBM GB/s (% of peak) at M=1; GEMM TOPS at M=512"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+INT8_PEAK_TOPS = 5000.0        # MI355X dense int8 matrix peak
+
+WORKLOADS = {
+    "decode_2b_m1": lambda: wl.decode_2b(1),
+    "decode_2b_m8": lambda: wl.decode_2b(8),
+    "decode_2b_m16": lambda: wl.decode_2b(16),
+    "decode_2b_m32": lambda: wl.decode_2b(32),
+    "prefill_2b_m512": lambda: wl.prefill_2b(512),
+    "decode_8b_m1": lambda: wl.decode_8b(1),
+    "decode_8b_m64": lambda: wl.decode_8b(64),
+}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_sources_sha():
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "gemm_i2_bit_amd", "csrc",
+                                           "*"))):
+        with open(f, "rb") as fh:
+            h.update(os.path.basename(f).encode())
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+class WorkSet:
+    """Device buffers, plan and step function for one workload."""
+
+    def __init__(self, work: wl.Workload, torch, bt, mode="grouped"):
+        self.work = work
+        self.torch = torch
+        self.bt = bt
+        self.mode = mode
+        dev = torch.device("cuda:0")
+        probs = work.problems()
+        m = work.m
+        self.m = m
+        ks = sorted({p.k for p in probs})
+        rows = {k: m * sum(1 for p in probs if p.k == k) for k in ks}
+        self.x = {k: torch.empty((rows[k], k), dtype=torch.float32,
+                                 device=dev) for k in ks}
+        self.xq = {k: torch.empty((rows[k], k), dtype=torch.int8, device=dev)
+                   for k in ks}
+        self.sa = {k: torch.empty(rows[k], dtype=torch.float32, device=dev)
+                   for k in ks}
+        off = {k: 0 for k in ks}
+        self.problems = []
+        t0 = time.time()
+        for i, p in enumerate(probs):
+            t, s_w = work.weights(p.layer, p.proj)
+            packed = bt.bt_pack_i2s(torch.from_numpy(t).to(dev))
+            del t
+            x = work.activations(p.layer, p.proj)
+            o = off[p.k]
+            self.x[p.k][o:o + m].copy_(torch.from_numpy(x))
+            off[p.k] += m
+            y = torch.empty((m, p.n), dtype=torch.float32, device=dev)
+            self.problems.append(dict(packed=packed, s_w=float(s_w), n=p.n,
+                                      k=p.k, x_q=self.xq[p.k][o:o + m],
+                                      s_a=self.sa[p.k][o:o + m], y=y))
+            if (i + 1) % 50 == 0:
+                log(f"[bench] prepared {i + 1}/{len(probs)} tensors "
+                    f"({time.time() - t0:.1f} s)")
+        torch.cuda.synchronize()
+        self.plan = bt.bt_grouped_plan(self.problems)
+        self.ks = ks
+
+    # algorithmic bytes and ops -------------------------------------------
+    def product_bytes(self):
+        """Packed weights + int8 activations + scales + fp32 outputs."""
+        m = self.m
+        return sum(self.bt.bt_packed_bytes(p["n"], p["k"]) + m * p["k"] + 4 * m
+                   + 4 * m * p["n"] for p in self.problems)
+
+    def quant_bytes(self):
+        m = self.m
+        return sum(5 * m * p["k"] + 4 * m for p in self.problems)
+
+    def weight_bytes(self):
+        return sum(self.bt.bt_packed_bytes(p["n"], p["k"])
+                   for p in self.problems)
+
+    def ops(self):
+        return sum(2 * self.m * p["n"] * p["k"] for p in self.problems)
+
+    # the step ------------------------------------------------------------
+    def quant(self):
+        for k in self.ks:
+            self.bt.bt_quant_act(self.x[k], self.xq[k], self.sa[k])
+
+    def product(self):
+        if self.mode == "grouped":
+            self.bt.bt_gemm_grouped(self.plan)
+        else:
+            for p in self.problems:
+                self.bt.bt_gemm(p["packed"], p["s_w"], p["n"], p["k"],
+                                p["x_q"], p["s_a"], y=p["y"])
+
+
+def run_timed(ws: WorkSet, steps: int, warmup: int, torch):
+    for _ in range(warmup):
+        ws.quant()
+        ws.product()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        ws.quant()
+        ev[i][0].record()
+        ws.product()
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kern_ms = [a.elapsed_time(b) for a, b in ev]
+    return wall, kern_ms
+
+
+def cpu_baseline(work: wl.Workload, seconds: float):
+    """The oracle, as it stands, on a bounded sample of the same workload:
+    whole layers (all 7 projections) until `seconds` of timed work."""
+    import oracle
+    threads = int(os.environ.get("OMP_NUM_THREADS", 0) or os.cpu_count() or 1)
+    timed = 0.0
+    nbytes = 0
+    layers = 0
+    for layer in range(work.layers):
+        items = []
+        for proj in work.projs:
+            t, s_w = work.weights(layer, proj)
+            packed, _ = oracle.pack_i2s(t)          # offline step: untimed
+            x = work.activations(layer, proj)
+            items.append((packed, s_w, t.shape[0], t.shape[1], x))
+            del t
+        t0 = time.perf_counter()
+        for packed, s_w, n, k, x in items:
+            q, s_a = oracle.quant_act(x)
+            oracle.gemm(packed, s_w, n, k, q, s_a, nthreads=threads)
+        timed += time.perf_counter() - t0
+        m = work.m
+        nbytes += sum(p.size + m * k + 4 * m + 4 * m * n
+                      for p, _, n, k, _ in items)
+        layers += 1
+        if timed >= seconds:
+            break
+    return dict(value=nbytes / timed / 1e9, unit="GB/s", cores=threads,
+                kind="oracle",
+                sample=f"{layers} of {work.layers} layers x {len(work.projs)} "
+                       f"projections at M={work.m} (quantize + product, "
+                       f"{timed:.1f} s timed)")
+
+
+def load_traffic(workload: str, sha: str, launch_bytes: int):
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_sources_sha") != sha:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="decode_2b_m1",
+                    choices=sorted(WORKLOADS))
+    ap.add_argument("--mode", default="grouped",
+                    choices=["grouped", "per-launch"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the M=512 prefill figure")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py runs on one GPU only: the ternary product is measured "
+              "on a single MI355X (no sharding, no collectives); "
+              "use --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import gemm_i2_bit_amd as bt
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    bt.lib()  # fails loudly if the HIP library is missing
+
+    work = WORKLOADS[args.workload]()
+    log(f"[bench] workload {work.name}: {len(work.problems())} products, "
+        f"{work.weight_bytes() / 1e6:.1f} MB packed weights")
+    ws = WorkSet(work, torch, bt, args.mode)
+    wall, kern_ms = run_timed(ws, args.steps, args.warmup, torch)
+    ms_step = wall / args.steps * 1e3
+    kern_avg = float(np.mean(kern_ms))
+    step_bytes = ws.product_bytes() + ws.quant_bytes()
+    prefill = work.m >= 128
+    if prefill:
+        value = ws.ops() / (ms_step * 1e-3) / 1e12
+        unit = "TOPS"
+    else:
+        value = step_bytes / (ms_step * 1e-3) / 1e9
+        unit = "GB/s"
+    launch_bytes = ws.product_bytes()
+    sha = kernel_sources_sha()
+    if prefill:
+        achieved = ws.ops() / (kern_avg * 1e-3) / 1e12
+        roof = dict(bound="mfma", achieved=round(achieved, 2),
+                    peak=INT8_PEAK_TOPS, unit="TFLOP/s",
+                    frac=round(achieved / INT8_PEAK_TOPS, 4),
+                    traffic=load_traffic(args.workload, sha, launch_bytes))
+    else:
+        achieved = launch_bytes / (kern_avg * 1e-3) / 1e9
+        roof = dict(bound="hbm", achieved=round(achieved, 1),
+                    peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=round(achieved / HBM_PEAK_GBS, 4),
+                    traffic=load_traffic(args.workload, sha, launch_bytes))
+    out = {
+        "metric": METRIC, "value": round(value, 2), "unit": unit,
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "int8",
+        "data": "synthetic",
+        "config": {"workload": work.name, "m": work.m,
+                   "layers": work.layers, "projections": len(work.projs),
+                   "weight_bytes": ws.weight_bytes(),
+                   "launch": args.mode,
+                   "product_kernel_ms": round(kern_avg, 5),
+                   "tokens_per_s_equiv": round(work.m / (ms_step * 1e-3), 1),
+                   "tops": round(ws.ops() / (ms_step * 1e-3) / 1e12, 3)},
+        "roofline": roof,
+    }
+    del ws
+    torch.cuda.empty_cache()
+
+    if not args.no_extra and not prefill:
+        pw = wl.prefill_2b(512)
+        pws = WorkSet(pw, torch, bt, "grouped")
+        pwall, pk = run_timed(pws, 20, 3, torch)
+        pk_avg = float(np.mean(pk))
+        tops_k = pws.ops() / (pk_avg * 1e-3) / 1e12
+        out["prefill_m512"] = {
+            "workload": pw.name, "ms_per_step": round(pwall / 20 * 1e3, 4),
+            "product_kernel_ms": round(pk_avg, 5),
+            "tops_step": round(pws.ops() / (pwall / 20) / 1e12, 2),
+            "tops_kernel": round(tops_k, 2),
+            "frac_int8_peak": round(tops_k / INT8_PEAK_TOPS, 4)}
+        del pws
+        torch.cuda.empty_cache()
+
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a sample")
+        out["cpu_baseline"] = cpu_baseline(work, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

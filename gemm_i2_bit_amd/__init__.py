@@ -1,0 +1,244 @@
+"""Python binding of libbt, the MI355X (gfx950) ternary W1.58A8 GEMV/GEMM
+library.  Argument marshalling only: every step of the product runs in the
+library's HIP kernels.  PyTorch supplies device memory and streams.
+
+Functions carry the C ABI's names (see include/bt.h for the contract):
+bt_pack_i2s, bt_quant_act, bt_gemv, bt_gemm, bt_grouped_plan,
+bt_gemm_grouped, bt_packed_bytes, bt_status_str.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libbt.so")
+
+BT_OK, BT_E_NULL, BT_E_SHAPE, BT_E_ALIGN, BT_E_ARG, BT_E_HIP, BT_E_ARCH = (
+    0, -1, -2, -3, -4, -5, -6)
+
+_lib = None
+
+
+class BtError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {bt_status_str(status)} (status {status})")
+
+
+class bt_problem(ctypes.Structure):
+    _fields_ = [("packed", ctypes.c_void_p), ("x_q", ctypes.c_void_p),
+                ("s_a", ctypes.c_void_p), ("y", ctypes.c_void_p),
+                ("acc", ctypes.c_void_p), ("s_w", ctypes.c_float),
+                ("n", ctypes.c_int32), ("k", ctypes.c_int32),
+                ("m", ctypes.c_int32)]
+
+
+def lib() -> ctypes.CDLL:
+    """Load libbt.so; fails loudly when it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with "
+                "`python gemm_i2_bit_amd/build.py` (hipcc, gfx950)")
+        L = ctypes.CDLL(LIB_PATH)
+        p, i32, i64, f32 = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64,
+                            ctypes.c_float)
+        L.bt_status_str.argtypes = [i32]
+        L.bt_status_str.restype = ctypes.c_char_p
+        L.bt_packed_bytes.argtypes = [i64, i64]
+        L.bt_packed_bytes.restype = i64
+        L.bt_pack_i2s.argtypes = [p, i64, i64, p, p, p]
+        L.bt_pack_i2s.restype = i32
+        L.bt_quant_act.argtypes = [p, i64, i64, p, p, p]
+        L.bt_quant_act.restype = i32
+        L.bt_gemv.argtypes = [p, f32, i64, i64, p, p, p, p, p]
+        L.bt_gemv.restype = i32
+        L.bt_gemm.argtypes = [p, f32, i64, i64, i64, p, p, p, p, p]
+        L.bt_gemm.restype = i32
+        L.bt_grouped_plan_bytes.argtypes = [p, i32]
+        L.bt_grouped_plan_bytes.restype = i64
+        L.bt_grouped_plan.argtypes = [p, i32, p, i64]
+        L.bt_grouped_plan.restype = i32
+        L.bt_gemm_grouped.argtypes = [p, p, p]
+        L.bt_gemm_grouped.restype = i32
+        _lib = L
+    return _lib
+
+
+def bt_status_str(status: int) -> str:
+    return lib().bt_status_str(int(status)).decode()
+
+
+def _check(status: int, what: str):
+    if status != BT_OK:
+        raise BtError(status, what)
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dev(t, dtype, name):
+    """Pointer of a contiguous GPU tensor of the given dtype (None -> NULL)."""
+    if t is None:
+        return None
+    torch = _torch()
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a GPU tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
+
+
+def bt_packed_bytes(n: int, k: int) -> int:
+    r = lib().bt_packed_bytes(n, k)
+    if r < 0:
+        raise BtError(r, "bt_packed_bytes")
+    return r
+
+
+def bt_pack_i2s(t, packed=None, n_invalid=None, stream=None):
+    """int8 trits [n, k] (GPU) -> packed uint8 (GPU, bt_packed_bytes)."""
+    torch = _torch()
+    n, k = t.shape
+    if packed is None:
+        packed = torch.empty(bt_packed_bytes(n, k), dtype=torch.uint8,
+                             device=t.device)
+    if packed.numel() != bt_packed_bytes(n, k):
+        raise ValueError("packed has the wrong size")
+    _check(lib().bt_pack_i2s(_dev(t, torch.int8, "t"), n, k,
+                             _dev(packed, torch.uint8, "packed"),
+                             _dev(n_invalid, torch.int32, "n_invalid"),
+                             _stream(stream)), "bt_pack_i2s")
+    return packed
+
+
+def bt_quant_act(x, x_q=None, s_a=None, stream=None):
+    """fp32 [m, k] (GPU) -> (int8 x_q [m, k], fp32 s_a [m])."""
+    torch = _torch()
+    if x.dim() == 1:
+        x = x.unsqueeze(0)
+    m, k = x.shape
+    if x_q is None:
+        x_q = torch.empty((m, k), dtype=torch.int8, device=x.device)
+    if s_a is None:
+        s_a = torch.empty(m, dtype=torch.float32, device=x.device)
+    if x_q.numel() != m * k or s_a.numel() != m:
+        raise ValueError("x_q or s_a has the wrong size")
+    _check(lib().bt_quant_act(_dev(x, torch.float32, "x"), m, k,
+                              _dev(x_q, torch.int8, "x_q"),
+                              _dev(s_a, torch.float32, "s_a"),
+                              _stream(stream)), "bt_quant_act")
+    return x_q, s_a
+
+
+def _outputs(m, n, device, y, acc, want_acc):
+    torch = _torch()
+    if y is None:
+        y = torch.empty((m, n), dtype=torch.float32, device=device)
+    if acc is None and want_acc:
+        acc = torch.empty((m, n), dtype=torch.int32, device=device)
+    if y.numel() != m * n or (acc is not None and acc.numel() != m * n):
+        raise ValueError("y or acc has the wrong size")
+    return y, acc
+
+
+def bt_gemm(packed, s_w, n: int, k: int, x_q, s_a, y=None, acc=None,
+            want_acc: bool = False, stream=None):
+    """y [m, n] = (trits . x_q) * s_w * s_a; returns (y, acc or None)."""
+    torch = _torch()
+    m = x_q.shape[0] if x_q.dim() == 2 else 1
+    if x_q.numel() != m * k or s_a.numel() != m:
+        raise ValueError("x_q or s_a has the wrong size")
+    if packed.numel() != bt_packed_bytes(n, k):
+        raise ValueError("packed has the wrong size")
+    y, acc = _outputs(m, n, x_q.device, y, acc, want_acc)
+    _check(lib().bt_gemm(_dev(packed, torch.uint8, "packed"), float(s_w), n,
+                         k, m, _dev(x_q, torch.int8, "x_q"),
+                         _dev(s_a, torch.float32, "s_a"),
+                         _dev(y, torch.float32, "y"),
+                         _dev(acc, torch.int32, "acc"), _stream(stream)),
+           "bt_gemm")
+    return y, acc
+
+
+def bt_gemv(packed, s_w, n: int, k: int, x_q, s_a, y=None, acc=None,
+            want_acc: bool = False, stream=None):
+    """One token: x_q [k] or [1, k] -> y [1, n]."""
+    torch = _torch()
+    if x_q.numel() != k or s_a.numel() != 1:
+        raise ValueError("x_q or s_a has the wrong size")
+    if packed.numel() != bt_packed_bytes(n, k):
+        raise ValueError("packed has the wrong size")
+    y, acc = _outputs(1, n, x_q.device, y, acc, want_acc)
+    _check(lib().bt_gemv(_dev(packed, torch.uint8, "packed"), float(s_w), n,
+                         k, _dev(x_q, torch.int8, "x_q"),
+                         _dev(s_a, torch.float32, "s_a"),
+                         _dev(y, torch.float32, "y"),
+                         _dev(acc, torch.int32, "acc"), _stream(stream)),
+           "bt_gemv")
+    return y, acc
+
+
+class GroupedPlan:
+    """A grouped-product plan: the host image and its device copy.  Keeps
+    references to every tensor the plan points at."""
+
+    def __init__(self, host: np.ndarray, dev, tensors):
+        self.host = host
+        self.dev = dev
+        self._tensors = tensors
+
+
+def bt_grouped_plan(problems, device=None) -> GroupedPlan:
+    """problems: list of dicts with packed, s_w, n, k, x_q, s_a, y and
+    optionally acc (GPU tensors; every problem has the same m)."""
+    torch = _torch()
+    arr = (bt_problem * len(problems))()
+    keep = []
+    for i, p in enumerate(problems):
+        m = p["x_q"].shape[0] if p["x_q"].dim() == 2 else 1
+        if (p["x_q"].numel() != m * p["k"] or p["s_a"].numel() != m
+                or p["y"].numel() != m * p["n"]
+                or p["packed"].numel() != bt_packed_bytes(p["n"], p["k"])
+                or (p.get("acc") is not None
+                    and p["acc"].numel() != m * p["n"])):
+            raise ValueError(f"problem {i} has inconsistent sizes")
+        arr[i] = bt_problem(_dev(p["packed"], torch.uint8, "packed"),
+                            _dev(p["x_q"], torch.int8, "x_q"),
+                            _dev(p["s_a"], torch.float32, "s_a"),
+                            _dev(p["y"], torch.float32, "y"),
+                            _dev(p.get("acc"), torch.int32, "acc"),
+                            float(p["s_w"]), p["n"], p["k"], m)
+        keep.append(p)
+    nbytes = lib().bt_grouped_plan_bytes(arr, len(problems))
+    if nbytes < 0:
+        raise BtError(nbytes, "bt_grouped_plan_bytes")
+    host = np.zeros(nbytes, np.uint8)
+    _check(lib().bt_grouped_plan(arr, len(problems), host.ctypes.data,
+                                 nbytes), "bt_grouped_plan")
+    if device is None:
+        device = problems[0]["x_q"].device
+    dev = torch.from_numpy(host).to(device)
+    return GroupedPlan(host, dev, keep)
+
+
+def bt_gemm_grouped(plan: GroupedPlan, stream=None):
+    torch = _torch()
+    _check(lib().bt_gemm_grouped(_dev(plan.dev, torch.uint8, "plan"),
+                                 plan.host.ctypes.data, _stream(stream)),
+           "bt_gemm_grouped")

@@ -1,0 +1,85 @@
+// Internal declarations shared by the library's HIP translation units.
+// Device code targets gfx950 (CDNA4) only.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "bt.h"
+
+namespace bt {
+
+// One problem as the kernels see it (the grouped plan stores an array of
+// these in device memory; single calls pass one by value).
+struct alignas(16) Desc {
+  const uint8_t* w;   // packed weights, 64-row-tiled layout
+  const int8_t* xq;   // int8 activations [m, k]
+  const float* sa;    // activation scales [m]
+  float* y;           // fp32 outputs [m, n]
+  int32_t* acc;       // int32 accumulators [m, n] or nullptr
+  float sw;           // weight scale
+  int32_t n, k, m;
+  int32_t nblk;       // 64-row blocks = ceil(n / 64)
+  int32_t ntt;        // 32-token tiles = ceil(m / 32) (matrix-core path)
+  // grouped streaming path: position of this problem in the concatenated
+  // stream of 1 KiB chunks, and its first row block in the scratch area
+  int64_t chunk0;
+  int32_t blk0;
+  int32_t kc;         // k / 64 = chunks per row block
+  int64_t pad[2];
+};
+static_assert(sizeof(Desc) == 96, "Desc is 96 bytes");
+
+// One work unit of a grouped launch: problem index and a sub-index whose
+// meaning depends on the kernel (row block, or row block * ntt + token tile).
+struct Unit {
+  int32_t prob;
+  int32_t sub;
+};
+
+// Host-side header at the start of a grouped plan image.  Layout:
+//   PlanHeader | Desc[count] | int64 chunk0[count] | Unit[units] |
+//   int32 scratch_acc[blocks * m * 64] | int32 scratch_cnt[blocks]
+// (the streaming kind has units = 0; the matrix-core kind has no scratch).
+struct PlanHeader {
+  uint32_t magic;
+  int32_t count;
+  int32_t m;
+  int32_t kind;        // kKindDot4 or kKindMfma
+  int64_t units;
+  int64_t desc_off;    // byte offset of Desc[count]
+  int64_t chunk_off;   // byte offset of int64 chunk0[count]
+  int64_t unit_off;    // byte offset of Unit[units]
+  int64_t sacc_off;    // byte offset of the int32 partial sums
+  int64_t scnt_off;    // byte offset of the int32 arrival counters
+  int64_t bytes;       // total image size
+  int64_t total_chunks;
+  int64_t blocks;      // row blocks over all problems
+  int64_t pad[5];
+};
+static_assert(sizeof(PlanHeader) == 128, "PlanHeader is 128 bytes");
+
+constexpr uint32_t kPlanMagic = 0x31475442u;  // "BTG1"
+constexpr int kKindDot4 = 0;   // m <= 4: packed dot products
+constexpr int kKindMfma = 1;   // m > 4: int8 matrix cores
+constexpr int kDot4MaxM = 4;
+#ifndef BT_STREAM_WG_PER_CU
+#define BT_STREAM_WG_PER_CU 4
+#endif
+constexpr int kStreamWgPerCu = BT_STREAM_WG_PER_CU;  // persistent grid: WGs/CU
+
+// Launchers (host code in the kernels' translation units).
+hipError_t launch_pack(const int8_t* t, int64_t n, int64_t k, uint8_t* packed,
+                       int32_t* n_invalid, hipStream_t s);
+hipError_t launch_quant(const float* x, int64_t m, int64_t k, int8_t* xq,
+                        float* sa, hipStream_t s);
+hipError_t launch_dot4(const Desc& d, hipStream_t s);
+hipError_t launch_stream_grouped(const Desc* descs, const int64_t* chunk0,
+                                 int32_t count, int64_t total_chunks, int m,
+                                 int32_t* sacc, int32_t* scnt, int workgroups,
+                                 hipStream_t s);
+hipError_t launch_mfma(const Desc& d, hipStream_t s);
+hipError_t launch_mfma_grouped(const Desc* descs, const Unit* units,
+                               int64_t count, hipStream_t s);
+
+}  // namespace bt

@@ -1,0 +1,426 @@
+// Grouped ternary GEMV / very skinny GEMM (m <= 4) over many independent
+// problems in one persistent launch: the decode step of a ternary model.
+//
+// The step is bound by HBM bandwidth: every packed weight is read once and
+// used m <= 4 times ("1bit-systems" page, section "性能实测：92%的内存带宽
+// 利用率": the ternary GEMV saturates memory; only reading fewer bytes makes
+// it faster).  The kernel is therefore organised around the read stream:
+//
+//  * All problems' packed weights, in the 64-row-tiled layout, form one
+//    logical stream of 1 KiB chunks (chunk = 64 rows x 64 inputs).  Inside a
+//    problem, chunk L is at byte offset L * 1024, row block L / kc, input
+//    chunk L % kc.
+//  * The grid is persistent (a few workgroups per CU).  Wave w of W streams
+//    chunks [w T / W, (w + 1) T / W): every wave reads the same number of
+//    bytes, whatever the problem shapes, so the launch ends evenly.
+//  * Lane l of a wave owns row 64 rb + l; for chunk L it loads 16 bytes with
+//    one non-temporal 128-bit load (the wave reads 1 contiguous KiB); a wave
+//    issues a group of D chunks, then consumes them, and the other resident
+//    waves keep HBM busy meanwhile.
+//  * The 64 activation bytes of a chunk are the same for every lane: scalar
+//    loads bring them into SGPRs and v_dot4_i32_i8 takes them as an operand.
+//    Each 2-bit field is masked in place (field j holds 4^j * code) and has
+//    its own accumulator, combined with exact shifts at the end of a row
+//    block.  Codes c = trit + 1 are used as they are; the finalising wave
+//    subtracts the token's activation sum (sum (c - 1) q = sum c q - sum q;
+//    bitnet.cpp CPU tutorial §1.1 for the sign-and-accumulate product).
+//  * A row block cut by a wave-range boundary is shared by 2+ waves: each
+//    adds its int32 partial sums into a scratch slot with device-scope
+//    atomics (integer addition is exact and order-free), the last to arrive
+//    (arrival counter) reads the total, writes the outputs and clears the
+//    slot and counter for the next launch.
+#include "bt_internal.h"
+
+namespace bt {
+namespace {
+
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
+typedef const __attribute__((address_space(4))) int* const_iptr;
+typedef const __attribute__((address_space(4))) float* const_fptr;
+typedef const __attribute__((address_space(1))) v4u* gv4u_ptr;
+typedef __attribute__((address_space(1))) float* gfloat_ptr;
+typedef __attribute__((address_space(1))) int32_t* gint_ptr;
+typedef const __attribute__((address_space(1))) int* gcint_ptr;
+typedef const __attribute__((address_space(1))) float* gcfloat_ptr;
+
+constexpr int D = 8;  // chunks per load group (two groups in flight)
+
+__device__ __forceinline__ int sdot4(int a, int b, int c) {
+  return __builtin_amdgcn_sdot4(a, b, c, false);
+}
+
+// Sum over the 64 lanes, returned in a scalar register: DPP adds within each
+// row of 16 lanes, then the four row totals are read out.
+__device__ __forceinline__ int wave_sum(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false);  // quad 1032
+  v += __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false);  // quad 2301
+  v += __builtin_amdgcn_update_dpp(0, v, 0x141, 0xF, 0xF, false); // half mirror
+  v += __builtin_amdgcn_update_dpp(0, v, 0x140, 0xF, 0xF, false); // mirror
+  return __builtin_amdgcn_readlane(v, 0) + __builtin_amdgcn_readlane(v, 16) +
+         __builtin_amdgcn_readlane(v, 32) + __builtin_amdgcn_readlane(v, 48);
+}
+
+// Index of the last problem whose first chunk is <= pos (chunk0 ascending).
+// Every lane reads 4 entries per round, so up to 256 problems take a single
+// memory round trip.
+__device__ __forceinline__ int find_problem(const int64_t* chunk0, int count,
+                                            int64_t pos) {
+  const int lane = threadIdx.x & 63;
+  int p = 0;
+  for (int base = 0; base < count; base += 256) {
+    int64_t v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = base + u * 64 + lane;
+      v[u] = i < count ? chunk0[i] : INT64_MAX;
+    }
+    bool more = true;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const uint64_t mask = __ballot(v[u] <= pos);
+      p += __popcll(mask);
+      more = more && mask == ~0ull;
+    }
+    if (!more) break;
+  }
+  return __builtin_amdgcn_readfirstlane(p - 1);
+}
+
+// Owner wave of global chunk x when T chunks are split over W waves.
+__device__ __forceinline__ int64_t owner(int64_t x, int64_t W, int64_t T) {
+  return ((x + 1) * W - 1) / T;
+}
+
+template <int TOK>
+struct Acc {
+  int f[4][TOK];  // per 2-bit field j: sum of (4^j * code) * q
+  __device__ __forceinline__ void zero() {
+#pragma unroll
+    for (int t = 0; t < TOK; ++t) f[0][t] = f[1][t] = f[2][t] = f[3][t] = 0;
+  }
+  __device__ __forceinline__ int total(int t) const {
+    return f[0][t] + (f[1][t] >> 2) + (f[2][t] >> 4) + f[3][t];
+  }
+  // Empty volatile asm that reads and writes every accumulator: the dot
+  // products issued so far complete before any later volatile asm, which
+  // keeps each pair of chunks' work in program order.
+  __device__ __forceinline__ void pin() {
+#pragma unroll
+    for (int t = 0; t < TOK; ++t)
+      asm volatile("" : "+v"(f[0][t]), "+v"(f[1][t]), "+v"(f[2][t]),
+                   "+v"(f[3][t]));
+  }
+};
+
+// A run of cnt <= D consecutive chunks inside row block rb, starting at input
+// chunk c (problem-local chunk index rb * kc + c).  All 32-bit and uniform.
+struct Group {
+  int rb, c, cnt;
+  // Re-assert that the fields are wave-uniform (scalar registers); without
+  // it the compiler keeps the loop-carried copies in VGPRs, where its
+  // bookkeeping would overwrite registers of loads still in flight.
+  __device__ __forceinline__ void uniform() {
+    rb = __builtin_amdgcn_readfirstlane(rb);
+    c = __builtin_amdgcn_readfirstlane(c);
+    cnt = __builtin_amdgcn_readfirstlane(cnt);
+  }
+};
+
+template <int TOK>
+struct Stream {
+  // problem
+  gv4u_ptr w;        // this lane's 16 bytes of chunk 0
+  const int8_t* xq;
+  const_fptr sa;     // scalar loads: a vector load would wait behind the
+                     // weight loads in flight
+  gfloat_ptr y;
+  gint_ptr accout;
+  float sw;
+  int n, k, kc, blk0;
+  int64_t chunk0;
+  // wave range (global chunks) and grid
+  int64_t lo, hi, W, T;
+  int32_t* sacc;
+  int32_t* scnt;
+  int qsum[TOK];
+
+  // Next group after g in a segment ending at problem-local chunk s1.
+  __device__ __forceinline__ Group next(Group g, int s1) const {
+    Group r;
+    r.rb = g.rb;
+    r.c = g.c + g.cnt;
+    if (r.c == kc) {
+      r.c = 0;
+      ++r.rb;
+    }
+    r.cnt = max(0, min(min(D, kc - r.c), s1 - (r.rb * kc + r.c)));
+    r.uniform();
+    return r;
+  }
+
+  // Loads are unconditional (addresses clamped to chunk `last`); a clamped
+  // load re-reads a line that is already cached.
+  __device__ __forceinline__ void load_group(v4u (&buf)[D], Group g,
+                                             int last) const {
+    const int start = g.rb * kc + g.c;
+#pragma unroll
+    for (int j = 0; j < D; ++j) {
+      const int L = min(start + j, last);
+      buf[j] = __builtin_nontemporal_load(w + (size_t)L * 64);
+    }
+  }
+
+  // Chunk with input-chunk index c; keep = 0 discards it (all codes 0, which
+  // contribute nothing) without a branch: the masks are scalar registers.
+  __device__ __forceinline__ void dot_chunk(const v4u& wv, int c,
+                                            uint32_t keep, int pin,
+                                            Acc<TOK>& a) const {
+    const uint32_t m0 = 0x03030303u & keep, m1 = 0x0C0C0C0Cu & keep,
+                   m2 = 0x30303030u & keep;
+    const uint32_t words[4] = {wv.x, wv.y, wv.z, wv.w};
+#pragma unroll
+    for (int t = 0; t < TOK; ++t) {
+      const_iptr q =
+          (const_iptr)(xq + (size_t)t * k + (size_t)c * 64 + pin);
+#pragma unroll
+      for (int ww = 0; ww < 4; ++ww) {
+        const int e0 = (int)(words[ww] & m0);
+        const int e1 = (int)(words[ww] & m1);
+        const int e2 = (int)(words[ww] & m2);
+        const int e3 = (int)((words[ww] >> 6) & m0);
+        a.f[0][t] = sdot4(e0, q[4 * ww + 0], a.f[0][t]);
+        a.f[1][t] = sdot4(e1, q[4 * ww + 1], a.f[1][t]);
+        a.f[2][t] = sdot4(e2, q[4 * ww + 2], a.f[2][t]);
+        a.f[3][t] = sdot4(e3, q[4 * ww + 3], a.f[3][t]);
+      }
+    }
+  }
+
+  // All D chunks are consumed unconditionally (chunks past g.cnt are masked
+  // out and read a clamped activation chunk), so the compiler keeps every
+  // load of the group ahead of the first use instead of sinking loads into
+  // branches.  Each pair of chunks is pinned in order (opaque zero on the
+  // activation addresses before, accumulator pin after), so the scalar
+  // activation loads of at most two chunks (32 SGPRs per token) are live.
+  __device__ __forceinline__ void consume(const v4u (&buf)[D], Group g,
+                                          Acc<TOK>& a) const {
+    int pin = 0;
+#pragma unroll
+    for (int j = 0; j < D; ++j) {
+      if (j % 2 == 0) {
+        // an opaque zero (scalar register) added to the activation address:
+        // the two chunks' loads cannot move above this point
+        asm volatile("s_mov_b32 %0, 0" : "=s"(pin));
+      }
+      const uint32_t keep = j < g.cnt ? 0xFFFFFFFFu : 0u;
+      dot_chunk(buf[j], min(g.c + j, kc - 1), keep, pin, a);
+      if (j % 2 == 1) a.pin();
+    }
+  }
+
+  __device__ __forceinline__ void write_rows(int rb, const int (&sum)[TOK]) {
+    const int row = rb * 64 + (threadIdx.x & 63);
+    if (row >= n) return;
+#pragma unroll
+    for (int t = 0; t < TOK; ++t) {
+      const int acc = sum[t] - qsum[t];
+      const size_t o = (size_t)t * n + row;
+      if (accout != nullptr) accout[o] = acc;
+      y[o] = __fmul_rn(__fmul_rn((float)acc, sw), sa[t]);
+    }
+  }
+
+  // Row block rb lies entirely in this wave's range: write its outputs.
+  __device__ __forceinline__ void finish_full(int rb, Acc<TOK>& a) {
+    int sum[TOK];
+#pragma unroll
+    for (int t = 0; t < TOK; ++t) sum[t] = a.total(t);
+    a.zero();
+    write_rows(rb, sum);
+  }
+
+  // This wave holds only part of row block rb (partial sums in sum[]): add
+  // them into the block's scratch slot; the last contributor writes the
+  // outputs.
+  __device__ __forceinline__ void finish_partial(int rb, int (&sum)[TOK]) {
+    const int lane = threadIdx.x & 63;
+    const int64_t first = chunk0 + (int64_t)rb * kc;
+    const int64_t last = first + kc - 1;
+    const int64_t slot = (int64_t)blk0 + rb;
+    int32_t* part = sacc + slot * (TOK * 64);
+#pragma unroll
+    for (int t = 0; t < TOK; ++t) atomicAdd(part + t * 64 + lane, sum[t]);
+    // The partial sums travel only through device-scope atomics, which are
+    // performed at the coherence point; waiting for this wave's atomics to
+    // complete orders them before its arrival.  (A full agent fence would
+    // also write back and invalidate the L2 of the XCD, which nothing here
+    // needs.)
+    __builtin_amdgcn_s_waitcnt(0);
+    const int contributors = (int)(owner(last, W, T) - owner(first, W, T) + 1);
+    int arrived = 0;
+    if (lane == 0) arrived = atomicAdd(scnt + slot, 1);
+    arrived = __builtin_amdgcn_readfirstlane(arrived);
+    if (arrived == contributors - 1) {
+#pragma unroll
+      for (int t = 0; t < TOK; ++t) sum[t] = atomicExch(part + t * 64 + lane, 0);
+      if (lane == 0) atomicExch(scnt + slot, 0);
+      write_rows(rb, sum);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+  }
+
+  // Sum of each token's activations (needed when finishing rows).  All
+  // loads are issued before any is used: one round trip for k <= 4096.
+  __device__ __forceinline__ void activation_sums() {
+    const int lane = threadIdx.x & 63;
+    const int n16 = k >> 4;  // 16-byte pieces per token row
+#pragma unroll
+    for (int t = 0; t < TOK; ++t) {
+      const gv4u_ptr q16 = (gv4u_ptr)(xq + (size_t)t * k);
+      int s = 0;
+      for (int i0 = 0; i0 < n16; i0 += 4 * 64) {
+        v4u v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int i = i0 + u * 64 + lane;
+          v[u] = i < n16 ? q16[i] : v4u{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          s = sdot4((int)v[u].x, 0x01010101, s);
+          s = sdot4((int)v[u].y, 0x01010101, s);
+          s = sdot4((int)v[u].z, 0x01010101, s);
+          s = sdot4((int)v[u].w, 0x01010101, s);
+        }
+      }
+      qsum[t] = wave_sum(s);
+    }
+  }
+
+  // Stream chunks [s0, s1) of the current problem (problem-local indices) in
+  // groups of D chunks, double buffered: while group i is consumed, group
+  // i + 1 is in flight.  Every load is unconditional (clamped), so the wait
+  // before each group is a fixed count (the other buffer's D loads), and the
+  // only other memory operations in the loop are the output stores at the
+  // end of each whole row block.  A row block cut by the range (at most the
+  // first and the last) keeps its partial sums in registers; their atomic
+  // hand-off happens after the loop.
+  __device__ __forceinline__ void segment(int s0, int s1) {
+    s0 = __builtin_amdgcn_readfirstlane(s0);
+    s1 = __builtin_amdgcn_readfirstlane(s1);
+    const int last = s1 - 1;
+    const int head_rb = s0 / kc;
+    const bool head_cut = s0 != head_rb * kc;  // first block starts early
+    int head_sum[TOK];
+#pragma unroll
+    for (int t = 0; t < TOK; ++t) head_sum[t] = 0;
+    Group g;
+    g.rb = head_rb;
+    g.c = s0 - head_rb * kc;
+    g.cnt = min(min(D, kc - g.c), s1 - s0);
+    g.uniform();
+    Group pg = next(g, s1);
+    Acc<TOK> a;
+    a.zero();
+    v4u A[D], B[D];
+    load_group(A, g, last);
+    load_group(B, pg, last);
+    activation_sums();  // its loads queue behind the first two groups
+    while (true) {
+      g.uniform();
+      pg.uniform();
+      consume(A, g, a);
+      if (g.c + g.cnt == kc) block_end(g.rb, head_rb, head_cut, head_sum, a);
+      pg = next(pg, s1);
+      load_group(A, pg, last);
+      g = next(g, s1);
+      if (g.cnt == 0) break;
+      consume(B, g, a);
+      if (g.c + g.cnt == kc) block_end(g.rb, head_rb, head_cut, head_sum, a);
+      pg = next(pg, s1);
+      load_group(B, pg, last);
+      g = next(g, s1);
+      if (g.cnt == 0) break;
+    }
+    // the cut head block's sums were stashed only if it also ended here;
+    // otherwise it is the last block and still sits in the accumulators
+    if (head_cut && (head_rb + 1) * kc <= s1) finish_partial(head_rb, head_sum);
+    if (s1 % kc != 0) {  // the range ends inside the last row block
+      int sum[TOK];
+#pragma unroll
+      for (int t = 0; t < TOK; ++t) sum[t] = a.total(t);
+      finish_partial((s1 - 1) / kc, sum);
+    }
+  }
+
+  __device__ __forceinline__ void block_end(int rb, int head_rb,
+                                            bool head_cut,
+                                            int (&head_sum)[TOK],
+                                            Acc<TOK>& a) {
+    if (head_cut && rb == head_rb) {
+#pragma unroll
+      for (int t = 0; t < TOK; ++t) head_sum[t] = a.total(t);
+      a.zero();
+    } else {
+      finish_full(rb, a);
+    }
+  }
+};
+
+template <int TOK>
+__global__ __launch_bounds__(256) void stream_kernel(
+    const Desc* __restrict__ descs, const int64_t* __restrict__ chunk0s,
+    int count, int64_t total, int32_t* sacc, int32_t* scnt) {
+  const int64_t W = (int64_t)gridDim.x * 4;
+  const int64_t wv =
+      (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  Stream<TOK> st;
+  st.lo = wv * total / W;
+  st.hi = (wv + 1) * total / W;
+  st.W = W;
+  st.T = total;
+  st.sacc = sacc;
+  st.scnt = scnt;
+  if (st.lo >= st.hi) return;
+  int p = find_problem(chunk0s, count, st.lo);
+  int64_t pos = st.lo;
+  while (pos < st.hi && p < count) {
+    const Desc& d = descs[p];
+    st.w = (gv4u_ptr)(d.w) + (threadIdx.x & 63);
+    st.xq = d.xq;
+    st.sa = (const_fptr)d.sa;
+    st.y = (gfloat_ptr)d.y;
+    st.accout = (gint_ptr)d.acc;
+    st.sw = d.sw;
+    st.n = d.n;
+    st.k = d.k;
+    st.kc = d.kc;
+    st.blk0 = d.blk0;
+    st.chunk0 = d.chunk0;
+    const int64_t chunks = (int64_t)d.nblk * d.kc;
+    const int64_t s0 = pos - d.chunk0;
+    const int64_t s1 = min(chunks, st.hi - d.chunk0);
+    st.segment((int)s0, (int)s1);
+    pos = d.chunk0 + s1;
+    ++p;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_stream_grouped(const Desc* descs, const int64_t* chunk0,
+                                 int32_t count, int64_t total_chunks, int m,
+                                 int32_t* sacc, int32_t* scnt, int workgroups,
+                                 hipStream_t s) {
+  const dim3 grid((unsigned)workgroups), block(256);
+  switch (m) {
+    case 1: stream_kernel<1><<<grid, block, 0, s>>>(descs, chunk0, count, total_chunks, sacc, scnt); break;
+    case 2: stream_kernel<2><<<grid, block, 0, s>>>(descs, chunk0, count, total_chunks, sacc, scnt); break;
+    case 3: stream_kernel<3><<<grid, block, 0, s>>>(descs, chunk0, count, total_chunks, sacc, scnt); break;
+    case 4: stream_kernel<4><<<grid, block, 0, s>>>(descs, chunk0, count, total_chunks, sacc, scnt); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace bt

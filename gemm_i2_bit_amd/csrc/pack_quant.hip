@@ -1,0 +1,138 @@
+// Packing of ternary weights and per-token int8 activation quantization.
+//
+// Packing: each weight takes 2 bits (bitnet.cpp CPU tutorial at m.qwbw.cn,
+// §1.1; the 2-bit format is called I2_S in "BitNet 1 位 LLM 独立推理引擎",
+// conversion paragraph).  Code = trit + 1; the 64-row-tiled byte layout is
+// stated in bt.h.
+//
+// Quantization: activations become 8-bit integers ("BitNet-rs" page, section
+// "技术实现细节"), one absmax scale per token; the rounding and scale
+// formula (round half to even, x * (127 / a), clamp +-127, a >= 1e-5) are the
+// readings stated in bt.h.
+#include "bt_internal.h"
+
+namespace bt {
+namespace {
+
+__device__ __forceinline__ int wave_sum(int v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+  return v;
+}
+
+// One thread per (row, 64-input chunk): reads 64 trits, writes one 16-byte
+// chunk of the packed layout.  Thread index L = (row block * kc + chunk) * 64
+// + row % 64 equals the chunk's position in the output, so stores coalesce.
+__global__ __launch_bounds__(256) void pack_kernel(const int8_t* __restrict__ t,
+                                                   int64_t n, int64_t k,
+                                                   int64_t total,
+                                                   uint8_t* __restrict__ packed,
+                                                   int32_t* n_invalid) {
+  const int64_t L = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t kc = k >> 6;
+  int bad = 0;
+  if (L < total) {
+    const int64_t r64 = L & 63;
+    const int64_t bc = L >> 6;
+    const int64_t c = bc % kc;
+    const int64_t row = (bc / kc) * 64 + r64;
+    uint32_t word[4] = {0x55555555u, 0x55555555u, 0x55555555u, 0x55555555u};
+    if (row < n) {
+      const int4* src = reinterpret_cast<const int4*>(t + row * k + c * 64);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        // 16 consecutive trits: inputs 64 c + 16 w + 4 j + i (j, i < 4)
+        const int4 v = src[w];
+        const int32_t d4[4] = {v.x, v.y, v.z, v.w};
+        uint32_t out = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int trit = (int8_t)((uint32_t)d4[j] >> (8 * i));
+            uint32_t code = (uint32_t)(trit + 1);
+            if (code > 2u) {
+              code = 3u;
+              ++bad;
+            }
+            out |= code << (8 * i + 2 * j);
+          }
+        }
+        word[w] = out;
+      }
+    }
+    uint4 o;
+    o.x = word[0];
+    o.y = word[1];
+    o.z = word[2];
+    o.w = word[3];
+    reinterpret_cast<uint4*>(packed)[L] = o;
+  }
+  if (n_invalid != nullptr) {
+    bad = wave_sum(bad);
+    if ((threadIdx.x & 63) == 0 && bad != 0) atomicAdd(n_invalid, bad);
+  }
+}
+
+// One workgroup per token row.  Pass 1: absmax; pass 2: scale, round half to
+// even, clamp, store int8 (4 per 32-bit store).
+__global__ __launch_bounds__(256) void quant_kernel(const float* __restrict__ x,
+                                                    int64_t k,
+                                                    int8_t* __restrict__ xq,
+                                                    float* __restrict__ sa) {
+  __shared__ float part[4];
+  const int64_t row = blockIdx.x;
+  const float4* xr = reinterpret_cast<const float4*>(x + row * k);
+  const int64_t k4 = k >> 2;
+  float amax = 0.0f;
+  for (int64_t i = threadIdx.x; i < k4; i += 256) {
+    const float4 v = xr[i];
+    amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)),
+                             fmaxf(fabsf(v.z), fabsf(v.w))));
+  }
+  amax = wave_max(amax);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(part[0], part[1]), fmaxf(part[2], part[3]));
+  const float a = fmaxf(amax, 1e-5f);
+  const float inv = __fdiv_rn(127.0f, a);
+  int32_t* qr = reinterpret_cast<int32_t*>(xq + row * k);
+  for (int64_t i = threadIdx.x; i < k4; i += 256) {
+    const float4 v = xr[i];
+    const float e[4] = {v.x, v.y, v.z, v.w};
+    uint32_t packed4 = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float r = rintf(__fmul_rn(e[j], inv));  // round half to even
+      r = fminf(fmaxf(r, -127.0f), 127.0f);
+      packed4 |= ((uint32_t)(int32_t)r & 0xffu) << (8 * j);
+    }
+    qr[i] = (int32_t)packed4;
+  }
+  if (threadIdx.x == 0) sa[row] = __fdiv_rn(a, 127.0f);
+}
+
+}  // namespace
+
+hipError_t launch_pack(const int8_t* t, int64_t n, int64_t k, uint8_t* packed,
+                       int32_t* n_invalid, hipStream_t s) {
+  const int64_t total = (n + 63) / 64 * (k >> 6) * 64;
+  const int64_t blocks = (total + 255) / 256;
+  pack_kernel<<<dim3((unsigned)blocks), dim3(256), 0, s>>>(t, n, k, total,
+                                                           packed, n_invalid);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant(const float* x, int64_t m, int64_t k, int8_t* xq,
+                        float* sa, hipStream_t s) {
+  quant_kernel<<<dim3((unsigned)m), dim3(256), 0, s>>>(x, k, xq, sa);
+  return hipGetLastError();
+}
+
+}  // namespace bt

@@ -48,8 +48,8 @@ def lib() -> ctypes.CDLL:
         L.oracle_unpack_i2s.restype = i64
         L.oracle_quant_act.argtypes = [p, i64, i64, p, p]
         L.oracle_quant_act.restype = i32
-        L.oracle_gemm.argtypes = [p, ctypes.c_float, i64, i64, i64, p, p, p, p,
-                                  i32]
+        L.oracle_gemm.argtypes = [p, ctypes.c_float, i64, i64, i64, p, p, i64,
+                                  i64, p, p, i32]
         L.oracle_gemm.restype = i32
         _lib = L
     return _lib
@@ -73,23 +73,27 @@ def ternarize_absmean(w):
     return t, np.float32(s[0])
 
 
+def packed_bytes(n: int, k: int) -> int:
+    """Size of the O2 layout: rows padded to a multiple of 64, 2 bits each."""
+    return (n + 63) // 64 * 64 * k // 4
+
+
 def pack_i2s(t):
-    """O2: int8 trits [n, k] -> (uint8 packed [n, k/4], invalid count)."""
+    """O2: int8 trits [n, k] -> (uint8 packed, flat, invalid count)."""
     t = _c(t, np.int8)
     n, k = t.shape
-    if k % 16:
-        raise ValueError("k must be a multiple of 16")
-    out = np.empty((n, k // 4), np.uint8)
+    if k % 64:
+        raise ValueError("k must be a multiple of 64")
+    out = np.empty(packed_bytes(n, k), np.uint8)
     bad = lib().oracle_pack_i2s(_ptr(t), n, k, _ptr(out))
     return out, int(bad)
 
 
-def unpack_i2s(packed, k: int):
-    """O2 inverse: uint8 [n, k/4] -> (int8 trits [n, k], invalid count)."""
-    packed = _c(packed, np.uint8)
-    n = packed.shape[0]
-    if packed.shape[1] * 4 != k:
-        raise ValueError("packed row length does not match k")
+def unpack_i2s(packed, n: int, k: int):
+    """O2 inverse: packed bytes -> (int8 trits [n, k], invalid count)."""
+    packed = _c(packed, np.uint8).ravel()
+    if packed.size != packed_bytes(n, k):
+        raise ValueError("packed size does not match n, k")
     t = np.empty((n, k), np.int8)
     bad = lib().oracle_unpack_i2s(_ptr(packed), n, k, _ptr(t))
     return t, int(bad)
@@ -107,26 +111,25 @@ def quant_act(x):
     return q, s
 
 
-def gemm(packed, s_w, k: int, q, s_a, nthreads: int = 1, rows=None):
-    """O4 + O5: (int32 acc [m, n], float64 y [m, n]).
+def gemm(packed, s_w, n: int, k: int, q, s_a, nthreads: int = 1, rows=None):
+    """O4 + O5: (int32 acc [m, r1-r0], float64 y [m, r1-r0]).
 
-    ``rows`` = (r0, r1) restricts the product to output rows r0..r1-1 of the
-    packed matrix (used to compute samples at full sizes)."""
-    packed = _c(packed, np.uint8)
+    ``rows`` = (r0, r1) restricts the product to output rows r0..r1-1 (used to
+    compute samples at full sizes); the default is every row."""
+    packed = _c(packed, np.uint8).ravel()
     q = _c(q, np.int8)
     if q.ndim == 1:
         q = q[None, :]
     s_a = _c(np.atleast_1d(s_a), np.float32)
-    if rows is not None:
-        packed = np.ascontiguousarray(packed[rows[0]:rows[1]])
-    n = packed.shape[0]
     m = q.shape[0]
-    if packed.shape[1] * 4 != k or q.shape[1] != k or s_a.shape[0] != m:
+    r0, r1 = (0, n) if rows is None else rows
+    if (packed.size != packed_bytes(n, k) or q.shape[1] != k
+            or s_a.shape[0] != m):
         raise ValueError("shape mismatch")
-    acc = np.empty((m, n), np.int32)
-    y = np.empty((m, n), np.float64)
+    acc = np.empty((m, r1 - r0), np.int32)
+    y = np.empty((m, r1 - r0), np.float64)
     rc = lib().oracle_gemm(_ptr(packed), float(np.float32(s_w)), n, k, m,
-                           _ptr(q), _ptr(s_a), _ptr(acc), _ptr(y),
+                           _ptr(q), _ptr(s_a), r0, r1, _ptr(acc), _ptr(y),
                            int(nthreads))
     if rc != 0:
         raise ValueError(f"oracle_gemm failed with {rc}")

@@ -43,23 +43,28 @@ int oracle_ternarize_absmean(const float* w, int64_t n, int64_t k, int8_t* t,
  * bitnet.cpp CPU tutorial, §1.1: each ternary weight is stored in 2 bits.
  * "BitNet 1 位 LLM 独立推理引擎" (conversion paragraph): this generic 2-bit
  * format is I2_S.  The byte layout is this library's reading (header). */
-static int64_t byte_of(int64_t k) { return 4 * (k / 16) + (k % 4); }
-static int shift_of(int64_t k) { return (int)(2 * ((k % 16) / 4)); }
+static int64_t offset_of(int64_t r, int64_t c, int64_t k) {
+  return (r / 64) * 16 * k + (c / 64) * 1024 + (r % 64) * 16 +
+         4 * ((c % 64) / 16) + (c % 4);
+}
+static int shift_of(int64_t c) { return (int)(2 * ((c % 16) / 4)); }
 
 int64_t oracle_pack_i2s(const int8_t* t, int64_t n, int64_t k,
                         uint8_t* packed) {
-  const int64_t row_bytes = k / 4;
+  const int64_t rows_padded = (n + 63) / 64 * 64;
   int64_t invalid = 0;
-  for (int64_t i = 0; i < n * row_bytes; ++i) packed[i] = 0;
-  for (int64_t r = 0; r < n; ++r) {
+  for (int64_t i = 0; i < rows_padded * k / 4; ++i) packed[i] = 0;
+  for (int64_t r = 0; r < rows_padded; ++r) {
     for (int64_t c = 0; c < k; ++c) {
-      const int8_t v = t[r * k + c];
-      unsigned code;
-      if (v == -1) code = 0;
-      else if (v == 0) code = 1;
-      else if (v == 1) code = 2;
-      else { code = 3; ++invalid; }
-      packed[r * row_bytes + byte_of(c)] |= (uint8_t)(code << shift_of(c));
+      unsigned code = 1;                       /* padding rows: trit 0 */
+      if (r < n) {
+        const int8_t v = t[r * k + c];
+        if (v == -1) code = 0;
+        else if (v == 0) code = 1;
+        else if (v == 1) code = 2;
+        else { code = 3; ++invalid; }
+      }
+      packed[offset_of(r, c, k)] |= (uint8_t)(code << shift_of(c));
     }
   }
   return invalid;
@@ -67,12 +72,10 @@ int64_t oracle_pack_i2s(const int8_t* t, int64_t n, int64_t k,
 
 int64_t oracle_unpack_i2s(const uint8_t* packed, int64_t n, int64_t k,
                           int8_t* t) {
-  const int64_t row_bytes = k / 4;
   int64_t invalid = 0;
   for (int64_t r = 0; r < n; ++r) {
     for (int64_t c = 0; c < k; ++c) {
-      const unsigned code =
-          (packed[r * row_bytes + byte_of(c)] >> shift_of(c)) & 3u;
+      const unsigned code = (packed[offset_of(r, c, k)] >> shift_of(c)) & 3u;
       if (code == 3) { ++invalid; t[r * k + c] = 2; }
       else t[r * k + c] = (int8_t)((int)code - 1);
     }
@@ -115,7 +118,7 @@ int oracle_quant_act(const float* x, int64_t m, int64_t k, int8_t* q,
 typedef struct {
   const uint8_t* packed;
   float s_w;
-  int64_t n, k, m;
+  int64_t k, m, width, base;
   const int8_t* q;
   const float* s_a;
   int32_t* acc;
@@ -126,39 +129,41 @@ typedef struct {
 
 static void* gemm_rows(void* arg) {
   gemm_job* j = (gemm_job*)arg;
-  const int64_t row_bytes = j->k / 4;
   for (int64_t r = j->r0; r < j->r1; ++r) {
     for (int64_t i = 0; i < j->m; ++i) {
       int64_t sum = 0;
       for (int64_t c = 0; c < j->k; ++c) {
         const unsigned code =
-            (j->packed[r * row_bytes + byte_of(c)] >> shift_of(c)) & 3u;
+            (j->packed[offset_of(r, c, j->k)] >> shift_of(c)) & 3u;
         if (code == 3) { j->status = -2; return NULL; }
         const int64_t trit = (int64_t)code - 1;
         sum += trit * (int64_t)j->q[i * j->k + c];
       }
       if (sum > INT32_MAX || sum < INT32_MIN) { j->status = -1; return NULL; }
-      if (j->acc) j->acc[i * j->n + r] = (int32_t)sum;
-      if (j->y)
-        j->y[i * j->n + r] = (double)sum * (double)j->s_w * (double)j->s_a[i];
+      const int64_t out = i * j->width + (r - j->base);
+      if (j->acc) j->acc[out] = (int32_t)sum;
+      if (j->y) j->y[out] = (double)sum * (double)j->s_w * (double)j->s_a[i];
     }
   }
   return NULL;
 }
 
 int oracle_gemm(const uint8_t* packed, float s_w, int64_t n, int64_t k,
-                int64_t m, const int8_t* q, const float* s_a, int32_t* acc,
-                double* y, int nthreads) {
+                int64_t m, const int8_t* q, const float* s_a, int64_t r0,
+                int64_t r1, int32_t* acc, double* y, int nthreads) {
+  if (r0 < 0 || r1 > n || r0 > r1) return -3;
+  const int64_t rows = r1 - r0;
   if (nthreads < 1) nthreads = 1;
-  if (nthreads > n) nthreads = n > 0 ? (int)n : 1;
+  if (nthreads > rows) nthreads = rows > 0 ? (int)rows : 1;
   gemm_job* jobs = (gemm_job*)calloc((size_t)nthreads, sizeof(gemm_job));
   pthread_t* tids = (pthread_t*)calloc((size_t)nthreads, sizeof(pthread_t));
   for (int t = 0; t < nthreads; ++t) {
     gemm_job* j = &jobs[t];
-    j->packed = packed; j->s_w = s_w; j->n = n; j->k = k; j->m = m;
+    j->packed = packed; j->s_w = s_w; j->k = k; j->m = m;
+    j->width = rows; j->base = r0;
     j->q = q; j->s_a = s_a; j->acc = acc; j->y = y;
-    j->r0 = n * t / nthreads;
-    j->r1 = n * (t + 1) / nthreads;
+    j->r0 = r0 + rows * t / nthreads;
+    j->r1 = r0 + rows * (t + 1) / nthreads;
     j->status = 0;
     if (t > 0) pthread_create(&tids[t], NULL, gemm_rows, j);
   }

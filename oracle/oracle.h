@@ -36,15 +36,18 @@ extern "C" {
 int oracle_ternarize_absmean(const float* w, int64_t n, int64_t k, int8_t* t,
                              float* s_w);
 
-/* O2: pack trits [n, k] (k % 16 == 0) into n * k / 4 bytes.
- * Code c = t + 1 in {0, 1, 2}.  Row r occupies bytes [r k/4, (r+1) k/4).
- * Weight k of a row sits in byte 4 (k / 16) + (k % 4) of the row, at bit
- * 2 ((k % 16) / 4).  Returns the number of entries outside {-1, 0, 1}; such
- * entries are stored as code 3 (the one code that no trit maps to). */
+/* O2: pack trits [n, k] (k % 64 == 0) into the 64-row-tiled 2-bit layout.
+ * Code c = t + 1 in {0, 1, 2}.  Rows are padded to np = ceil(n / 64) * 64;
+ * padding rows hold code 1 (trit 0).  Row block b = r / 64 occupies bytes
+ * [b * 16 k, (b + 1) * 16 k); inside it, 16-byte chunk c = k / 64 of row
+ * r % 64 sits at offset c * 1024 + (r % 64) * 16; inside the chunk, weight k
+ * sits in byte 4 ((k % 64) / 16) + (k % 4) at bit 2 ((k % 16) / 4).
+ * Total size np * k / 4 bytes.  Returns the number of entries outside
+ * {-1, 0, 1}; such entries are stored as code 3 (no trit maps to it). */
 int64_t oracle_pack_i2s(const int8_t* t, int64_t n, int64_t k, uint8_t* packed);
 
-/* O2 inverse: unpack to trits.  Code 3 is invalid: it is written as the
- * value 2 (not a trit) and counted; returns the count. */
+/* O2 inverse: unpack the first n rows to trits.  Code 3 is invalid: it is
+ * written as the value 2 (not a trit) and counted; returns the count. */
 int64_t oracle_unpack_i2s(const uint8_t* packed, int64_t n, int64_t k,
                           int8_t* t);
 
@@ -56,13 +59,14 @@ int oracle_quant_act(const float* x, int64_t m, int64_t k, int8_t* q,
 
 /* O4 + O5: acc[i, r] = sum_k trit(r, k) * q[i, k], exact (int64 sum, checked
  * to fit int32); y[i, r] = acc * s_w * s_a[i] evaluated in double.
- * packed is [n, k/4] in the O2 layout, q is [m, k], acc and y are [m, n]
- * (either may be NULL).  Output rows are split over `nthreads` threads in
- * contiguous slices; each output is computed by the same plain loop.
+ * packed holds n rows in the O2 layout, q is [m, k].  Only output rows
+ * r0 <= r < r1 are computed; acc and y are [m, r1 - r0] (either may be NULL).
+ * The rows are split over `nthreads` threads in contiguous slices; each
+ * output is computed by the same plain loop.
  * Returns 0, -1 if an accumulator left int32, -2 on an invalid code. */
 int oracle_gemm(const uint8_t* packed, float s_w, int64_t n, int64_t k,
-                int64_t m, const int8_t* q, const float* s_a, int32_t* acc,
-                double* y, int nthreads);
+                int64_t m, const int8_t* q, const float* s_a, int64_t r0,
+                int64_t r1, int32_t* acc, double* y, int nthreads);
 
 #ifdef __cplusplus
 }

@@ -1,0 +1,236 @@
+"""The C-ABI library loads, exports every declared symbol, and rejects bad
+arguments on the host before any HIP call.  CPU only: every call below fails
+an argument check first, so no kernel is launched and no pointer is used.
+
+Fake device pointers (small aligned integers) are only ever passed together
+with at least one argument that the host check rejects."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import gemm_i2_bit_amd as bt
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bt.h")
+
+P = 0x10000  # a 16-byte aligned fake address; never dereferenced here
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(bt_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(bt.LIB_PATH):
+        import importlib
+        build = importlib.import_module("gemm_i2_bit_amd.build")
+        build.build()
+    return bt.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    names = declared_functions()
+    assert {"bt_pack_i2s", "bt_quant_act", "bt_gemv", "bt_gemm",
+            "bt_gemm_grouped", "bt_grouped_plan"} <= set(names)
+    for name in names:
+        assert hasattr(L, name), name
+
+
+def test_status_strings(L):
+    for code in range(-6, 1):
+        assert len(bt.bt_status_str(code)) > 0
+    assert bt.bt_status_str(-99) == "unknown status"
+
+
+def test_packed_bytes(L):
+    assert L.bt_packed_bytes(512, 256) == 512 * 256 // 4
+    assert L.bt_packed_bytes(1, 64) == 64 * 16          # padded to 64 rows
+    assert L.bt_packed_bytes(70, 2560) == 128 * 640
+    assert L.bt_packed_bytes(2560, 6912) == 2560 * 6912 // 4
+    for n, k in [(0, 64), (1, 0), (1, 32), (1, 100), (1, 65536 + 64),
+                 (-5, 64), (1 << 29, 64)]:
+        assert L.bt_packed_bytes(n, k) == bt.BT_E_SHAPE
+
+
+def test_gemm_argument_errors(L):
+    g = L.bt_gemm
+    ok = dict(packed=P, s_w=0.5, n=64, k=64, m=1, x_q=P, s_a=P, y=P, acc=None)
+
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return g(a["packed"], a["s_w"], a["n"], a["k"], a["m"], a["x_q"],
+                 a["s_a"], a["y"], a["acc"], None)
+
+    assert call(packed=None, k=0) == bt.BT_E_NULL
+    assert call(x_q=None, k=0) == bt.BT_E_NULL
+    assert call(s_a=None, k=0) == bt.BT_E_NULL
+    assert call(y=None, k=0) == bt.BT_E_NULL
+    for bad in [dict(k=32), dict(k=100), dict(k=0), dict(k=65600),
+                dict(n=0), dict(m=0), dict(m=1 << 25), dict(n=1 << 29)]:
+        assert call(**bad) == bt.BT_E_SHAPE, bad
+    for bad in [dict(packed=P + 4), dict(x_q=P + 8), dict(y=P + 4),
+                dict(s_a=P + 2), dict(acc=P + 4)]:
+        assert call(k=64, s_w=float("nan"), **bad) == bt.BT_E_ALIGN, bad
+    for bad in [float("nan"), float("inf"), -1.0]:
+        assert call(s_w=bad, acc=P + 4) in (bt.BT_E_ALIGN,)  # align first
+        assert call(s_w=bad, n=0) == bt.BT_E_SHAPE
+    # the scale check itself, with everything else valid except alignment of
+    # nothing: use a NULL y so no HIP call can follow
+    assert call(s_w=-1.0, y=None) == bt.BT_E_NULL
+
+
+def test_scale_check_precedes_hip(L):
+    # all pointers valid-looking, shapes valid, scale invalid -> BT_E_ARG,
+    # returned before the device is queried (no HIP call, no launch)
+    for bad in [float("nan"), float("inf"), -0.5]:
+        assert L.bt_gemm(P, bad, 64, 64, 1, P, P, P, None, None) == bt.BT_E_ARG
+        assert L.bt_gemv(P, bad, 64, 64, P, P, P, None, None) == bt.BT_E_ARG
+
+
+def test_pack_and_quant_argument_errors(L):
+    assert L.bt_pack_i2s(None, 64, 64, P, None, None) == bt.BT_E_NULL
+    assert L.bt_pack_i2s(P, 64, 64, None, None, None) == bt.BT_E_NULL
+    assert L.bt_pack_i2s(P, 64, 63, P, None, None) == bt.BT_E_SHAPE
+    assert L.bt_pack_i2s(P, 0, 64, P, None, None) == bt.BT_E_SHAPE
+    assert L.bt_pack_i2s(P + 1, 64, 64, P, None, None) == bt.BT_E_ALIGN
+    assert L.bt_pack_i2s(P, 64, 64, P + 8, None, None) == bt.BT_E_ALIGN
+    assert L.bt_pack_i2s(P, 64, 64, P, P + 2, None) == bt.BT_E_ALIGN
+    assert L.bt_quant_act(None, 1, 64, P, P, None) == bt.BT_E_NULL
+    assert L.bt_quant_act(P, 1, 64, None, P, None) == bt.BT_E_NULL
+    assert L.bt_quant_act(P, 1, 64, P, None, None) == bt.BT_E_NULL
+    assert L.bt_quant_act(P, 0, 64, P, P, None) == bt.BT_E_SHAPE
+    assert L.bt_quant_act(P, 1, 96, P, P, None) == bt.BT_E_SHAPE
+    assert L.bt_quant_act(P + 4, 1, 64, P, P, None) == bt.BT_E_ALIGN
+    assert L.bt_quant_act(P, 1, 64, P + 4, P, None) == bt.BT_E_ALIGN
+    assert L.bt_quant_act(P, 1, 64, P, P + 1, None) == bt.BT_E_ALIGN
+
+
+# ------------------------------------------------------------ grouped plans
+def problems(specs):
+    arr = (bt.bt_problem * len(specs))()
+    for i, (n, k, m) in enumerate(specs):
+        base = P * (i + 1) * 16
+        arr[i] = bt.bt_problem(base, base + P, base + 2 * P, base + 3 * P,
+                               None, 0.25, n, k, m)
+    return arr
+
+
+HDR_FIELDS = ["units", "desc_off", "chunk_off", "unit_off", "sacc_off",
+              "scnt_off", "bytes", "total_chunks", "blocks"]
+
+
+def parse_plan(img):
+    magic, count, m, kind = np.frombuffer(img[:16].tobytes(), dtype=np.int32)
+    vals = np.frombuffer(img[16:16 + 8 * len(HDR_FIELDS)].tobytes(),
+                         dtype=np.int64)
+    p = dict(zip(HDR_FIELDS, (int(v) for v in vals)))
+    p.update(magic=int(magic) & 0xFFFFFFFF, count=int(count), m=int(m),
+             kind=int(kind))
+    u0 = p["unit_off"]
+    p["unit"] = np.frombuffer(img[u0:u0 + 8 * p["units"]].tobytes(),
+                              dtype=np.int32).reshape(-1, 2)
+    c0 = p["chunk_off"]
+    p["chunk0"] = np.frombuffer(img[c0:c0 + 8 * p["count"]].tobytes(),
+                                dtype=np.int64)
+    return p
+
+
+def desc(img, p, i):
+    base = p["desc_off"] + 96 * i
+    raw = img[base:base + 96]
+    ptrs = raw[:40].view(np.int64)
+    s_w = raw[40:44].view(np.float32)[0]
+    n, k, m, nblk, ntt = raw[44:64].view(np.int32)
+    chunk0 = raw[64:72].view(np.int64)[0]
+    blk0, kc = raw[72:80].view(np.int32)
+    return dict(ptrs=ptrs, s_w=s_w, n=n, k=k, m=m, nblk=nblk, ntt=ntt,
+                chunk0=chunk0, blk0=blk0, kc=kc)
+
+
+def test_grouped_plan_layout_stream(L):
+    specs = [(2560, 2560, 1), (640, 2560, 1), (2560, 6912, 1), (100, 64, 1)]
+    arr = problems(specs)
+    nbytes = L.bt_grouped_plan_bytes(arr, len(specs))
+    nblk = [(n + 63) // 64 for n, _, _ in specs]
+    kc = [k // 64 for _, k, _ in specs]
+    img = np.zeros(nbytes, np.uint8)
+    assert L.bt_grouped_plan(arr, len(specs), img.ctypes.data, nbytes) == 0
+    p = parse_plan(img)
+    assert p["magic"] == 0x31475442 and p["count"] == 4 and p["m"] == 1
+    assert p["kind"] == 0 and p["units"] == 0
+    assert p["blocks"] == sum(nblk)
+    assert p["total_chunks"] == sum(b * c for b, c in zip(nblk, kc))
+    assert p["desc_off"] == 256 and nbytes == p["bytes"]
+    for off in ("desc_off", "chunk_off", "unit_off", "sacc_off", "scnt_off",
+                "bytes"):
+        assert p[off] % 256 == 0
+    # scratch: 64 int32 partial sums per row block and token, one counter
+    assert p["scnt_off"] - p["sacc_off"] >= sum(nblk) * 64 * 4
+    assert p["bytes"] - p["scnt_off"] >= sum(nblk) * 4
+    assert not img[p["sacc_off"]:].any()
+    # problems keep their order; chunk and block offsets are prefix sums
+    prefix_c = np.cumsum([0] + [b * c for b, c in zip(nblk, kc)])[:-1]
+    prefix_b = np.cumsum([0] + nblk)[:-1]
+    assert p["chunk0"].tolist() == prefix_c.tolist()
+    for i, (n, k, m) in enumerate(specs):
+        d = desc(img, p, i)
+        assert d["ptrs"][0] == P * (i + 1) * 16
+        assert (d["n"], d["k"], d["m"]) == (n, k, m)
+        assert (d["nblk"], d["kc"]) == (nblk[i], kc[i])
+        assert d["chunk0"] == prefix_c[i] and d["blk0"] == prefix_b[i]
+        assert d["s_w"] == np.float32(0.25)
+
+
+def test_grouped_plan_layout_mfma(L):
+    specs = [(640, 2560, 40), (96, 6912, 40)]
+    arr = problems(specs)
+    nbytes = L.bt_grouped_plan_bytes(arr, 2)
+    img = np.zeros(nbytes, np.uint8)
+    assert L.bt_grouped_plan(arr, 2, img.ctypes.data, nbytes) == 0
+    p = parse_plan(img)
+    assert p["kind"] == 1 and p["units"] == 10 * 2 + 2 * 2
+    # largest reduction length first
+    assert p["unit"][0].tolist() == [1, 0]
+    assert p["unit"][4].tolist() == [0, 0]
+    assert p["scnt_off"] == p["sacc_off"]  # no scratch for this kind
+
+
+def test_grouped_plan_errors(L):
+    arr = problems([(64, 64, 1), (64, 64, 2)])
+    assert L.bt_grouped_plan_bytes(arr, 2) == bt.BT_E_SHAPE  # mixed m
+    assert L.bt_grouped_plan_bytes(arr, 0) == bt.BT_E_ARG
+    assert L.bt_grouped_plan_bytes(None, 1) == bt.BT_E_NULL
+    bad = problems([(64, 96, 1)])
+    assert L.bt_grouped_plan_bytes(bad, 1) == bt.BT_E_SHAPE
+    good = problems([(64, 64, 1)])
+    nbytes = L.bt_grouped_plan_bytes(good, 1)
+    img = np.zeros(nbytes, np.uint8)
+    assert L.bt_grouped_plan(good, 1, img.ctypes.data, nbytes - 1) == bt.BT_E_ARG
+    assert L.bt_grouped_plan(good, 1, None, nbytes) == bt.BT_E_NULL
+    # a launch with a corrupted host image is refused before any HIP call
+    assert L.bt_grouped_plan(good, 1, img.ctypes.data, nbytes) == 0
+    broken = img.copy()
+    broken[0] ^= 0xFF
+    assert L.bt_gemm_grouped(P, broken.ctypes.data, None) == bt.BT_E_ARG
+    broken = img.copy()
+    broken[8:12] = np.frombuffer(np.int32(7).tobytes(), np.uint8)  # m = 7
+    assert L.bt_gemm_grouped(P, broken.ctypes.data, None) == bt.BT_E_ARG
+    broken = img.copy()
+    broken[24:32] = np.frombuffer(np.int64(64).tobytes(), np.uint8)  # desc
+    assert L.bt_gemm_grouped(P, broken.ctypes.data, None) == bt.BT_E_ARG
+    assert L.bt_gemm_grouped(None, img.ctypes.data, None) == bt.BT_E_NULL
+    assert L.bt_gemm_grouped(P + 16, img.ctypes.data, None) == bt.BT_E_ALIGN
+
+
+def test_binding_rejects_host_tensors(L):
+    torch = pytest.importorskip("torch")
+    t = torch.zeros((64, 64), dtype=torch.int8)
+    with pytest.raises(TypeError):
+        bt.bt_pack_i2s(t, packed=torch.zeros(1024, dtype=torch.uint8))

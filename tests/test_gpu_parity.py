@@ -1,0 +1,269 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on the
+same seeded inputs.  Bit-exact for packed bytes, int8 activations, their
+scales and int32 accumulators; fp32 outputs within 1e-6 relative error of the
+oracle's float64 rescale (exactly 0 where the accumulator is 0).
+
+Inputs come from workloads.py (random numbers only).  Expected values come
+only from the oracle."""
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+bt = pytest.importorskip("gemm_i2_bit_amd")
+
+NTHREADS = min(16, os.cpu_count() or 1)
+RTOL = 1e-6
+GUARD = 4  # guard elements (16 bytes) on each side of every output
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    bt.lib()
+    oracle.lib()
+    return torch.device("cuda:0")
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to("cuda:0")
+
+
+def guarded(numel, dtype, fill):
+    buf = torch.full((numel + 2 * GUARD,), fill, dtype=dtype, device="cuda:0")
+    return buf, buf[GUARD:GUARD + numel]
+
+
+def check_guards(buf, fill):
+    host = buf.cpu()
+    head, tail = host[:GUARD], host[-GUARD:]
+    if buf.dtype == torch.float32:
+        assert torch.isnan(head).all() and torch.isnan(tail).all(), \
+            "write outside the output"
+    else:
+        assert (head == fill).all() and (tail == fill).all(), \
+            "write outside the output"
+
+
+def check_y(y_gpu, y_ref, acc_ref):
+    y_gpu = np.asarray(y_gpu, np.float64)
+    zero = acc_ref == 0
+    assert (y_gpu[zero] == 0).all()
+    nz = ~zero
+    rel = np.abs(y_gpu[nz] - y_ref[nz]) / np.abs(y_ref[nz])
+    assert rel.size == 0 or rel.max() <= RTOL, f"max rel err {rel.max()}"
+
+
+def gpu_product(t, x, s_w, guards=True):
+    """Pack, quantize and multiply on the GPU; return host arrays."""
+    n, k = t.shape
+    m = x.shape[0]
+    packed = bt.bt_pack_i2s(dev(t))
+    x_q, s_a = bt.bt_quant_act(dev(x))
+    ybuf, y = guarded(m * n, torch.float32, float("nan"))
+    abuf, acc = guarded(m * n, torch.int32, 0x7EADBEEF)
+    bt.bt_gemm(packed, s_w, n, k, x_q, s_a, y=y.view(m, n), acc=acc.view(m, n))
+    torch.cuda.synchronize()
+    if guards:
+        check_guards(ybuf, None)
+        check_guards(abuf, 0x7EADBEEF)
+    return (packed.cpu().numpy(), x_q.cpu().numpy(), s_a.cpu().numpy(),
+            acc.view(m, n).cpu().numpy(), y.view(m, n).cpu().numpy())
+
+
+def oracle_product(t, x, s_w, rows=None):
+    p, bad = oracle.pack_i2s(t)
+    assert bad == 0
+    q, s_a = oracle.quant_act(x)
+    acc, y = oracle.gemm(p, s_w, t.shape[0], t.shape[1], q, s_a,
+                         nthreads=NTHREADS, rows=rows)
+    return p, q, s_a, acc, y
+
+
+# ----------------------------------------------------------------- packing
+@pytest.mark.parametrize("n,k,dist", [
+    (512, 256, wl.UNIFORM), (70, 64, wl.UNIFORM), (130, 192, wl.DECODE_2B),
+    (2560, 2560, wl.DECODE_2B), (100, 6912, wl.SKEWED_8B), (1, 64, wl.UNIFORM)])
+def test_pack_matches_oracle(n, k, dist):
+    t = wl.trits(np.random.default_rng([100, n, k]), (n, k), dist)
+    p_ref, _ = oracle.pack_i2s(t)
+    p_gpu = bt.bt_pack_i2s(dev(t)).cpu().numpy()
+    np.testing.assert_array_equal(p_gpu, p_ref)
+
+
+def test_pack_counts_invalid():
+    t = np.zeros((70, 128), np.int8)
+    t[3, 5], t[69, 127], t[10, 64] = 2, -2, 100
+    n_bad = torch.zeros(1, dtype=torch.int32, device="cuda:0")
+    bt.bt_pack_i2s(dev(t), n_invalid=n_bad)
+    assert int(n_bad.item()) == 3
+
+
+# ------------------------------------------------------------ quantization
+def quant_cases():
+    rng = np.random.default_rng(101)
+    ties = np.zeros((1, 64), np.float32)
+    ties[0, :7] = [127, 2.5, -3.5, 0.5, -0.5, 1.5, -2.5]
+    zero_tiny = np.zeros((2, 128), np.float32)
+    zero_tiny[1, 7] = 1e-30
+    return [
+        ("single", wl.single_gemv()[2]),
+        ("outliers", wl.x_normal_outliers(rng, (1, 2560))),
+        ("batch8", wl.x_normal(rng, (8, 2560))),
+        ("student_t", wl.x_student_t(rng, (3, 6912))),
+        ("small", wl.x_normal(rng, (5, 64)) * np.float32(1e3)),
+        ("long", wl.x_normal(rng, (2, 14336))),
+        ("ties", ties),
+        ("zero_tiny", zero_tiny),
+        ("quarter_steps", np.round(wl.x_normal(rng, (4, 256)) * 4) / 4),
+    ]
+
+
+@pytest.mark.parametrize("name,x", quant_cases(), ids=lambda v: v if isinstance(v, str) else "")
+def test_quant_matches_oracle(name, x):
+    x = np.ascontiguousarray(x, np.float32)
+    q_ref, s_ref = oracle.quant_act(x)
+    q_gpu, s_gpu = bt.bt_quant_act(dev(x))
+    np.testing.assert_array_equal(q_gpu.cpu().numpy(), q_ref)
+    np.testing.assert_array_equal(s_gpu.cpu().numpy().view(np.uint32),
+                                  s_ref.view(np.uint32))
+
+
+# ------------------------------------------------------------- the product
+def test_pipeline_worked_example():
+    t = np.zeros((2, 64), np.int8)
+    t[0, :4] = [1, 0, -1, 1]
+    t[1, :4] = [-1, -1, 0, 1]
+    x = np.zeros((1, 64), np.float32)
+    x[0, :4] = [127, 2.5, -3.5, 0.5]
+    _, q, s_a, acc, y = gpu_product(t, x, 0.5)
+    assert q[0, :4].tolist() == [127, 2, -4, 0] and s_a[0] == 1.0
+    assert acc[0].tolist() == [131, -129]
+    assert y[0].tolist() == [65.5, -64.5]
+
+
+def test_single_gemv_config():
+    """M=1, K=256, N=512, seed 0, s_w = 0.02: every output."""
+    t, s_w, x = wl.single_gemv()
+    p, q, s_a, acc, y = gpu_product(t, x, s_w)
+    p_r, q_r, s_r, acc_r, y_r = oracle_product(t, x, s_w)
+    np.testing.assert_array_equal(p, p_r)
+    np.testing.assert_array_equal(q, q_r)
+    np.testing.assert_array_equal(s_a, s_r)
+    np.testing.assert_array_equal(acc, acc_r)
+    check_y(y, y_r, acc_r)
+
+
+@pytest.mark.parametrize("m", [1, 2, 3, 4, 5, 7, 8, 15, 16, 17, 31, 32, 33,
+                               63, 64, 65, 100])
+@pytest.mark.parametrize("n,k", [(200, 192), (64, 64), (130, 2560),
+                                 (70, 6912)])
+def test_gemm_matches_oracle(m, n, k):
+    rng = np.random.default_rng([102, m, n, k])
+    t = wl.trits(rng, (n, k), wl.DECODE_2B)
+    x = wl.x_normal_outliers(rng, (m, k))
+    s_w = wl.scale(rng, 0.01, 0.05)
+    p, q, s_a, acc, y = gpu_product(t, x, s_w)
+    p_r, q_r, s_r, acc_r, y_r = oracle_product(t, x, s_w)
+    np.testing.assert_array_equal(q, q_r)
+    np.testing.assert_array_equal(s_a, s_r)
+    np.testing.assert_array_equal(acc, acc_r)
+    check_y(y, y_r, acc_r)
+
+
+def test_gemm_extremes():
+    """All +1 against all 127 at the largest k: the int32 extreme; and all -1
+    rows, zero rows and an all-zero token."""
+    k, n, m = 65536, 66, 6
+    t = np.zeros((n, k), np.int8)
+    t[0] = 1
+    t[1] = -1
+    t[2:] = wl.trits(np.random.default_rng(103), (n - 2, k))
+    t[5] = 0
+    x = np.ones((m, k), np.float32)
+    x[1] = -1
+    x[2] = 0
+    x[3:] = wl.x_normal(np.random.default_rng(104), (m - 3, k))
+    for mm in (1, m):
+        p, q, s_a, acc, y = gpu_product(t, x[:mm], 1.0)
+        p_r, q_r, s_r, acc_r, y_r = oracle_product(t, x[:mm], 1.0)
+        assert acc[0, 0] == 127 * k and acc[0, 1] == -127 * k
+        np.testing.assert_array_equal(acc, acc_r)
+        check_y(y, y_r, acc_r)
+
+
+def test_gemv_entry_matches_gemm():
+    rng = np.random.default_rng(105)
+    t = wl.trits(rng, (300, 2560), wl.DECODE_2B)
+    x = wl.x_normal_outliers(rng, (1, 2560))
+    packed = bt.bt_pack_i2s(dev(t))
+    x_q, s_a = bt.bt_quant_act(dev(x))
+    y1, a1 = bt.bt_gemv(packed, 0.03, 300, 2560, x_q[0], s_a, want_acc=True)
+    y2, a2 = bt.bt_gemm(packed, 0.03, 300, 2560, x_q, s_a, want_acc=True)
+    torch.cuda.synchronize()
+    assert torch.equal(a1, a2) and torch.equal(y1, y2)
+    _, _, _, acc_r, y_r = oracle_product(t, x, np.float32(0.03))
+    np.testing.assert_array_equal(a1.cpu().numpy(), acc_r)
+
+
+# ------------------------------------------------------------ grouped calls
+def grouped_case(work, layers):
+    """Upload, pack and quantize `layers` layers of a workload; return the
+    problem dicts and the host inputs per problem."""
+    probs, host = [], []
+    for p in work.problems():
+        if p.layer >= layers:
+            continue
+        t, s_w = work.weights(p.layer, p.proj)
+        x = work.activations(p.layer, p.proj)
+        packed = bt.bt_pack_i2s(dev(t))
+        x_q, s_a = bt.bt_quant_act(dev(x))
+        y = torch.full((p.m, p.n), float("nan"), device="cuda:0")
+        acc = torch.full((p.m, p.n), 0x7EADBEEF, dtype=torch.int32,
+                         device="cuda:0")
+        probs.append(dict(packed=packed, s_w=s_w, n=p.n, k=p.k, x_q=x_q,
+                          s_a=s_a, y=y, acc=acc))
+        host.append((t, x, s_w))
+    return probs, host
+
+
+@pytest.mark.parametrize("m", [1, 3, 8, 32])
+def test_grouped_two_layers_match_oracle(m):
+    work = wl.decode_2b(m=m, layers=2)
+    probs, host = grouped_case(work, 2)
+    plan = bt.bt_grouped_plan(probs)
+    for _ in range(2):  # the plan is reusable
+        bt.bt_gemm_grouped(plan)
+    torch.cuda.synchronize()
+    for prob, (t, x, s_w) in zip(probs, host):
+        _, q_r, s_r, acc_r, y_r = oracle_product(t, x, s_w)
+        np.testing.assert_array_equal(prob["x_q"].cpu().numpy(), q_r)
+        np.testing.assert_array_equal(prob["acc"].cpu().numpy(), acc_r)
+        check_y(prob["y"].cpu().numpy(), y_r, acc_r)
+
+
+def test_prefill_layer_sampled():
+    """One 2B-shaped layer at M=512 (7 products): 24 sampled output rows per
+    projection against the oracle, all 512 tokens."""
+    work = wl.prefill_2b()
+    for p in work.problems():
+        t, s_w = work.weights(p.layer, p.proj)
+        x = work.activations(p.layer, p.proj)
+        _, q, s_a, acc, y = gpu_product(t, x, s_w)
+        rng = np.random.default_rng([106, wl.PROJ_NAMES.index(p.proj)])
+        starts = sorted(set(rng.integers(0, p.n - 8, size=3).tolist()))
+        for r0 in starts:
+            rows = (r0, r0 + 8)
+            q_r, s_r = oracle.quant_act(x)
+            pk, _ = oracle.pack_i2s(t[r0:r0 + 8])
+            acc_r, y_r = oracle.gemm(pk, s_w, 8, p.k, q_r, s_r,
+                                     nthreads=NTHREADS)
+            np.testing.assert_array_equal(acc[:, r0:r0 + 8], acc_r)
+            check_y(y[:, r0:r0 + 8], y_r, acc_r)

@@ -104,9 +104,18 @@ def test_absmean_all_zero(orc):
 # ------------------------------------------------------------------ O2
 def test_pack_closed_forms(orc):
     for trit, byte in [(0, 0x55), (1, 0xAA), (-1, 0x00)]:
-        p, bad = orc.pack_i2s(np.full((3, 64), trit, np.int8))
-        assert bad == 0 and p.shape == (3, 16)
+        p, bad = orc.pack_i2s(np.full((64, 128), trit, np.int8))
+        assert bad == 0 and p.shape == (64 * 128 // 4,)
         assert (p == byte).all()
+
+
+def test_pack_padding_rows_are_zero_trits(orc):
+    # n = 70 pads to 128 rows; rows 70..127 hold code 1 (trit 0) = 0x55
+    t = np.full((70, 64), 1, np.int8)
+    p, bad = orc.pack_i2s(t)
+    assert bad == 0 and p.size == 128 * 16
+    blk1 = p[1024:].reshape(64, 16)  # second row block, one 64-k chunk
+    assert (blk1[:6] == 0xAA).all() and (blk1[6:] == 0x55).all()
 
 
 def test_pack_single_plus_one_golden(orc):
@@ -116,21 +125,34 @@ def test_pack_single_plus_one_golden(orc):
         t = np.zeros((1, 64), np.int8)
         t[0, int(k)] = 1
         p, _ = orc.pack_i2s(t)
-        expect = np.full(16, 0x55, np.uint8)
+        expect = np.full(1024, 0x55, np.uint8)  # row 0 + 63 padding rows
         expect[int(bidx)] = int(val, 16)
-        np.testing.assert_array_equal(p[0], expect, err_msg=f"k={k}")
+        np.testing.assert_array_equal(p, expect, err_msg=f"k={k}")
+
+
+def test_pack_chunk_and_block_placement(orc):
+    # 16-byte chunk c of row r sits at (r // 64) * 16 k + c * 1024 + (r % 64)
+    # * 16: set one +1 at (r, 64 c) and find the only changed byte.
+    n, k = 130, 192
+    for r, c in [(0, 0), (1, 0), (63, 2), (64, 0), (65, 1), (129, 2)]:
+        t = np.zeros((n, k), np.int8)
+        t[r, 64 * c] = 1
+        p, _ = orc.pack_i2s(t)
+        changed = np.flatnonzero(p != 0x55)
+        assert changed.tolist() == [(r // 64) * 16 * k + c * 1024 + (r % 64) * 16]
+        assert p[changed[0]] == 0x56
 
 
 def test_pack_round_trip_all_81_bytes(orc):
     # positions 0, 4, 8, 12 share byte 0 of the row (one field each)
     seen = set()
     for combo in itertools.product((-1, 0, 1), repeat=4):
-        t = np.zeros((1, 16), np.int8)
+        t = np.zeros((1, 64), np.int8)
         t[0, [0, 4, 8, 12]] = combo
         p, bad = orc.pack_i2s(t)
         assert bad == 0
-        seen.add(int(p[0, 0]))
-        back, bad2 = orc.unpack_i2s(p, 16)
+        seen.add(int(p[0]))
+        back, bad2 = orc.unpack_i2s(p, 1, 64)
         assert bad2 == 0
         np.testing.assert_array_equal(back, t)
     assert len(seen) == 81
@@ -141,32 +163,32 @@ def test_pack_round_trip_all_81_bytes(orc):
 
 def test_pack_round_trip_random(orc):
     rng = np.random.default_rng(14)
-    t = rng.integers(-1, 2, size=(37, 320), dtype=np.int8)
+    t = rng.integers(-1, 2, size=(137, 320), dtype=np.int8)
     p, bad = orc.pack_i2s(t)
-    assert bad == 0 and p.shape == (37, 80)
-    back, bad2 = orc.unpack_i2s(p, 320)
+    assert bad == 0 and p.shape == (192 * 80,)
+    back, bad2 = orc.unpack_i2s(p, 137, 320)
     assert bad2 == 0
     np.testing.assert_array_equal(back, t)
 
 
 def test_pack_invalid_counted(orc):
-    t = np.zeros((2, 16), np.int8)
+    t = np.zeros((2, 64), np.int8)
     t[0, 3] = 2
     t[1, 7] = -2
     t[1, 9] = 5
     _, bad = orc.pack_i2s(t)
     assert bad == 3
-    _, bad_unpack = orc.unpack_i2s(np.full((1, 4), 0xFF, np.uint8), 16)
-    assert bad_unpack == 16
+    _, bad_unpack = orc.unpack_i2s(np.full(1024, 0xFF, np.uint8), 1, 64)
+    assert bad_unpack == 64
 
 
 def test_pack_size_matches_two_bits_per_weight(orc):
     # bitnet.cpp CPU tutorial §1.1: a 1B-parameter model's weights take about
     # 250 MB at 2 bits each; the packed size is n*k/4 bytes.
-    t = np.zeros((8, 1024), np.int8)
+    t = np.zeros((128, 1024), np.int8)
     p, _ = orc.pack_i2s(t)
     assert p.nbytes * 4 == t.size
-    assert 10 ** 9 // 4 == 250_000_000
+    assert orc.packed_bytes(10 ** 6, 1024) == 256_000_000  # ~1B weights
 
 
 # ------------------------------------------------------------------ O3
@@ -244,21 +266,21 @@ def test_gemm_matches_numpy_int64(orc):
         t = rng.integers(-1, 2, size=(n, k), dtype=np.int8)
         q = rng.integers(-127, 128, size=(m, k), dtype=np.int8)
         p, _ = orc.pack_i2s(t)
-        acc, _ = orc.gemm(p, 1.0, k, q, np.ones(m, np.float32))
+        acc, _ = orc.gemm(p, 1.0, n, k, q, np.ones(m, np.float32))
         ref = q.astype(np.int64) @ t.astype(np.int64).T
         np.testing.assert_array_equal(acc, ref)
 
 
 def test_gemm_brute_force_all_rows_of_four(orc):
     rows = np.array(list(itertools.product((-1, 0, 1), repeat=4)), np.int8)
-    t = np.zeros((81, 16), np.int8)
+    t = np.zeros((81, 64), np.int8)
     t[:, :4] = rows
-    qs = np.zeros((3, 16), np.int8)
+    qs = np.zeros((3, 64), np.int8)
     qs[0, :4] = [127, 2, -4, 0]
     qs[1, :4] = [-127, -127, 127, 1]
     qs[2, :4] = [5, -3, 7, -11]
     p, _ = orc.pack_i2s(t)
-    acc, _ = orc.gemm(p, 1.0, 16, qs, np.ones(3, np.float32))
+    acc, _ = orc.gemm(p, 1.0, 81, 64, qs, np.ones(3, np.float32))
     for i in range(3):
         for r in range(81):
             s = 0
@@ -277,7 +299,7 @@ def test_gemm_closed_forms(orc):
     for c in range(k):
         t[3 + c, c] = 1  # one-hot rows
     p, _ = orc.pack_i2s(t)
-    acc, _ = orc.gemm(p, 1.0, k, q, np.ones(2, np.float32))
+    acc, _ = orc.gemm(p, 1.0, 3 + k, k, q, np.ones(2, np.float32))
     qs = q.astype(np.int64).sum(axis=1)
     assert (acc[:, 0] == 0).all()
     np.testing.assert_array_equal(acc[:, 1], qs)
@@ -291,18 +313,19 @@ def test_gemm_invariants(orc):
     t = rng.integers(-1, 2, size=(n, k), dtype=np.int8)
     q = rng.integers(-127, 128, size=(m, k), dtype=np.int8)
     ones = np.ones(m, np.float32)
-    acc, _ = orc.gemm(orc.pack_i2s(t)[0], 1.0, k, q, ones)
-    accn, _ = orc.gemm(orc.pack_i2s(-t)[0], 1.0, k, q, ones)
+    acc, _ = orc.gemm(orc.pack_i2s(t)[0], 1.0, n, k, q, ones)
+    accn, _ = orc.gemm(orc.pack_i2s(-t)[0], 1.0, n, k, q, ones)
     np.testing.assert_array_equal(accn, -acc)
     perm = rng.permutation(k)
-    accp, _ = orc.gemm(orc.pack_i2s(t[:, perm])[0], 1.0, k, q[:, perm], ones)
+    accp, _ = orc.gemm(orc.pack_i2s(t[:, perm])[0], 1.0, n, k, q[:, perm],
+                       ones)
     np.testing.assert_array_equal(accp, acc)
     # additivity while the sum stays ternary: split t into disjoint supports
     mask = rng.random((n, k)) < 0.5
     t1 = np.where(mask, t, 0).astype(np.int8)
     t2 = np.where(mask, 0, t).astype(np.int8)
-    a1, _ = orc.gemm(orc.pack_i2s(t1)[0], 1.0, k, q, ones)
-    a2, _ = orc.gemm(orc.pack_i2s(t2)[0], 1.0, k, q, ones)
+    a1, _ = orc.gemm(orc.pack_i2s(t1)[0], 1.0, n, k, q, ones)
+    a2, _ = orc.gemm(orc.pack_i2s(t2)[0], 1.0, n, k, q, ones)
     np.testing.assert_array_equal(a1 + a2, acc)
 
 
@@ -313,19 +336,20 @@ def test_gemm_threads_and_row_ranges_agree(orc):
     q = rng.integers(-127, 128, size=(m, k), dtype=np.int8)
     s_a = np.array([0.5, 0.25, 2.0], np.float32)
     p, _ = orc.pack_i2s(t)
-    a1, y1 = orc.gemm(p, 0.125, k, q, s_a, nthreads=1)
-    a7, y7 = orc.gemm(p, 0.125, k, q, s_a, nthreads=7)
+    a1, y1 = orc.gemm(p, 0.125, n, k, q, s_a, nthreads=1)
+    a7, y7 = orc.gemm(p, 0.125, n, k, q, s_a, nthreads=7)
     np.testing.assert_array_equal(a1, a7)
     np.testing.assert_array_equal(y1, y7)
-    ar, yr = orc.gemm(p, 0.125, k, q, s_a, rows=(10, 20))
+    ar, yr = orc.gemm(p, 0.125, n, k, q, s_a, rows=(10, 20))
     np.testing.assert_array_equal(ar, a1[:, 10:20])
+    np.testing.assert_array_equal(yr, y1[:, 10:20])
 
 
 def test_gemm_extreme_accumulator(orc):
     k = 65536
     t = np.ones((1, k), np.int8)
     q = np.full((1, k), 127, np.int8)
-    acc, _ = orc.gemm(orc.pack_i2s(t)[0], 1.0, k, q, np.ones(1, np.float32))
+    acc, _ = orc.gemm(orc.pack_i2s(t)[0], 1.0, 1, k, q, np.ones(1, np.float32))
     assert acc[0, 0] == 127 * k
 
 
@@ -334,7 +358,7 @@ def test_pipeline_worked_example(orc):
     g, _ = read_golden("pipeline_example.txt")
     t4 = np.array([[int(v) for v in g["T0"]], [int(v) for v in g["T1"]]],
                   np.int8)
-    for k in (4 * 4, 64):
+    for k in (64, 192):
         t = np.zeros((2, k), np.int8)
         t[:, :4] = t4
         x = np.zeros((1, k), np.float32)
@@ -342,7 +366,8 @@ def test_pipeline_worked_example(orc):
         q, s_a = orc.quant_act(x)
         assert q[0, :4].tolist() == [int(v) for v in g["q"]]
         assert s_a[0] == float(g["s_a"][0])
-        acc, y = orc.gemm(orc.pack_i2s(t)[0], float(g["s_w"][0]), k, q, s_a)
+        acc, y = orc.gemm(orc.pack_i2s(t)[0], float(g["s_w"][0]), 2, k, q,
+                          s_a)
         assert acc[0].tolist() == [int(v) for v in g["acc"]]
         assert y[0].tolist() == [float(v) for v in g["y"]]
 
@@ -356,7 +381,7 @@ def test_rescale_close_to_exact_product(orc):
     x = rng.standard_normal((m, k)).astype(np.float32)
     q, s_a = orc.quant_act(x)
     s_w = np.float32(0.0317)
-    acc, y = orc.gemm(orc.pack_i2s(t)[0], s_w, k, q, s_a)
+    acc, y = orc.gemm(orc.pack_i2s(t)[0], s_w, n, k, q, s_a)
     for i in range(m):
         for r in range(n):
             exact = Fraction(int(acc[i, r])) * Fraction(float(s_w)) * \
