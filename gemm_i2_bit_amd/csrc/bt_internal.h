@@ -64,7 +64,7 @@ constexpr int kKindDot4 = 0;   // m <= 4: packed dot products
 constexpr int kKindMfma = 1;   // m > 4: int8 matrix cores
 constexpr int kDot4MaxM = 4;
 #ifndef BT_STREAM_WG_PER_CU
-#define BT_STREAM_WG_PER_CU 4
+#define BT_STREAM_WG_PER_CU 2
 #endif
 constexpr int kStreamWgPerCu = BT_STREAM_WG_PER_CU;  // persistent grid: WGs/CU
 

@@ -11,8 +11,8 @@
 //    problem, chunk L is at byte offset L * 1024, row block L / kc, input
 //    chunk L % kc.
 //  * The grid is persistent (a few workgroups per CU).  Wave w of W streams
-//    chunks [w T / W, (w + 1) T / W): every wave reads the same number of
-//    bytes, whatever the problem shapes, so the launch ends evenly.
+//    chunks [w T / W, (w + 1) T / W) (W <= T): every wave reads the same
+//    number of bytes, whatever the problem shapes, so the launch ends evenly.
 //  * Lane l of a wave owns row 64 rb + l; for chunk L it loads 16 bytes with
 //    one non-temporal 128-bit load (the wave reads 1 contiguous KiB); a wave
 //    issues a group of D chunks, then consumes them, and the other resident
@@ -170,28 +170,39 @@ struct Stream {
     }
   }
 
-  // Chunk with input-chunk index c; keep = 0 discards it (all codes 0, which
+  // The 64 activation bytes of input chunk c for every token (SGPRs).
+  struct QChunk {
+    int v[TOK][16];
+  };
+  __device__ __forceinline__ void load_q(QChunk& qc, int c, int pin) const {
+#pragma unroll
+    for (int t = 0; t < TOK; ++t) {
+      const_iptr q = (const_iptr)(xq + (size_t)t * k + (size_t)c * 64 + pin);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) qc.v[t][i] = q[i];
+    }
+  }
+
+  // Chunk with activations qc; keep = 0 discards it (all codes 0, which
   // contribute nothing) without a branch: the masks are scalar registers.
-  __device__ __forceinline__ void dot_chunk(const v4u& wv, int c,
-                                            uint32_t keep, int pin,
+  __device__ __forceinline__ void dot_chunk(const v4u& wv, const QChunk& qc,
+                                            uint32_t keep,
                                             Acc<TOK>& a) const {
     const uint32_t m0 = 0x03030303u & keep, m1 = 0x0C0C0C0Cu & keep,
                    m2 = 0x30303030u & keep;
     const uint32_t words[4] = {wv.x, wv.y, wv.z, wv.w};
 #pragma unroll
     for (int t = 0; t < TOK; ++t) {
-      const_iptr q =
-          (const_iptr)(xq + (size_t)t * k + (size_t)c * 64 + pin);
 #pragma unroll
       for (int ww = 0; ww < 4; ++ww) {
         const int e0 = (int)(words[ww] & m0);
         const int e1 = (int)(words[ww] & m1);
         const int e2 = (int)(words[ww] & m2);
         const int e3 = (int)((words[ww] >> 6) & m0);
-        a.f[0][t] = sdot4(e0, q[4 * ww + 0], a.f[0][t]);
-        a.f[1][t] = sdot4(e1, q[4 * ww + 1], a.f[1][t]);
-        a.f[2][t] = sdot4(e2, q[4 * ww + 2], a.f[2][t]);
-        a.f[3][t] = sdot4(e3, q[4 * ww + 3], a.f[3][t]);
+        a.f[0][t] = sdot4(e0, qc.v[t][4 * ww + 0], a.f[0][t]);
+        a.f[1][t] = sdot4(e1, qc.v[t][4 * ww + 1], a.f[1][t]);
+        a.f[2][t] = sdot4(e2, qc.v[t][4 * ww + 2], a.f[2][t]);
+        a.f[3][t] = sdot4(e3, qc.v[t][4 * ww + 3], a.f[3][t]);
       }
     }
   }
@@ -199,22 +210,24 @@ struct Stream {
   // All D chunks are consumed unconditionally (chunks past g.cnt are masked
   // out and read a clamped activation chunk), so the compiler keeps every
   // load of the group ahead of the first use instead of sinking loads into
-  // branches.  Each pair of chunks is pinned in order (opaque zero on the
-  // activation addresses before, accumulator pin after), so the scalar
-  // activation loads of at most two chunks (32 SGPRs per token) are live.
+  // branches.  Chunks go in runs of P: the run's activations are requested
+  // together (one wait per run), and an opaque zero on their addresses plus
+  // an accumulator pin after the run keep at most P chunks' activations
+  // (16 SGPRs per chunk and token) live.
+  static constexpr int P = TOK == 1 ? 2 : 1;
   __device__ __forceinline__ void consume(const v4u (&buf)[D], Group g,
                                           Acc<TOK>& a) const {
-    int pin = 0;
 #pragma unroll
-    for (int j = 0; j < D; ++j) {
-      if (j % 2 == 0) {
-        // an opaque zero (scalar register) added to the activation address:
-        // the two chunks' loads cannot move above this point
-        asm volatile("s_mov_b32 %0, 0" : "=s"(pin));
-      }
-      const uint32_t keep = j < g.cnt ? 0xFFFFFFFFu : 0u;
-      dot_chunk(buf[j], min(g.c + j, kc - 1), keep, pin, a);
-      if (j % 2 == 1) a.pin();
+    for (int j = 0; j < D; j += P) {
+      int pin;
+      asm volatile("s_mov_b32 %0, 0" : "=s"(pin));
+      QChunk q[P];
+#pragma unroll
+      for (int r = 0; r < P; ++r) load_q(q[r], min(g.c + j + r, kc - 1), pin);
+#pragma unroll
+      for (int r = 0; r < P; ++r)
+        dot_chunk(buf[j + r], q[r], j + r < g.cnt ? 0xFFFFFFFFu : 0u, a);
+      a.pin();
     }
   }
 
@@ -371,9 +384,13 @@ template <int TOK>
 __global__ __launch_bounds__(256) void stream_kernel(
     const Desc* __restrict__ descs, const int64_t* __restrict__ chunk0s,
     int count, int64_t total, int32_t* sacc, int32_t* scnt) {
-  const int64_t W = (int64_t)gridDim.x * 4;
+  // With fewer chunks than waves, only the first `total` waves take part, so
+  // every participating wave owns at least one chunk (the arrival count of a
+  // shared row block counts exactly the waves that hold part of it).
+  const int64_t W = min((int64_t)gridDim.x * 4, total);
   const int64_t wv =
       (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (wv >= W) return;
   Stream<TOK> st;
   st.lo = wv * total / W;
   st.hi = (wv + 1) * total / W;

@@ -249,6 +249,38 @@ def test_grouped_two_layers_match_oracle(m):
         check_y(prob["y"].cpu().numpy(), y_r, acc_r)
 
 
+@pytest.mark.parametrize("m", [1, 2, 3, 4, 8])
+def test_grouped_small_problems(m):
+    """Grouped calls with fewer 1 KiB chunks than waves (tiny shapes, ragged
+    rows, k of one chunk): row blocks shared by many waves; each plan is
+    launched twice to check that the scratch area is left clean."""
+    specs = [(512, 256), (64, 64), (70, 192), (1, 64), (130, 320)]
+    probs, host = [], []
+    for i, (n, k) in enumerate(specs):
+        rng = np.random.default_rng([107, m, i])
+        t = wl.trits(rng, (n, k), wl.DECODE_2B)
+        x = wl.x_normal_outliers(rng, (m, k))
+        s_w = wl.scale(rng, 0.01, 0.05)
+        x_q, s_a = bt.bt_quant_act(dev(x))
+        probs.append(dict(packed=bt.bt_pack_i2s(dev(t)), s_w=s_w, n=n, k=k,
+                          x_q=x_q, s_a=s_a,
+                          y=torch.full((m, n), float("nan"), device="cuda:0"),
+                          acc=torch.full((m, n), 0x7EADBEEF, dtype=torch.int32,
+                                         device="cuda:0")))
+        host.append((t, x, s_w))
+    for sub in (probs[:1], probs):
+        plan = bt.bt_grouped_plan(sub)
+        for _ in range(2):
+            for p in sub:
+                p["y"].fill_(float("nan"))
+            bt.bt_gemm_grouped(plan)
+            torch.cuda.synchronize()
+            for prob, (t, x, s_w) in zip(sub, host):
+                _, q_r, s_r, acc_r, y_r = oracle_product(t, x, s_w)
+                np.testing.assert_array_equal(prob["acc"].cpu().numpy(), acc_r)
+                check_y(prob["y"].cpu().numpy(), y_r, acc_r)
+
+
 def test_prefill_layer_sampled():
     """One 2B-shaped layer at M=512 (7 products): 24 sampled output rows per
     projection against the oracle, all 512 tokens."""
