@@ -69,7 +69,7 @@ int32_t check_problem(const uint8_t* packed, float s_w, int64_t n, int64_t k,
   if (!n_ok(n) || !k_ok(k) || !m_ok(m)) return BT_E_SHAPE;
   // chunk indices inside one problem and grids stay 32-bit
   if ((n + 63) / 64 * (k / 64) >= INT32_MAX ||
-      (m > 4 && ((n + 63) / 64) * ((m + 31) / 32) / 4 >= INT32_MAX))
+      bt::kind_units(bt::plan_kind(m), n, m) >= INT32_MAX / 4)
     return BT_E_SHAPE;
   if (!aligned(packed, 16) || !aligned(x_q, 16) || !aligned(y, 16) ||
       !aligned(s_a, 4) || (acc && !aligned(acc, 16)))
@@ -105,9 +105,10 @@ std::vector<Unit> plan_units(const bt_problem* probs, int32_t count, int m) {
   std::stable_sort(order.begin(), order.end(), [&](int32_t a, int32_t b) {
     return probs[a].k > probs[b].k;
   });
+  const int kind = bt::plan_kind(m);
   std::vector<Unit> units;
   for (int32_t p : order) {
-    const int64_t per = (probs[p].n + 63) / 64 * ((m + 31) / 32);
+    const int64_t per = bt::kind_units(kind, probs[p].n, m);
     for (int64_t s = 0; s < per; ++s) units.push_back(Unit{p, (int32_t)s});
   }
   return units;
@@ -121,16 +122,17 @@ PlanHeader plan_layout(const bt_problem* probs, int32_t count) {
   h.magic = bt::kPlanMagic;
   h.count = count;
   h.m = m;
-  h.kind = m <= bt::kDot4MaxM ? bt::kKindDot4 : bt::kKindMfma;
-  int64_t blocks = 0, chunks = 0;
+  h.kind = bt::plan_kind(m);
+  int64_t blocks = 0, chunks = 0, units = 0;
   for (int32_t i = 0; i < count; ++i) {
     const int64_t nblk = (probs[i].n + 63) / 64;
     blocks += nblk;
     chunks += nblk * (probs[i].k / 64);
+    units += bt::kind_units(h.kind, probs[i].n, m);
   }
   h.blocks = blocks;
   h.total_chunks = chunks;
-  h.units = h.kind == bt::kKindMfma ? blocks * ((m + 31) / 32) : 0;
+  h.units = units;
   auto up = [](int64_t x) { return (x + 255) / 256 * 256; };
   h.desc_off = up(sizeof(PlanHeader));
   h.chunk_off = up(h.desc_off + (int64_t)count * sizeof(Desc));
@@ -158,6 +160,7 @@ int32_t check_group(const bt_problem* probs, int32_t count) {
   }
   // grid, scratch slots and unit indices stay within 32-bit ranges
   if (blocks * ((probs[0].m + 31) / 32) >= INT32_MAX / 64) return BT_E_SHAPE;
+  (void)bt::kKindPrefill;
   return BT_OK;
 }
 
@@ -217,8 +220,11 @@ int32_t bt_gemm(const uint8_t* packed, float s_w, int64_t n, int64_t k,
   if (arch != BT_OK) return arch;
   const Desc d = make_desc(packed, s_w, n, k, m, x_q, s_a, y, acc);
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  return hip_status(m <= bt::kDot4MaxM ? bt::launch_dot4(d, s)
-                                       : bt::launch_mfma(d, s));
+  switch (bt::plan_kind(m)) {
+    case bt::kKindDot4: return hip_status(bt::launch_dot4(d, s));
+    case bt::kKindMfma: return hip_status(bt::launch_mfma(d, s));
+    default: return hip_status(bt::launch_prefill(d, s));
+  }
 }
 
 int32_t bt_gemv(const uint8_t* packed, float s_w, int64_t n, int64_t k,
@@ -257,7 +263,7 @@ int32_t bt_grouped_plan(const bt_problem* probs, int32_t count, void* plan,
     chunk0 += (int64_t)d.nblk * d.kc;
     blk0 += d.nblk;
   }
-  if (h.kind == bt::kKindMfma) {
+  if (h.kind != bt::kKindDot4) {
     const std::vector<Unit> units = plan_units(probs, count, h.m);
     memcpy(out + h.unit_off, units.data(), units.size() * sizeof(Unit));
   }
@@ -272,22 +278,23 @@ int32_t bt_gemm_grouped(const void* plan_dev, const void* plan_host,
   memcpy(&h, plan_host, sizeof(h));
   if (h.magic != bt::kPlanMagic || h.count < 1 || h.blocks < 1 ||
       h.total_chunks < 1 ||
-      (h.kind != bt::kKindDot4 && h.kind != bt::kKindMfma) ||
-      (h.kind == bt::kKindDot4) != (h.m >= 1 && h.m <= bt::kDot4MaxM) ||
-      h.m < 1 || h.m > BT_MAX_M || h.desc_off != 256 ||
+      h.m < 1 || h.m > BT_MAX_M || h.kind != bt::plan_kind(h.m) ||
+      h.desc_off != 256 ||
       h.bytes < h.scnt_off || h.scnt_off < h.sacc_off ||
       h.sacc_off < h.unit_off || h.unit_off < h.chunk_off ||
       h.chunk_off < h.desc_off + (int64_t)h.count * (int64_t)sizeof(Desc) ||
-      (h.kind == bt::kKindMfma && h.units < 1))
+      (h.kind != bt::kKindDot4 && h.units < 1))
     return BT_E_ARG;
   const int32_t arch = check_arch();
   if (arch != BT_OK) return arch;
   const unsigned char* base = static_cast<const unsigned char*>(plan_dev);
   const Desc* descs = reinterpret_cast<const Desc*>(base + h.desc_off);
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  if (h.kind == bt::kKindMfma) {
+  if (h.kind != bt::kKindDot4) {
     const Unit* units = reinterpret_cast<const Unit*>(base + h.unit_off);
-    return hip_status(bt::launch_mfma_grouped(descs, units, h.units, s));
+    return hip_status(h.kind == bt::kKindMfma
+                          ? bt::launch_mfma_grouped(descs, units, h.units, s)
+                          : bt::launch_prefill_grouped(descs, units, h.units, s));
   }
   const int cus = cu_count();
   if (cus <= 0) return BT_E_HIP;

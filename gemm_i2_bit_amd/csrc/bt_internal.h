@@ -60,9 +60,23 @@ struct PlanHeader {
 static_assert(sizeof(PlanHeader) == 128, "PlanHeader is 128 bytes");
 
 constexpr uint32_t kPlanMagic = 0x31475442u;  // "BTG1"
-constexpr int kKindDot4 = 0;   // m <= 4: packed dot products
-constexpr int kKindMfma = 1;   // m > 4: int8 matrix cores
+constexpr int kKindDot4 = 0;     // m <= 4: packed dot products
+constexpr int kKindMfma = 1;     // 4 < m < kPrefillMinM: matrix cores, codes
+                                 // expanded per 32-token tile
+constexpr int kKindPrefill = 2;  // m >= kPrefillMinM: LDS-staged tiles
 constexpr int kDot4MaxM = 4;
+constexpr int kPrefillMinM = 65;
+
+inline int plan_kind(int64_t m) {
+  return m <= kDot4MaxM ? kKindDot4
+                        : (m < kPrefillMinM ? kKindMfma : kKindPrefill);
+}
+// work units of one problem for the matrix-core kinds
+inline int64_t kind_units(int kind, int64_t n, int64_t m) {
+  if (kind == kKindMfma) return (n + 63) / 64 * ((m + 31) / 32);
+  if (kind == kKindPrefill) return (n + 127) / 128 * ((m + 127) / 128);
+  return 0;
+}
 #ifndef BT_STREAM_WG_PER_CU
 #define BT_STREAM_WG_PER_CU 2
 #endif
@@ -81,5 +95,8 @@ hipError_t launch_stream_grouped(const Desc* descs, const int64_t* chunk0,
 hipError_t launch_mfma(const Desc& d, hipStream_t s);
 hipError_t launch_mfma_grouped(const Desc* descs, const Unit* units,
                                int64_t count, hipStream_t s);
+hipError_t launch_prefill(const Desc& d, hipStream_t s);
+hipError_t launch_prefill_grouped(const Desc* descs, const Unit* units,
+                                  int64_t count, hipStream_t s);
 
 }  // namespace bt

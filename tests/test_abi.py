@@ -202,6 +202,21 @@ def test_grouped_plan_layout_mfma(L):
     assert p["scnt_off"] == p["sacc_off"]  # no scratch for this kind
 
 
+def test_grouped_plan_layout_prefill(L):
+    # m >= 65: 128-row x 128-token tiles, largest reduction length first
+    specs = [(2560, 2560, 512), (640, 2560, 512), (2560, 6912, 512)]
+    arr = problems(specs)
+    nbytes = L.bt_grouped_plan_bytes(arr, 3)
+    img = np.zeros(nbytes, np.uint8)
+    assert L.bt_grouped_plan(arr, 3, img.ctypes.data, nbytes) == 0
+    p = parse_plan(img)
+    per = [(n + 127) // 128 * 4 for n, _, _ in specs]
+    assert p["kind"] == 2 and p["units"] == sum(per)
+    assert p["unit"][:per[2], 0].tolist() == [2] * per[2]
+    assert p["unit"][:per[2], 1].tolist() == list(range(per[2]))
+    assert p["unit"][per[2]:, 0].tolist() == [0] * per[0] + [1] * per[1]
+
+
 def test_grouped_plan_errors(L):
     arr = problems([(64, 64, 1), (64, 64, 2)])
     assert L.bt_grouped_plan_bytes(arr, 2) == bt.BT_E_SHAPE  # mixed m

@@ -234,10 +234,11 @@ def grouped_case(work, layers):
     return probs, host
 
 
-@pytest.mark.parametrize("m", [1, 3, 8, 32])
-def test_grouped_two_layers_match_oracle(m):
-    work = wl.decode_2b(m=m, layers=2)
-    probs, host = grouped_case(work, 2)
+@pytest.mark.parametrize("m,layers", [(1, 2), (3, 2), (8, 2), (32, 2),
+                                      (64, 1), (130, 1)])
+def test_grouped_layers_match_oracle(m, layers):
+    work = wl.decode_2b(m=m, layers=layers)
+    probs, host = grouped_case(work, layers)
     plan = bt.bt_grouped_plan(probs)
     for _ in range(2):  # the plan is reusable
         bt.bt_gemm_grouped(plan)
