@@ -74,7 +74,7 @@ inline int plan_kind(int64_t m) {
 // work units of one problem for the matrix-core kinds
 inline int64_t kind_units(int kind, int64_t n, int64_t m) {
   if (kind == kKindMfma) return (n + 63) / 64 * ((m + 31) / 32);
-  if (kind == kKindPrefill) return (n + 127) / 128 * ((m + 127) / 128);
+  if (kind == kKindPrefill) return (n + 255) / 256 * ((m + 127) / 128);
   return 0;
 }
 #ifndef BT_STREAM_WG_PER_CU

@@ -203,14 +203,14 @@ def test_grouped_plan_layout_mfma(L):
 
 
 def test_grouped_plan_layout_prefill(L):
-    # m >= 65: 128-row x 128-token tiles, largest reduction length first
+    # m >= 65: 256-row x 128-token tiles, largest reduction length first
     specs = [(2560, 2560, 512), (640, 2560, 512), (2560, 6912, 512)]
     arr = problems(specs)
     nbytes = L.bt_grouped_plan_bytes(arr, 3)
     img = np.zeros(nbytes, np.uint8)
     assert L.bt_grouped_plan(arr, 3, img.ctypes.data, nbytes) == 0
     p = parse_plan(img)
-    per = [(n + 127) // 128 * 4 for n, _, _ in specs]
+    per = [(n + 255) // 256 * 4 for n, _, _ in specs]
     assert p["kind"] == 2 and p["units"] == sum(per)
     assert p["unit"][:per[2], 0].tolist() == [2] * per[2]
     assert p["unit"][:per[2], 1].tolist() == list(range(per[2]))

@@ -162,7 +162,7 @@ def test_single_gemv_config():
 
 
 @pytest.mark.parametrize("m", [1, 2, 3, 4, 5, 7, 8, 15, 16, 17, 31, 32, 33,
-                               63, 64, 65, 100])
+                               63, 64, 65, 100, 257])
 @pytest.mark.parametrize("n,k", [(200, 192), (64, 64), (130, 2560),
                                  (70, 6912)])
 def test_gemm_matches_oracle(m, n, k):
