@@ -93,7 +93,7 @@ Desc make_desc(const uint8_t* packed, float s_w, int64_t n, int64_t k,
   d.k = (int32_t)k;
   d.m = (int32_t)m;
   d.nblk = (int32_t)((n + 63) / 64);
-  d.ntt = (int32_t)((m + 31) / 32);
+  d.ntt = (int32_t)((m + bt::token_tile(m) - 1) / bt::token_tile(m));
   return d;
 }
 
@@ -160,7 +160,6 @@ int32_t check_group(const bt_problem* probs, int32_t count) {
   }
   // grid, scratch slots and unit indices stay within 32-bit ranges
   if (blocks * ((probs[0].m + 31) / 32) >= INT32_MAX / 64) return BT_E_SHAPE;
-  (void)bt::kKindPrefill;
   return BT_OK;
 }
 
@@ -220,11 +219,9 @@ int32_t bt_gemm(const uint8_t* packed, float s_w, int64_t n, int64_t k,
   if (arch != BT_OK) return arch;
   const Desc d = make_desc(packed, s_w, n, k, m, x_q, s_a, y, acc);
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  switch (bt::plan_kind(m)) {
-    case bt::kKindDot4: return hip_status(bt::launch_dot4(d, s));
-    case bt::kKindMfma: return hip_status(bt::launch_mfma(d, s));
-    default: return hip_status(bt::launch_prefill(d, s));
-  }
+  if (bt::plan_kind(m) == bt::kKindDot4)
+    return hip_status(bt::launch_dot4(d, s));
+  return hip_status(bt::launch_tiled(d, s));
 }
 
 int32_t bt_gemv(const uint8_t* packed, float s_w, int64_t n, int64_t k,
@@ -292,9 +289,8 @@ int32_t bt_gemm_grouped(const void* plan_dev, const void* plan_host,
   const hipStream_t s = static_cast<hipStream_t>(stream);
   if (h.kind != bt::kKindDot4) {
     const Unit* units = reinterpret_cast<const Unit*>(base + h.unit_off);
-    return hip_status(h.kind == bt::kKindMfma
-                          ? bt::launch_mfma_grouped(descs, units, h.units, s)
-                          : bt::launch_prefill_grouped(descs, units, h.units, s));
+    return hip_status(
+        bt::launch_tiled_grouped(descs, units, h.units, h.m, s));
   }
   const int cus = cu_count();
   if (cus <= 0) return BT_E_HIP;

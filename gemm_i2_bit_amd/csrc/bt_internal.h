@@ -20,7 +20,7 @@ struct alignas(16) Desc {
   float sw;           // weight scale
   int32_t n, k, m;
   int32_t nblk;       // 64-row blocks = ceil(n / 64)
-  int32_t ntt;        // 32-token tiles = ceil(m / 32) (matrix-core path)
+  int32_t ntt;        // token tiles of the matrix-core kernels
   // grouped streaming path: position of this problem in the concatenated
   // stream of 1 KiB chunks, and its first row block in the scratch area
   int64_t chunk0;
@@ -31,7 +31,7 @@ struct alignas(16) Desc {
 static_assert(sizeof(Desc) == 96, "Desc is 96 bytes");
 
 // One work unit of a grouped launch: problem index and a sub-index whose
-// meaning depends on the kernel (row block, or row block * ntt + token tile).
+// meaning depends on the kernel (256-row tile * ntt + token tile).
 struct Unit {
   int32_t prob;
   int32_t sub;
@@ -40,12 +40,13 @@ struct Unit {
 // Host-side header at the start of a grouped plan image.  Layout:
 //   PlanHeader | Desc[count] | int64 chunk0[count] | Unit[units] |
 //   int32 scratch_acc[blocks * m * 64] | int32 scratch_cnt[blocks]
-// (the streaming kind has units = 0; the matrix-core kind has no scratch).
+// (the streaming kind has units = 0; the matrix-core kinds have no
+// scratch).
 struct PlanHeader {
   uint32_t magic;
   int32_t count;
   int32_t m;
-  int32_t kind;        // kKindDot4 or kKindMfma
+  int32_t kind;        // kKindDot4, kKindMfma or kKindPrefill
   int64_t units;
   int64_t desc_off;    // byte offset of Desc[count]
   int64_t chunk_off;   // byte offset of int64 chunk0[count]
@@ -61,9 +62,9 @@ static_assert(sizeof(PlanHeader) == 128, "PlanHeader is 128 bytes");
 
 constexpr uint32_t kPlanMagic = 0x31475442u;  // "BTG1"
 constexpr int kKindDot4 = 0;     // m <= 4: packed dot products
-constexpr int kKindMfma = 1;     // 4 < m < kPrefillMinM: matrix cores, codes
-                                 // expanded per 32-token tile
-constexpr int kKindPrefill = 2;  // m >= kPrefillMinM: LDS-staged tiles
+constexpr int kKindMfma = 1;     // 4 < m < kPrefillMinM: matrix-core tiles of
+                                 // 32 or 64 tokens (weight-stream bound)
+constexpr int kKindPrefill = 2;  // m >= kPrefillMinM: 128-token tiles
 constexpr int kDot4MaxM = 4;
 constexpr int kPrefillMinM = 65;
 
@@ -71,11 +72,14 @@ inline int plan_kind(int64_t m) {
   return m <= kDot4MaxM ? kKindDot4
                         : (m < kPrefillMinM ? kKindMfma : kKindPrefill);
 }
-// work units of one problem for the matrix-core kinds
+// tokens per workgroup tile of the matrix-core kernels
+inline int token_tile(int64_t m) { return m <= 32 ? 32 : (m <= 64 ? 64 : 128); }
+// work units (256-row x token-tile workgroups) of one problem for the
+// matrix-core kinds
 inline int64_t kind_units(int kind, int64_t n, int64_t m) {
-  if (kind == kKindMfma) return (n + 63) / 64 * ((m + 31) / 32);
-  if (kind == kKindPrefill) return (n + 255) / 256 * ((m + 127) / 128);
-  return 0;
+  if (kind == kKindDot4) return 0;
+  const int bm = token_tile(m);
+  return (n + 255) / 256 * ((m + bm - 1) / bm);
 }
 #ifndef BT_STREAM_WG_PER_CU
 #define BT_STREAM_WG_PER_CU 2
@@ -92,11 +96,8 @@ hipError_t launch_stream_grouped(const Desc* descs, const int64_t* chunk0,
                                  int32_t count, int64_t total_chunks, int m,
                                  int32_t* sacc, int32_t* scnt, int workgroups,
                                  hipStream_t s);
-hipError_t launch_mfma(const Desc& d, hipStream_t s);
-hipError_t launch_mfma_grouped(const Desc* descs, const Unit* units,
-                               int64_t count, hipStream_t s);
-hipError_t launch_prefill(const Desc& d, hipStream_t s);
-hipError_t launch_prefill_grouped(const Desc* descs, const Unit* units,
-                                  int64_t count, hipStream_t s);
+hipError_t launch_tiled(const Desc& d, hipStream_t s);
+hipError_t launch_tiled_grouped(const Desc* descs, const Unit* units,
+                                int64_t count, int m, hipStream_t s);
 
 }  // namespace bt

@@ -1,0 +1,400 @@
+// Ternary GEMM for m > 4 tokens on int8 matrix cores
+// (v_mfma_i32_32x32x32_i8, gfx950), operands staged through LDS by direct
+// buffer-to-LDS loads.
+//
+// Once the 2-bit codes are expanded to int8 the ternary product is a dense
+// integer contraction (bitnet.cpp CPU tutorial §1.1: each product with a
+// trit is the activation, its negation or nothing, then accumulated).  Codes
+// c = trit + 1 in {0, 1, 2} feed the matrix cores as they are; the per-token
+// activation sum removes the +1 (sum (c - 1) q = sum c q - sum q), exact in
+// int32.  Skinny token counts (up to 64) stay bound by the weight stream from
+// HBM; prefill-sized ones (128-token tiles) by the matrix cores.
+//
+// Workgroup tile: 256 weight rows (four 64-row blocks of the packed layout,
+// one per wave) x BM tokens (32, 64 or 128).  The reduction runs in stages of
+// 2 packed chunks (128 inputs) through a ring of NS LDS slots: the loads of
+// stage st + NS - 1 are issued when stage st starts, so NS - 1 stages of work
+// cover each load's latency.  One barrier per stage.
+//  * Loads are buffer loads that write LDS directly (16 bytes per lane), with
+//    no registers in between.  Their ranges end at the tile's last token and
+//    at the block's last chunk, so tokens past m and weight words past the
+//    row read as zero.  All variable offsets go in the range-checked offset.
+//  * Activation slot: BM token rows of 144 bytes (128 + 16 of padding).  Nine
+//    is odd, so the matrix-core reads (one token per lane, 16 bytes at the
+//    same column) meet no bank conflicts, and every read offset within a
+//    stage is an immediate.
+//  * Weight slot: per wave, the block's two 1 KiB chunks copied as they are.
+//  * Each slot is an LDS array of its own, so the compiler can tell them apart
+//    and a read of one slot does not wait for the loads into the others.
+//  * Matrix-core operands: lane (h, i) takes 8 bytes of row i's 16-byte chunk,
+//    32-bit words 2h and 2h + 1 (inputs 64 c + 32 h + [0, 32)).  Word s is
+//    expanded in registers (shift and mask per 4 inputs) into the 16 int8
+//    codes of inputs 64 c + 32 h + 16 s + [0, 16): the A operand of step s;
+//    it feeds one MFMA per 32-token tile of the wave.  The B operand is the
+//    same 16 inputs of token i, one 128-bit LDS read; the k assignment is
+//    identical on both sides, so each step covers 32 distinct inputs.
+//  * Activation sums: wave w visits its token tiles starting at tile w mod NB
+//    and adds up the B operands of that first tile as they pass (4 dot4 per
+//    step); the sums go through LDS to the epilogue.
+//  * Ragged k (an odd number of chunks): the second chunk of the last stage
+//    has zero weight words (out of range) and is left out of the activation
+//    sums.  A block past the last row block reads zeros and is never stored.
+//  * Output D[row][token] of a 32x32 tile sits in lane token + 32 ((row / 4)
+//    % 2), register 4 (row / 8) + row % 4: each lane holds one token and 16
+//    rows, stored as four 16-byte pieces.
+#include "bt_internal.h"
+
+namespace bt {
+namespace {
+
+typedef int v2i __attribute__((ext_vector_type(2)));
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(1))) float* gfloat_ptr;
+typedef __attribute__((address_space(1))) int32_t* gint_ptr;
+typedef const __attribute__((address_space(1))) float* gcfloat_ptr;
+typedef __attribute__((address_space(3))) void* lds_ptr;
+
+constexpr int BLK = 4;                 // 64-row blocks per tile, one per wave
+constexpr int CPS = 2;                 // packed chunks per stage
+constexpr int kRowGran = CPS * 4 + 1;  // 16-byte granules per token row,
+                                       // one of them padding
+constexpr int kRow = kRowGran * 16;    // 144 bytes
+constexpr int kWSlot = BLK * CPS * 1024;  // 8 KiB
+// Buffer resource word 3 for raw (untyped, unswizzled) gfx9 buffer loads.
+constexpr int kRsrcFlags = 0x00020000;
+
+template <int BM_, int NS_>
+struct Cfg {
+  static constexpr int BM = BM_;       // tokens per workgroup tile
+  static constexpr int NB = BM / 32;   // 32-token MFMA tiles per wave
+  static constexpr int NS = NS_;       // LDS ring slots
+  // activation slot, rounded up to whole 1 KiB loads
+  static constexpr int kActSlot = (BM * kRow + 1023) / 1024 * 1024;
+  // direct loads filling one activation slot, 64 granules each, spread over
+  // the waves (extra rounds repeat the last load)
+  static constexpr int kActLoads = (BM * kRowGran + 63) / 64;
+  static constexpr int kActDma = (kActLoads + BLK - 1) / BLK;
+  static constexpr int kDmaPerStage = kActDma + CPS;  // per wave
+  static_assert(kActLoads * 1024 <= kActSlot, "slot holds every load");
+  static_assert((NS - 2) * kDmaPerStage < 64, "vmcnt range");
+};
+using CfgS32 = Cfg<32, 6>;
+using CfgS64 = Cfg<64, 4>;
+using CfgP128 = Cfg<128, 3>;
+
+// s_waitcnt immediate: vmcnt(v) and lgkmcnt(0); expcnt not waited on
+constexpr int waitcnt_vm(int v) {
+  return (v & 15) | ((v >> 4) << 14) | (7 << 4) | (0 << 8);
+}
+
+__device__ __forceinline__ int sdot4(int a, int b, int c) {
+  return __builtin_amdgcn_sdot4(a, b, c, false);
+}
+
+__device__ __forceinline__ v4i expand(uint32_t word) {
+  v4i a;
+  a.x = (int)(word & 0x03030303u);
+  a.y = (int)((word >> 2) & 0x03030303u);
+  a.z = (int)((word >> 4) & 0x03030303u);
+  a.w = (int)((word >> 6) & 0x03030303u);
+  return a;
+}
+
+// One 16-byte piece per lane from buffer [base, base + bytes) at byte offset
+// voff (range-checked: past the end reads zero) straight into LDS at
+// lds + 16 lane.  `lds` is wave-uniform.
+__device__ __forceinline__ void load_lds16(const void* base, int bytes,
+                                           int8_t* lds, int voff) {
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<void*>(base), 0, bytes, kRsrcFlags);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr)lds, 16, voff, 0, 0, 0);
+}
+
+// Ring slot S of a configuration: one LDS array per slot and operand.
+template <class C, int S>
+__device__ __forceinline__ int8_t* act_slot() {
+  __shared__ __attribute__((aligned(1024))) int8_t buf[C::kActSlot];
+  return buf;
+}
+template <class C, int S>
+__device__ __forceinline__ int8_t* wts_slot() {
+  __shared__ __attribute__((aligned(1024))) int8_t buf[kWSlot];
+  return buf;
+}
+
+template <class C>
+__device__ __forceinline__ int* tsum_array() {
+  __shared__ int buf[C::BM];
+  return buf;
+}
+
+__device__ __forceinline__ void store_rows(const Desc& d, const v16i& c,
+                                           int row0, int tok, int h, int qsum,
+                                           float sa) {
+  const size_t base = (size_t)tok * d.n;
+  const gfloat_ptr y = (gfloat_ptr)d.y + base;
+  const gint_ptr acc = d.acc ? (gint_ptr)d.acc + base : nullptr;
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    const int row = row0 + 8 * g + 4 * h;  // 4 consecutive rows
+    int a[4];
+    float v[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      a[r] = c[4 * g + r] - qsum;
+      v[r] = __fmul_rn(__fmul_rn((float)a[r], d.sw), sa);
+    }
+    if ((d.n & 3) == 0 && row + 3 < d.n) {
+      *reinterpret_cast<__attribute__((address_space(1))) v4f*>(y + row) =
+          v4f{v[0], v[1], v[2], v[3]};
+      if (acc)
+        *reinterpret_cast<__attribute__((address_space(1))) v4i*>(acc + row) =
+            v4i{a[0], a[1], a[2], a[3]};
+    } else {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        if (row + r < d.n) {
+          y[row + r] = v[r];
+          if (acc) acc[row + r] = a[r];
+        }
+      }
+    }
+  }
+}
+
+// One stage of matrix-core work from one ring slot.  `ones1` is 0x01010101,
+// or 0 when the stage's second chunk lies past the row (odd kc): its weight
+// words read as zero, so only the activation sums have to skip it.
+template <class C>
+__device__ __forceinline__ void compute_stage(const int8_t* act,
+                                              const int8_t* wslot,
+                                              const int (&bread)[C::NB],
+                                              int wread, int ones1,
+                                              v16i (&acc)[2][C::NB],
+                                              int& tsum_part) {
+#pragma unroll
+  for (int j = 0; j < CPS; ++j) {
+    const int ones = j == 0 ? 0x01010101 : ones1;
+    const v2i w0 = *reinterpret_cast<const v2i*>(wslot + j * 1024 + wread);
+    const v2i w1 =
+        *reinterpret_cast<const v2i*>(wslot + j * 1024 + wread + 512);
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      v4i b[C::NB];
+#pragma unroll
+      for (int i = 0; i < C::NB; ++i)
+        b[i] = *reinterpret_cast<const v4i*>(act + bread[i] + 64 * j + 16 * s);
+      const v4i a0 = expand((uint32_t)(s == 0 ? w0.x : w0.y));
+      const v4i a1 = expand((uint32_t)(s == 0 ? w1.x : w1.y));
+#pragma unroll
+      for (int i = 0; i < C::NB; ++i) {
+        acc[0][i] =
+            __builtin_amdgcn_mfma_i32_32x32x32_i8(a0, b[i], acc[0][i], 0, 0, 0);
+        acc[1][i] =
+            __builtin_amdgcn_mfma_i32_32x32x32_i8(a1, b[i], acc[1][i], 0, 0, 0);
+      }
+      tsum_part = sdot4(b[0].x, ones, tsum_part);
+      tsum_part = sdot4(b[0].y, ones, tsum_part);
+      tsum_part = sdot4(b[0].z, ones, tsum_part);
+      tsum_part = sdot4(b[0].w, ones, tsum_part);
+    }
+  }
+}
+
+// Per-wave state of one workgroup tile.
+template <class C>
+struct TileState {
+  const void* wbase;  // the wave's weight block
+  int wbytes;
+  const void* abase;  // the tile's activation rows
+  int abytes;
+  int av[C::kActDma];         // per-lane source offsets of the activation loads
+  int aq[C::kActDma];         // their load indices q (uniform)
+  int bread[C::NB];           // LDS offsets of the B operands
+  int wread;                  // LDS offset of the A words
+  int wave, lane, nfull;
+  v16i acc[2][C::NB];
+  int tsum_part;
+};
+
+// Loads of stage st into ring slot S: activation loads, then the wave's two
+// weight chunks.
+template <class C, int S>
+__device__ __forceinline__ void issue(const TileState<C>& x, int st) {
+  int8_t* act = act_slot<C, S>();
+  int8_t* wts = wts_slot<C, S>();
+  const int c0 = st * CPS;
+#pragma unroll
+  for (int r = 0; r < C::kActDma; ++r)
+    load_lds16(x.abase, x.abytes, act + x.aq[r] * 1024, x.av[r] + c0 * 64);
+#pragma unroll
+  for (int j = 0; j < CPS; ++j)
+    load_lds16(x.wbase, x.wbytes, wts + (x.wave * CPS + j) * 1024,
+               x.lane * 16 + (c0 + j) * 1024);
+}
+
+// Stage st from slot S; stage st + NS - 1 goes into slot S - 1 (mod NS),
+// whose previous stage every wave finished before the barrier.
+template <class C, int S>
+__device__ __forceinline__ void run_stage(TileState<C>& x, int st) {
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm((C::NS - 2) * C::kDmaPerStage));
+  __builtin_amdgcn_s_barrier();
+  issue<C, (S + C::NS - 1) % C::NS>(x, st + C::NS - 1);
+  compute_stage<C>(act_slot<C, S>(), wts_slot<C, S>(), x.bread, x.wread,
+                   st < x.nfull ? 0x01010101 : 0, x.acc, x.tsum_part);
+}
+
+// Slots S .. NS-1 of one pass around the ring, starting at stage st0; with
+// `bounded`, only the stages below nst.
+template <class C, int S>
+__device__ __forceinline__ void ring_pass(TileState<C>& x, int st0,
+                                          bool bounded, int nst) {
+  if constexpr (S < C::NS) {
+    if (!bounded || st0 + S < nst) run_stage<C, S>(x, st0 + S);
+    ring_pass<C, S + 1>(x, st0, bounded, nst);
+  }
+}
+
+// Loads of stages S .. NS-2 into their slots.
+template <class C, int S>
+__device__ __forceinline__ void prologue(const TileState<C>& x) {
+  if constexpr (S < C::NS - 1) {
+    issue<C, S>(x, S);
+    prologue<C, S + 1>(x);
+  }
+}
+
+// One workgroup tile: weight rows [256 rt, 256 rt + 256) x tokens
+// [BM tt, BM tt + BM).
+template <class C>
+__device__ __forceinline__ void run_tile(const Desc& d, int rt, int tt) {
+  constexpr int NB = C::NB;
+  int* tsum = tsum_array<C>();
+  TileState<C> x;
+  const int tid = threadIdx.x;
+  x.wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  x.lane = tid & 63;
+  const int wave = x.wave;
+  const int h = x.lane >> 5;
+  const int li = x.lane & 31;
+  const int k = d.k;
+  const int kc = k >> 6;
+  const int nst = (kc + CPS - 1) / CPS;
+  x.nfull = kc / CPS;  // full stages; an odd kc adds one more
+  const int blk = rt * BLK + wave;
+  const bool blk_ok = blk < d.nblk;  // wave-uniform
+
+  // weight loads: the wave's block, 1 KiB per chunk, lane = 16-byte row piece
+  x.wbase = d.w + (size_t)(blk_ok ? blk : 0) * 16 * (size_t)k;
+  x.wbytes = blk_ok ? 16 * k : 0;
+  // activation loads: load q fills slot granules 64 q + lane, granule g of
+  // the slot being byte 16 (g % 9) of token g / 9 (the ninth is padding and
+  // gets a copy of the eighth; granules past the tile's tokens are out of
+  // range).  Wave w issues loads q = w + 4 r.
+  const int tok0 = tt * C::BM;
+  x.abase = d.xq + (size_t)tok0 * k;
+  x.abytes = min(C::BM, d.m - tok0) * k;
+#pragma unroll
+  for (int r = 0; r < C::kActDma; ++r) {
+    const int q = min(wave + BLK * r, C::kActLoads - 1);
+    x.aq[r] = q;
+    const int g = q * 64 + x.lane;
+    const int t = g / kRowGran;
+    const int xg = min(g % kRowGran, kRowGran - 2);
+    x.av[r] = t * k + xg * 16;
+  }
+  // matrix-core reads: B operand i is token 32 ((i + wave) % NB) + li,
+  // inputs 64 j + 32 h + 16 s + [0, 16) of the stage
+#pragma unroll
+  for (int i = 0; i < NB; ++i)
+    x.bread[i] = (32 * ((i + wave) % NB) + li) * kRow + 32 * h;
+  x.wread = wave * CPS * 1024 + li * 16 + 8 * h;
+#pragma unroll
+  for (int r2 = 0; r2 < 2; ++r2)
+#pragma unroll
+    for (int i = 0; i < NB; ++i) x.acc[r2][i] = v16i{0};
+  x.tsum_part = 0;
+
+  // Prologue: stages 0 .. NS-2 in flight.  Every stage issues one more (past
+  // the end they read out of range or unused rows and are never consumed),
+  // so exactly NS-2 stages are younger than the one awaited.
+  prologue<C, 0>(x);
+  int st = 0;
+  for (; st + C::NS <= nst; st += C::NS) ring_pass<C, 0>(x, st, false, nst);
+  ring_pass<C, 0>(x, st, true, nst);
+  // drain the loads issued past the end before LDS is reused
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+
+  // activation sums of token tile `wave`: lanes li and li + 32 hold the two
+  // input halves of token 32 wave + li
+  const int ts = x.tsum_part + __shfl_xor(x.tsum_part, 32, 64);
+  if (h == 0 && wave < NB) tsum[wave * 32 + li] = ts;
+  __syncthreads();
+
+  if (!blk_ok) return;
+#pragma unroll
+  for (int i = 0; i < NB; ++i) {
+    const int tl = 32 * ((i + wave) % NB) + li;  // token within the tile
+    const int tok = tok0 + tl;
+    if (tok < d.m) {
+      const int qs = tsum[tl];
+      const float sa = *((gcfloat_ptr)d.sa + tok);
+      store_rows(d, x.acc[0][i], blk * 64, tok, h, qs, sa);
+      store_rows(d, x.acc[1][i], blk * 64 + 32, tok, h, qs, sa);
+    }
+  }
+}
+
+template <class C>
+__global__ __launch_bounds__(256, 2) void tiled_kernel(Desc d, int ntt) {
+  const int u = blockIdx.x;
+  run_tile<C>(d, u / ntt, u % ntt);
+}
+
+template <class C>
+__global__ __launch_bounds__(256, 2) void tiled_grouped_kernel(
+    const Desc* __restrict__ descs, const Unit* __restrict__ units) {
+  const Unit u = units[blockIdx.x];
+  const Desc d = descs[u.prob];
+  const int ntt = (d.m + C::BM - 1) / C::BM;
+  run_tile<C>(d, u.sub / ntt, u.sub % ntt);
+}
+
+template <class C>
+hipError_t launch_one(const Desc& d, hipStream_t s) {
+  const int ntt = (d.m + C::BM - 1) / C::BM;
+  const int64_t units = (int64_t)((d.n + 255) / 256) * ntt;
+  tiled_kernel<C><<<dim3((unsigned)units), dim3(256), 0, s>>>(d, ntt);
+  return hipGetLastError();
+}
+
+template <class C>
+hipError_t launch_group(const Desc* descs, const Unit* units, int64_t count,
+                        hipStream_t s) {
+  tiled_grouped_kernel<C><<<dim3((unsigned)count), dim3(256), 0, s>>>(descs,
+                                                                      units);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_tiled(const Desc& d, hipStream_t s) {
+  switch (token_tile(d.m)) {
+    case 32: return launch_one<CfgS32>(d, s);
+    case 64: return launch_one<CfgS64>(d, s);
+    default: return launch_one<CfgP128>(d, s);
+  }
+}
+
+hipError_t launch_tiled_grouped(const Desc* descs, const Unit* units,
+                                int64_t count, int m, hipStream_t s) {
+  switch (token_tile(m)) {
+    case 32: return launch_group<CfgS32>(descs, units, count, s);
+    case 64: return launch_group<CfgS64>(descs, units, count, s);
+    default: return launch_group<CfgP128>(descs, units, count, s);
+  }
+}
+
+}  // namespace bt

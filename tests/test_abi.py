@@ -195,10 +195,11 @@ def test_grouped_plan_layout_mfma(L):
     img = np.zeros(nbytes, np.uint8)
     assert L.bt_grouped_plan(arr, 2, img.ctypes.data, nbytes) == 0
     p = parse_plan(img)
-    assert p["kind"] == 1 and p["units"] == 10 * 2 + 2 * 2
+    # 256-row tiles, one 64-token tile
+    assert p["kind"] == 1 and p["units"] == 3 + 1
     # largest reduction length first
     assert p["unit"][0].tolist() == [1, 0]
-    assert p["unit"][4].tolist() == [0, 0]
+    assert p["unit"][1:].tolist() == [[0, 0], [0, 1], [0, 2]]
     assert p["scnt_off"] == p["sacc_off"]  # no scratch for this kind
 
 
