@@ -65,24 +65,33 @@ constexpr int kWSlot = BLK * CPS * 1024;  // 8 KiB
 // Buffer resource word 3 for raw (untyped, unswizzled) gfx9 buffer loads.
 constexpr int kRsrcFlags = 0x00020000;
 
-template <int BM_, int NS_>
+template <int BM_, int NS_, bool RegW_>
 struct Cfg {
   static constexpr int BM = BM_;       // tokens per workgroup tile
   static constexpr int NB = BM / 32;   // 32-token MFMA tiles per wave
   static constexpr int NS = NS_;       // LDS ring slots
+  // weight words go from memory straight to registers (else through LDS)
+  static constexpr bool kRegW = RegW_;
   // activation slot, rounded up to whole 1 KiB loads
   static constexpr int kActSlot = (BM * kRow + 1023) / 1024 * 1024;
   // direct loads filling one activation slot, 64 granules each, spread over
   // the waves (extra rounds repeat the last load)
   static constexpr int kActLoads = (BM * kRowGran + 63) / 64;
   static constexpr int kActDma = (kActLoads + BLK - 1) / BLK;
-  static constexpr int kDmaPerStage = kActDma + CPS;  // per wave
+  // memory instructions per wave per stage, in issue order: activation
+  // loads, then weight loads (into LDS, or into registers)
+  static constexpr int kWLoads = kRegW ? 2 : CPS;
+  static constexpr int kPerStage = kActDma + kWLoads;
+  // at the start of a stage, the loads younger than its activation loads:
+  // its own weight loads when they go to registers (the compiler waits for
+  // those where they are used), and NS - 2 whole stages
+  static constexpr int kYounger = (NS - 2) * kPerStage + (kRegW ? kWLoads : 0);
   static_assert(kActLoads * 1024 <= kActSlot, "slot holds every load");
-  static_assert((NS - 2) * kDmaPerStage < 64, "vmcnt range");
+  static_assert(kYounger < 64, "vmcnt range");
 };
-using CfgS32 = Cfg<32, 6>;
-using CfgS64 = Cfg<64, 4>;
-using CfgP128 = Cfg<128, 3>;
+using CfgS32 = Cfg<32, 6, true>;
+using CfgS64 = Cfg<64, 4, true>;
+using CfgP128 = Cfg<128, 3, false>;
 
 // s_waitcnt immediate: vmcnt(v) and lgkmcnt(0); expcnt not waited on
 constexpr int waitcnt_vm(int v) {
@@ -203,6 +212,39 @@ __device__ __forceinline__ void compute_stage(const int8_t* act,
   }
 }
 
+// One stage with weight words in registers: lane (h, i) holds the 16-byte
+// chunk 2 p + h of rows i and 32 + i (w[0], w[1]); word s gives the A
+// operands of step s, inputs 64 h + 16 s + [0, 16) of the stage.  `ones` is
+// 0 for lanes whose chunk lies past the row (odd kc), else 0x01010101.
+template <class C>
+__device__ __forceinline__ void compute_stage_reg(const int8_t* act,
+                                                  const v4i (&w)[2],
+                                                  const int (&bread)[C::NB],
+                                                  int ones,
+                                                  v16i (&acc)[2][C::NB],
+                                                  int& tsum_part) {
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    v4i b[C::NB];
+#pragma unroll
+    for (int i = 0; i < C::NB; ++i)
+      b[i] = *reinterpret_cast<const v4i*>(act + bread[i] + 16 * s);
+    const v4i a0 = expand((uint32_t)w[0][s]);
+    const v4i a1 = expand((uint32_t)w[1][s]);
+#pragma unroll
+    for (int i = 0; i < C::NB; ++i) {
+      acc[0][i] =
+          __builtin_amdgcn_mfma_i32_32x32x32_i8(a0, b[i], acc[0][i], 0, 0, 0);
+      acc[1][i] =
+          __builtin_amdgcn_mfma_i32_32x32x32_i8(a1, b[i], acc[1][i], 0, 0, 0);
+    }
+    tsum_part = sdot4(b[0].x, ones, tsum_part);
+    tsum_part = sdot4(b[0].y, ones, tsum_part);
+    tsum_part = sdot4(b[0].z, ones, tsum_part);
+    tsum_part = sdot4(b[0].w, ones, tsum_part);
+  }
+}
+
 // Per-wave state of one workgroup tile.
 template <class C>
 struct TileState {
@@ -213,37 +255,57 @@ struct TileState {
   int av[C::kActDma];         // per-lane source offsets of the activation loads
   int aq[C::kActDma];         // their load indices q (uniform)
   int bread[C::NB];           // LDS offsets of the B operands
-  int wread;                  // LDS offset of the A words
-  int wave, lane, nfull;
+  int wread;                  // LDS offset (or source offset) of the A words
+  int wave, lane, h, nfull;
+  v4i wreg[C::kRegW ? C::NS : 1][2];  // register ring of weight words
   v16i acc[2][C::NB];
   int tsum_part;
 };
 
 // Loads of stage st into ring slot S: activation loads, then the wave's two
-// weight chunks.
+// weight chunks (into LDS, or into the slot's registers).
 template <class C, int S>
-__device__ __forceinline__ void issue(const TileState<C>& x, int st) {
+__device__ __forceinline__ void issue(TileState<C>& x, int st) {
   int8_t* act = act_slot<C, S>();
-  int8_t* wts = wts_slot<C, S>();
   const int c0 = st * CPS;
 #pragma unroll
   for (int r = 0; r < C::kActDma; ++r)
     load_lds16(x.abase, x.abytes, act + x.aq[r] * 1024, x.av[r] + c0 * 64);
+  if constexpr (C::kRegW) {
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<void*>(x.wbase), 0, x.wbytes, kRsrcFlags);
+    // streamed once: non-temporal
 #pragma unroll
-  for (int j = 0; j < CPS; ++j)
-    load_lds16(x.wbase, x.wbytes, wts + (x.wave * CPS + j) * 1024,
-               x.lane * 16 + (c0 + j) * 1024);
+    for (int r2 = 0; r2 < 2; ++r2)
+      x.wreg[S][r2] = __builtin_amdgcn_raw_buffer_load_b128(
+          r, x.wread + c0 * 1024 + r2 * 512, 0, 2);
+  } else {
+    int8_t* wts = wts_slot<C, S>();
+#pragma unroll
+    for (int j = 0; j < CPS; ++j)
+      load_lds16(x.wbase, x.wbytes, wts + (x.wave * CPS + j) * 1024,
+                 x.lane * 16 + (c0 + j) * 1024);
+  }
 }
 
 // Stage st from slot S; stage st + NS - 1 goes into slot S - 1 (mod NS),
 // whose previous stage every wave finished before the barrier.
 template <class C, int S>
 __device__ __forceinline__ void run_stage(TileState<C>& x, int st) {
-  __builtin_amdgcn_s_waitcnt(waitcnt_vm((C::NS - 2) * C::kDmaPerStage));
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(C::kYounger));
   __builtin_amdgcn_s_barrier();
   issue<C, (S + C::NS - 1) % C::NS>(x, st + C::NS - 1);
-  compute_stage<C>(act_slot<C, S>(), wts_slot<C, S>(), x.bread, x.wread,
-                   st < x.nfull ? 0x01010101 : 0, x.acc, x.tsum_part);
+  // keep register-bound weight loads at the top of the stage: the scheduler
+  // would otherwise sink them below the stage's math and shorten the
+  // prefetch distance
+  if constexpr (C::kRegW) __builtin_amdgcn_sched_barrier(0);
+  if constexpr (C::kRegW)
+    compute_stage_reg<C>(act_slot<C, S>(), x.wreg[S], x.bread,
+                         (x.h == 0 || st < x.nfull) ? 0x01010101 : 0, x.acc,
+                         x.tsum_part);
+  else
+    compute_stage<C>(act_slot<C, S>(), wts_slot<C, S>(), x.bread, x.wread,
+                     st < x.nfull ? 0x01010101 : 0, x.acc, x.tsum_part);
 }
 
 // Slots S .. NS-1 of one pass around the ring, starting at stage st0; with
@@ -259,7 +321,7 @@ __device__ __forceinline__ void ring_pass(TileState<C>& x, int st0,
 
 // Loads of stages S .. NS-2 into their slots.
 template <class C, int S>
-__device__ __forceinline__ void prologue(const TileState<C>& x) {
+__device__ __forceinline__ void prologue(TileState<C>& x) {
   if constexpr (S < C::NS - 1) {
     issue<C, S>(x, S);
     prologue<C, S + 1>(x);
@@ -307,10 +369,21 @@ __device__ __forceinline__ void run_tile(const Desc& d, int rt, int tt) {
   }
   // matrix-core reads: B operand i is token 32 ((i + wave) % NB) + li,
   // inputs 64 j + 32 h + 16 s + [0, 16) of the stage
+  x.h = h;
+  if constexpr (C::kRegW) {
+    // lane (h, li) takes chunk 2 p + h of rows li and 32 + li: B operands
+    // from inputs 64 h + [0, 64) of the stage
 #pragma unroll
-  for (int i = 0; i < NB; ++i)
-    x.bread[i] = (32 * ((i + wave) % NB) + li) * kRow + 32 * h;
-  x.wread = wave * CPS * 1024 + li * 16 + 8 * h;
+    for (int i = 0; i < NB; ++i)
+      x.bread[i] = (32 * ((i + wave) % NB) + li) * kRow + 64 * h;
+    x.wread = h * 1024 + li * 16;
+  } else {
+    // lane (h, li) takes words 2h, 2h + 1 of each chunk of rows li, 32 + li
+#pragma unroll
+    for (int i = 0; i < NB; ++i)
+      x.bread[i] = (32 * ((i + wave) % NB) + li) * kRow + 32 * h;
+    x.wread = wave * CPS * 1024 + li * 16 + 8 * h;
+  }
 #pragma unroll
   for (int r2 = 0; r2 < 2; ++r2)
 #pragma unroll
