@@ -94,21 +94,53 @@ Desc make_desc(const uint8_t* packed, float s_w, int64_t n, int64_t k,
   d.m = (int32_t)m;
   d.nblk = (int32_t)((n + 63) / 64);
   d.ntt = (int32_t)((m + bt::token_tile(m) - 1) / bt::token_tile(m));
+  d.kc = (int32_t)(k / 64);
+  d.nsplit = 1;
+  d.split_len = d.kc;
+  d.slot0 = -1;
   return d;
 }
 
-// Work units of a matrix-core grouped plan, largest reduction length first
-// so that the longest units start early and the launch ends on short ones.
-std::vector<Unit> plan_units(const bt_problem* probs, int32_t count, int m) {
+// Reduction split of each problem of a matrix-core plan.  Prefill tiles are
+// bound by the matrix cores and one tile runs per workgroup, so a problem
+// with a long reduction would finish last: its tiles are cut into ranges of
+// about the shortest problem's chunk count (an even number of chunks, so
+// that only the last range of a row can end on an odd chunk).
+struct Split {
+  int32_t nsplit, len;
+};
+std::vector<Split> plan_splits(const bt_problem* probs, int32_t count,
+                               int kind) {
+  std::vector<Split> out(count);
+  int32_t kc_min = INT32_MAX;
+  for (int32_t i = 0; i < count; ++i)
+    kc_min = std::min(kc_min, (int32_t)(probs[i].k / 64));
+  for (int32_t i = 0; i < count; ++i) {
+    const int32_t kc = probs[i].k / 64;
+    int32_t ns = 1;
+    if (kind == bt::kKindPrefill) ns = std::max(1, (kc + kc_min / 2) / kc_min);
+    int32_t len = (kc + ns - 1) / ns;
+    len += len & 1;
+    if (len >= kc) len = kc;
+    out[i] = Split{(kc + len - 1) / len, len};
+  }
+  return out;
+}
+
+// Work units of a matrix-core grouped plan, longest unit (chunks per
+// reduction range) first, so that the longest units start early and the
+// launch ends on short ones.
+std::vector<Unit> plan_units(const bt_problem* probs, int32_t count, int m,
+                             const std::vector<Split>& split) {
   std::vector<int32_t> order(count);
   for (int32_t i = 0; i < count; ++i) order[i] = i;
   std::stable_sort(order.begin(), order.end(), [&](int32_t a, int32_t b) {
-    return probs[a].k > probs[b].k;
+    return split[a].len > split[b].len;
   });
   const int kind = bt::plan_kind(m);
   std::vector<Unit> units;
   for (int32_t p : order) {
-    const int64_t per = bt::kind_units(kind, probs[p].n, m);
+    const int64_t per = bt::kind_units(kind, probs[p].n, m) * split[p].nsplit;
     for (int64_t s = 0; s < per; ++s) units.push_back(Unit{p, (int32_t)s});
   }
   return units;
@@ -123,12 +155,15 @@ PlanHeader plan_layout(const bt_problem* probs, int32_t count) {
   h.count = count;
   h.m = m;
   h.kind = bt::plan_kind(m);
-  int64_t blocks = 0, chunks = 0, units = 0;
+  const std::vector<Split> split = plan_splits(probs, count, h.kind);
+  int64_t blocks = 0, chunks = 0, units = 0, slots = 0;
   for (int32_t i = 0; i < count; ++i) {
     const int64_t nblk = (probs[i].n + 63) / 64;
     blocks += nblk;
     chunks += nblk * (probs[i].k / 64);
-    units += bt::kind_units(h.kind, probs[i].n, m);
+    units += bt::kind_units(h.kind, probs[i].n, m) * split[i].nsplit;
+    if (h.kind != bt::kKindDot4 && split[i].nsplit > 1)
+      slots += nblk * ((m + bt::token_tile(m) - 1) / bt::token_tile(m));
   }
   h.blocks = blocks;
   h.total_chunks = chunks;
@@ -138,10 +173,11 @@ PlanHeader plan_layout(const bt_problem* probs, int32_t count) {
   h.chunk_off = up(h.desc_off + (int64_t)count * sizeof(Desc));
   h.unit_off = up(h.chunk_off + (int64_t)count * 8);
   h.sacc_off = up(h.unit_off + h.units * (int64_t)sizeof(Unit));
-  const int64_t sacc_bytes =
-      h.kind == bt::kKindDot4 ? blocks * m * 64 * 4 : 0;
+  const int64_t sacc_bytes = h.kind == bt::kKindDot4
+                                 ? blocks * m * 64 * 4
+                                 : slots * bt::split_slot_ints(m) * 4;
   h.scnt_off = up(h.sacc_off + sacc_bytes);
-  const int64_t scnt_bytes = h.kind == bt::kKindDot4 ? blocks * 4 : 0;
+  const int64_t scnt_bytes = (h.kind == bt::kKindDot4 ? blocks : slots) * 4;
   h.bytes = up(h.scnt_off + scnt_bytes);
   return h;
 }
@@ -160,6 +196,14 @@ int32_t check_group(const bt_problem* probs, int32_t count) {
   }
   // grid, scratch slots and unit indices stay within 32-bit ranges
   if (blocks * ((probs[0].m + 31) / 32) >= INT32_MAX / 64) return BT_E_SHAPE;
+  const int kind = bt::plan_kind(probs[0].m);
+  if (kind != bt::kKindDot4) {
+    const std::vector<Split> split = plan_splits(probs, count, kind);
+    int64_t units = 0;
+    for (int32_t i = 0; i < count; ++i)
+      units += bt::kind_units(kind, probs[i].n, probs[i].m) * split[i].nsplit;
+    if (units >= INT32_MAX / 2) return BT_E_SHAPE;
+  }
   return BT_OK;
 }
 
@@ -246,22 +290,31 @@ int32_t bt_grouped_plan(const bt_problem* probs, int32_t count, void* plan,
   unsigned char* out = static_cast<unsigned char*>(plan);
   memset(out, 0, (size_t)h.bytes);  // scratch area starts at zero
   memcpy(out, &h, sizeof(h));
+  const std::vector<Split> split = plan_splits(probs, count, h.kind);
   int64_t chunk0 = 0;
   int64_t blk0 = 0;
+  int64_t slot0 = 0;
   for (int32_t i = 0; i < count; ++i) {
     const bt_problem& p = probs[i];
     Desc d = make_desc(p.packed, p.s_w, p.n, p.k, p.m, p.x_q, p.s_a, p.y,
                        p.acc);
     d.chunk0 = chunk0;
     d.blk0 = (int32_t)blk0;
-    d.kc = p.k / 64;
+    if (h.kind != bt::kKindDot4) {
+      d.nsplit = split[i].nsplit;
+      d.split_len = split[i].len;
+      if (d.nsplit > 1) {
+        d.slot0 = slot0;
+        slot0 += (int64_t)d.nblk * d.ntt;
+      }
+    }
     memcpy(out + h.desc_off + (int64_t)i * sizeof(Desc), &d, sizeof(d));
     memcpy(out + h.chunk_off + (int64_t)i * 8, &chunk0, 8);
     chunk0 += (int64_t)d.nblk * d.kc;
     blk0 += d.nblk;
   }
   if (h.kind != bt::kKindDot4) {
-    const std::vector<Unit> units = plan_units(probs, count, h.m);
+    const std::vector<Unit> units = plan_units(probs, count, h.m, split);
     memcpy(out + h.unit_off, units.data(), units.size() * sizeof(Unit));
   }
   return BT_OK;
@@ -289,8 +342,10 @@ int32_t bt_gemm_grouped(const void* plan_dev, const void* plan_host,
   const hipStream_t s = static_cast<hipStream_t>(stream);
   if (h.kind != bt::kKindDot4) {
     const Unit* units = reinterpret_cast<const Unit*>(base + h.unit_off);
-    return hip_status(
-        bt::launch_tiled_grouped(descs, units, h.units, h.m, s));
+    unsigned char* mut = const_cast<unsigned char*>(base);
+    return hip_status(bt::launch_tiled_grouped(
+        descs, units, h.units, h.m, reinterpret_cast<int32_t*>(mut + h.sacc_off),
+        reinterpret_cast<int32_t*>(mut + h.scnt_off), s));
   }
   const int cus = cu_count();
   if (cus <= 0) return BT_E_HIP;

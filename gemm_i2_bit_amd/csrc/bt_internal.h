@@ -26,12 +26,19 @@ struct alignas(16) Desc {
   int64_t chunk0;
   int32_t blk0;
   int32_t kc;         // k / 64 = chunks per row block
-  int64_t pad[2];
+  // matrix-core kinds: the reduction of every tile is split into nsplit
+  // ranges of split_len chunks (even; the last range may be shorter); with
+  // nsplit > 1, 64-row block b and token tile t combine their partial sums
+  // in scratch slot slot0 + b * ntt + t
+  int32_t nsplit;
+  int32_t split_len;
+  int64_t slot0;
 };
 static_assert(sizeof(Desc) == 96, "Desc is 96 bytes");
 
 // One work unit of a grouped launch: problem index and a sub-index whose
-// meaning depends on the kernel (256-row tile * ntt + token tile).
+// meaning depends on the kernel: for the matrix-core kinds,
+// (256-row tile * ntt + token tile) * nsplit + reduction range.
 struct Unit {
   int32_t prob;
   int32_t sub;
@@ -39,9 +46,10 @@ struct Unit {
 
 // Host-side header at the start of a grouped plan image.  Layout:
 //   PlanHeader | Desc[count] | int64 chunk0[count] | Unit[units] |
-//   int32 scratch_acc[blocks * m * 64] | int32 scratch_cnt[blocks]
-// (the streaming kind has units = 0; the matrix-core kinds have no
-// scratch).
+//   int32 scratch_acc[slots * slot ints] | int32 scratch_cnt[slots]
+// The streaming kind has units = 0 and one slot of m * 64 ints per row block.
+// The matrix-core kinds have one slot of 64 * token_tile ints per (row block,
+// token tile) of the problems whose reduction is split, and none otherwise.
 struct PlanHeader {
   uint32_t magic;
   int32_t count;
@@ -75,12 +83,14 @@ inline int plan_kind(int64_t m) {
 // tokens per workgroup tile of the matrix-core kernels
 inline int token_tile(int64_t m) { return m <= 32 ? 32 : (m <= 64 ? 64 : 128); }
 // work units (256-row x token-tile workgroups) of one problem for the
-// matrix-core kinds
+// matrix-core kinds, before any split of the reduction
 inline int64_t kind_units(int kind, int64_t n, int64_t m) {
   if (kind == kKindDot4) return 0;
   const int bm = token_tile(m);
   return (n + 255) / 256 * ((m + bm - 1) / bm);
 }
+// int32 entries of one split-reduction scratch slot (64 rows x token tile)
+inline int64_t split_slot_ints(int64_t m) { return 64 * token_tile(m); }
 #ifndef BT_STREAM_WG_PER_CU
 #define BT_STREAM_WG_PER_CU 2
 #endif
@@ -98,6 +108,7 @@ hipError_t launch_stream_grouped(const Desc* descs, const int64_t* chunk0,
                                  hipStream_t s);
 hipError_t launch_tiled(const Desc& d, hipStream_t s);
 hipError_t launch_tiled_grouped(const Desc* descs, const Unit* units,
-                                int64_t count, int m, hipStream_t s);
+                                int64_t count, int m, int32_t* sacc,
+                                int32_t* scnt, hipStream_t s);
 
 }  // namespace bt

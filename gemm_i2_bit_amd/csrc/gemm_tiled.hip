@@ -257,6 +257,7 @@ struct TileState {
   int bread[C::NB];           // LDS offsets of the B operands
   int wread;                  // LDS offset (or source offset) of the A words
   int wave, lane, h, nfull;
+  int c_begin;  // first chunk of the tile's reduction range
   v4i wreg[C::kRegW ? C::NS : 1][2];  // register ring of weight words
   v16i acc[2][C::NB];
   int tsum_part;
@@ -267,7 +268,7 @@ struct TileState {
 template <class C, int S>
 __device__ __forceinline__ void issue(TileState<C>& x, int st) {
   int8_t* act = act_slot<C, S>();
-  const int c0 = st * CPS;
+  const int c0 = x.c_begin + st * CPS;
 #pragma unroll
   for (int r = 0; r < C::kActDma; ++r)
     load_lds16(x.abase, x.abytes, act + x.aq[r] * 1024, x.av[r] + c0 * 64);
@@ -328,10 +329,63 @@ __device__ __forceinline__ void prologue(TileState<C>& x) {
   }
 }
 
-// One workgroup tile: weight rows [256 rt, 256 rt + 256) x tokens
-// [BM tt, BM tt + BM).
+// Partial sums of a tile whose reduction is split: every range adds its
+// int32 partials (already net of its activation sums) into the scratch slot
+// of (block, token tile) with device-scope atomics, in the accumulator
+// layout [r2][tile][register][lane], so that each atomic instruction covers
+// 256 contiguous bytes.  The range that arrives last (arrival counter) takes
+// the totals back with an exchange that also clears the slot, and writes the
+// outputs.  Integer addition is exact and order-free.
 template <class C>
-__device__ __forceinline__ void run_tile(const Desc& d, int rt, int tt) {
+__device__ __forceinline__ void combine_split(const Desc& d, TileState<C>& x,
+                                              int blk, int tt, int tok0,
+                                              const int* tsum, int32_t* sacc,
+                                              int32_t* scnt) {
+  constexpr int NB = C::NB;
+  const int lane = x.lane, h = x.h, li = lane & 31, wave = x.wave;
+  const int64_t slot = d.slot0 + (int64_t)blk * d.ntt + tt;
+  int32_t* part = sacc + slot * (64 * C::BM);
+#pragma unroll
+  for (int r2 = 0; r2 < 2; ++r2)
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      const int qs = tsum[32 * ((i + wave) % NB) + li];
+#pragma unroll
+      for (int g = 0; g < 16; ++g)
+        atomicAdd(part + ((r2 * NB + i) * 16 + g) * 64 + lane,
+                  x.acc[r2][i][g] - qs);
+    }
+  // The partials travel only through device-scope atomics, performed at the
+  // coherence point; waiting for them orders them before the arrival.
+  __builtin_amdgcn_s_waitcnt(0);
+  int arrived = 0;
+  if (lane == 0) arrived = atomicAdd(scnt + slot, 1);
+  arrived = __builtin_amdgcn_readfirstlane(arrived);
+  if (arrived == d.nsplit - 1) {
+#pragma unroll
+    for (int r2 = 0; r2 < 2; ++r2)
+#pragma unroll
+      for (int i = 0; i < NB; ++i) {
+        v16i tot;
+#pragma unroll
+        for (int g = 0; g < 16; ++g)
+          tot[g] = atomicExch(part + ((r2 * NB + i) * 16 + g) * 64 + lane, 0);
+        const int tok = tok0 + 32 * ((i + wave) % NB) + li;
+        if (tok < d.m)
+          store_rows(d, tot, blk * 64 + 32 * r2, tok, h, 0,
+                     *((gcfloat_ptr)d.sa + tok));
+      }
+    if (lane == 0) atomicExch(scnt + slot, 0);
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+}
+
+// One workgroup tile: weight rows [256 rt, 256 rt + 256) x tokens
+// [BM tt, BM tt + BM), reduction over chunks [c_begin, c_end).
+template <class C>
+__device__ __forceinline__ void run_tile(const Desc& d, int rt, int tt,
+                                         int c_begin, int c_end,
+                                         int32_t* sacc, int32_t* scnt) {
   constexpr int NB = C::NB;
   int* tsum = tsum_array<C>();
   TileState<C> x;
@@ -342,9 +396,10 @@ __device__ __forceinline__ void run_tile(const Desc& d, int rt, int tt) {
   const int h = x.lane >> 5;
   const int li = x.lane & 31;
   const int k = d.k;
-  const int kc = k >> 6;
-  const int nst = (kc + CPS - 1) / CPS;
-  x.nfull = kc / CPS;  // full stages; an odd kc adds one more
+  const int nc = c_end - c_begin;
+  const int nst = (nc + CPS - 1) / CPS;
+  x.nfull = nc / CPS;  // full stages; an odd count (last range) adds one
+  x.c_begin = c_begin;
   const int blk = rt * BLK + wave;
   const bool blk_ok = blk < d.nblk;  // wave-uniform
 
@@ -407,6 +462,10 @@ __device__ __forceinline__ void run_tile(const Desc& d, int rt, int tt) {
   __syncthreads();
 
   if (!blk_ok) return;
+  if (d.nsplit > 1) {
+    combine_split<C>(d, x, blk, tt, tok0, tsum, sacc, scnt);
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < NB; ++i) {
     const int tl = 32 * ((i + wave) % NB) + li;  // token within the tile
@@ -423,16 +482,22 @@ __device__ __forceinline__ void run_tile(const Desc& d, int rt, int tt) {
 template <class C>
 __global__ __launch_bounds__(256, 2) void tiled_kernel(Desc d, int ntt) {
   const int u = blockIdx.x;
-  run_tile<C>(d, u / ntt, u % ntt);
+  run_tile<C>(d, u / ntt, u % ntt, 0, d.k >> 6, nullptr, nullptr);
 }
 
+// Unit sub-index: (256-row tile * ntt + token tile) * nsplit + range.
 template <class C>
 __global__ __launch_bounds__(256, 2) void tiled_grouped_kernel(
-    const Desc* __restrict__ descs, const Unit* __restrict__ units) {
+    const Desc* __restrict__ descs, const Unit* __restrict__ units,
+    int32_t* sacc, int32_t* scnt) {
   const Unit u = units[blockIdx.x];
   const Desc d = descs[u.prob];
   const int ntt = (d.m + C::BM - 1) / C::BM;
-  run_tile<C>(d, u.sub / ntt, u.sub % ntt);
+  const int tile = u.sub / d.nsplit;
+  const int ks = u.sub % d.nsplit;
+  const int c_begin = ks * d.split_len;
+  const int c_end = min(c_begin + d.split_len, d.k >> 6);
+  run_tile<C>(d, tile / ntt, tile % ntt, c_begin, c_end, sacc, scnt);
 }
 
 template <class C>
@@ -445,9 +510,9 @@ hipError_t launch_one(const Desc& d, hipStream_t s) {
 
 template <class C>
 hipError_t launch_group(const Desc* descs, const Unit* units, int64_t count,
-                        hipStream_t s) {
-  tiled_grouped_kernel<C><<<dim3((unsigned)count), dim3(256), 0, s>>>(descs,
-                                                                      units);
+                        int32_t* sacc, int32_t* scnt, hipStream_t s) {
+  tiled_grouped_kernel<C><<<dim3((unsigned)count), dim3(256), 0, s>>>(
+      descs, units, sacc, scnt);
   return hipGetLastError();
 }
 
@@ -462,11 +527,12 @@ hipError_t launch_tiled(const Desc& d, hipStream_t s) {
 }
 
 hipError_t launch_tiled_grouped(const Desc* descs, const Unit* units,
-                                int64_t count, int m, hipStream_t s) {
+                                int64_t count, int m, int32_t* sacc,
+                                int32_t* scnt, hipStream_t s) {
   switch (token_tile(m)) {
-    case 32: return launch_group<CfgS32>(descs, units, count, s);
-    case 64: return launch_group<CfgS64>(descs, units, count, s);
-    default: return launch_group<CfgP128>(descs, units, count, s);
+    case 32: return launch_group<CfgS32>(descs, units, count, sacc, scnt, s);
+    case 64: return launch_group<CfgS64>(descs, units, count, sacc, scnt, s);
+    default: return launch_group<CfgP128>(descs, units, count, sacc, scnt, s);
   }
 }
 

@@ -149,9 +149,11 @@ def desc(img, p, i):
     s_w = raw[40:44].view(np.float32)[0]
     n, k, m, nblk, ntt = raw[44:64].view(np.int32)
     chunk0 = raw[64:72].view(np.int64)[0]
-    blk0, kc = raw[72:80].view(np.int32)
+    blk0, kc, nsplit, split_len = raw[72:88].view(np.int32)
+    slot0 = raw[88:96].view(np.int64)[0]
     return dict(ptrs=ptrs, s_w=s_w, n=n, k=k, m=m, nblk=nblk, ntt=ntt,
-                chunk0=chunk0, blk0=blk0, kc=kc)
+                chunk0=chunk0, blk0=blk0, kc=kc, nsplit=nsplit,
+                split_len=split_len, slot0=slot0)
 
 
 def test_grouped_plan_layout_stream(L):
@@ -204,18 +206,37 @@ def test_grouped_plan_layout_mfma(L):
 
 
 def test_grouped_plan_layout_prefill(L):
-    # m >= 65: 256-row x 128-token tiles, largest reduction length first
+    # m >= 65: 256-row x 128-token tiles; the k=6912 problem's reduction is
+    # cut into 3 ranges of 36 chunks (about the 40 chunks of k=2560, even)
     specs = [(2560, 2560, 512), (640, 2560, 512), (2560, 6912, 512)]
     arr = problems(specs)
     nbytes = L.bt_grouped_plan_bytes(arr, 3)
     img = np.zeros(nbytes, np.uint8)
     assert L.bt_grouped_plan(arr, 3, img.ctypes.data, nbytes) == 0
     p = parse_plan(img)
-    per = [(n + 255) // 256 * 4 for n, _, _ in specs]
-    assert p["kind"] == 2 and p["units"] == sum(per)
-    assert p["unit"][:per[2], 0].tolist() == [2] * per[2]
-    assert p["unit"][:per[2], 1].tolist() == list(range(per[2]))
-    assert p["unit"][per[2]:, 0].tolist() == [0] * per[0] + [1] * per[1]
+    tiles = [(n + 255) // 256 * 4 for n, _, _ in specs]
+    splits = [1, 1, 3]
+    assert p["kind"] == 2
+    assert p["units"] == sum(t * s for t, s in zip(tiles, splits))
+    # longest range first: the 40-chunk problems, then the 36-chunk ranges
+    u = p["unit"]
+    assert u[:tiles[0], 0].tolist() == [0] * tiles[0]
+    assert u[:tiles[0], 1].tolist() == list(range(tiles[0]))
+    assert u[tiles[0]:tiles[0] + tiles[1], 0].tolist() == [1] * tiles[1]
+    rest = u[tiles[0] + tiles[1]:]
+    assert rest[:, 0].tolist() == [2] * (tiles[2] * 3)
+    assert rest[:, 1].tolist() == list(range(tiles[2] * 3))
+    for i, (nsplit, length, slot0) in enumerate([(1, 40, -1), (1, 40, -1),
+                                                 (3, 36, 0)]):
+        d = desc(img, p, i)
+        assert (d["nsplit"], d["split_len"], d["slot0"]) == (nsplit, length,
+                                                             slot0)
+    # one scratch slot (64 rows x 128 tokens of int32) and one counter per
+    # (64-row block, token tile) of the split problem
+    slots = 40 * 4
+    assert p["scnt_off"] - p["sacc_off"] >= slots * 64 * 128 * 4
+    assert p["bytes"] - p["scnt_off"] >= slots * 4
+    assert not img[p["sacc_off"]:].any()  # the scratch area starts at zero
 
 
 def test_grouped_plan_errors(L):

@@ -282,6 +282,42 @@ def test_grouped_small_problems(m):
                 check_y(prob["y"].cpu().numpy(), y_r, acc_r)
 
 
+@pytest.mark.parametrize("m", [70, 130])
+@pytest.mark.parametrize("specs", [
+    [(300, 576), (200, 2368)],            # 37 chunks cut into 4 ranges
+    [(300, 576), (200, 2368), (64, 64)],  # one-chunk rows: 19 ranges of 2
+])
+def test_grouped_split_ranges(m, specs):
+    """Grouped prefill-sized calls whose long reductions are cut into ranges
+    combined through the plan's scratch slots (odd chunk counts, partial row
+    and token tiles); each plan is launched twice to check that the slots and
+    counters are left clean."""
+    probs, host = [], []
+    for i, (n, k) in enumerate(specs):
+        rng = np.random.default_rng([108, m, i, len(specs)])
+        t = wl.trits(rng, (n, k))
+        x = wl.x_normal(rng, (m, k))
+        s_w = wl.scale(rng, 0.01, 0.05)
+        x_q, s_a = bt.bt_quant_act(dev(x))
+        probs.append(dict(packed=bt.bt_pack_i2s(dev(t)), s_w=s_w, n=n, k=k,
+                          x_q=x_q, s_a=s_a,
+                          y=torch.full((m, n), float("nan"), device="cuda:0"),
+                          acc=torch.full((m, n), 0x7EADBEEF, dtype=torch.int32,
+                                         device="cuda:0")))
+        host.append((t, x, s_w))
+    plan = bt.bt_grouped_plan(probs)
+    for _ in range(2):
+        for p in probs:
+            p["y"].fill_(float("nan"))
+            p["acc"].fill_(0x7EADBEEF)
+        bt.bt_gemm_grouped(plan)
+        torch.cuda.synchronize()
+        for prob, (t, x, s_w) in zip(probs, host):
+            _, q_r, s_r, acc_r, y_r = oracle_product(t, x, s_w)
+            np.testing.assert_array_equal(prob["acc"].cpu().numpy(), acc_r)
+            check_y(prob["y"].cpu().numpy(), y_r, acc_r)
+
+
 def test_prefill_layer_sampled():
     """One 2B-shaped layer at M=512 (7 products): 24 sampled output rows per
     projection against the oracle, all 512 tokens."""
