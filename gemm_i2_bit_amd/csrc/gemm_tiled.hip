@@ -41,7 +41,8 @@
 //    sums.  A block past the last row block reads zeros and is never stored.
 //  * Output D[row][token] of a 32x32 tile sits in lane token + 32 ((row / 4)
 //    % 2), register 4 (row / 8) + row % 4: each lane holds one token and 16
-//    rows, stored as four 16-byte pieces.
+//    rows.  The epilogue transposes them through LDS so that every token's
+//    64 rows of a block go out as one 256-byte segment.
 #include "bt_internal.h"
 
 namespace bt {
@@ -139,37 +140,31 @@ __device__ __forceinline__ int* tsum_array() {
   return buf;
 }
 
-__device__ __forceinline__ void store_rows(const Desc& d, const v16i& c,
-                                           int row0, int tok, int h, int qsum,
-                                           float sa) {
-  const size_t base = (size_t)tok * d.n;
-  const gfloat_ptr y = (gfloat_ptr)d.y + base;
-  const gint_ptr acc = d.acc ? (gint_ptr)d.acc + base : nullptr;
+// Output staging of the epilogue: a wave's accumulators hold one token per
+// lane and 16 rows per register set, so direct stores would scatter 16-byte
+// pieces over 32 token rows.  Instead each wave passes TP tokens at a time
+// through an LDS region of its own (rows of one token contiguous, rows padded
+// to 272 bytes so that both the writes and the reads are free of bank
+// conflicts) and stores every token's 64 rows as one 256-byte segment (16
+// lanes x 16 bytes).  The region reuses the ring, which is idle by then.
+constexpr int kEpRow = 272;  // bytes per token in the staging region
+
+// 16 bytes per lane of one staged token row: rows 4 (lane % 16) .. + 3 of the
+// wave's block, token `tok`.
+template <typename T>
+__device__ __forceinline__ void store_row16(T* out, int n, int tok, int row,
+                                            const int8_t* src) {
+  T* dst = out + (size_t)tok * n + row;
+  if ((n & 3) == 0 && row + 3 < n) {
+    *reinterpret_cast<__attribute__((address_space(1))) v4i*>(
+        (__attribute__((address_space(1))) T*)dst) =
+        *reinterpret_cast<const v4i*>(src);
+  } else {
 #pragma unroll
-  for (int g = 0; g < 4; ++g) {
-    const int row = row0 + 8 * g + 4 * h;  // 4 consecutive rows
-    int a[4];
-    float v[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      a[r] = c[4 * g + r] - qsum;
-      v[r] = __fmul_rn(__fmul_rn((float)a[r], d.sw), sa);
-    }
-    if ((d.n & 3) == 0 && row + 3 < d.n) {
-      *reinterpret_cast<__attribute__((address_space(1))) v4f*>(y + row) =
-          v4f{v[0], v[1], v[2], v[3]};
-      if (acc)
-        *reinterpret_cast<__attribute__((address_space(1))) v4i*>(acc + row) =
-            v4i{a[0], a[1], a[2], a[3]};
-    } else {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        if (row + r < d.n) {
-          y[row + r] = v[r];
-          if (acc) acc[row + r] = a[r];
-        }
-      }
-    }
+    for (int r = 0; r < 4; ++r)
+      if (row + r < n)
+        ((__attribute__((address_space(1))) T*)dst)[r] =
+            reinterpret_cast<const T*>(src)[r];
   }
 }
 
@@ -329,32 +324,157 @@ __device__ __forceinline__ void prologue(TileState<C>& x) {
   }
 }
 
+// Direct stores of the wave's final sums (no staging): lane (h, i) writes
+// its token's rows as four 16-byte pieces per register set.  Used for
+// 32-token tiles holding at most 16 tokens, where the staging passes cost
+// more than the scattered pieces.
+template <class C>
+__device__ __forceinline__ void store_direct(const Desc& d,
+                                             const TileState<C>& x,
+                                             v16i (&fin)[2][C::NB], int blk,
+                                             int tok0) {
+  const int lane = x.lane, h = x.h, li = lane & 31, wave = x.wave;
+#pragma unroll
+  for (int i = 0; i < C::NB; ++i) {
+    const int tok = tok0 + 32 * ((i + wave) % C::NB) + li;
+    if (tok >= d.m) continue;
+    const float sa = *((gcfloat_ptr)d.sa + tok);
+#pragma unroll
+    for (int r2 = 0; r2 < 2; ++r2)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int row = blk * 64 + 32 * r2 + 8 * g4 + 4 * h;
+        v4i a, v;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          a[r] = fin[r2][i][4 * g4 + r];
+          v[r] = __float_as_int(__fmul_rn(__fmul_rn((float)a[r], d.sw), sa));
+        }
+        store_row16(d.y, d.n, tok, row, reinterpret_cast<const int8_t*>(&v));
+        if (d.acc)
+          store_row16(d.acc, d.n, tok, row,
+                      reinterpret_cast<const int8_t*>(&a));
+      }
+  }
+}
+
+// The staging region of a wave (TP tokens x kEpRow bytes) inside the ring's
+// activation slots.
+template <class C>
+struct Staging {
+  static constexpr int kPerSlot = C::kActSlot / kEpRow;  // tokens per slot
+  // tokens per pass: 32 when two waves share a slot or a wave has one of
+  // its own, else 16
+  static constexpr int TP =
+      C::kActSlot >= 2 * 32 * kEpRow ? 32 : (kPerSlot >= 32 ? 32 : 16);
+  static_assert(TP * kEpRow <= C::kActSlot, "staging fits a slot");
+  static_assert(C::kActSlot >= 2 * 32 * kEpRow || C::NS >= BLK,
+                "one slot per wave");
+};
+template <class C>
+__device__ __forceinline__ int8_t* staging(int wave) {
+  if constexpr (C::kActSlot >= 2 * 32 * kEpRow) {
+    int8_t* base = wave < 2 ? act_slot<C, 0>() : act_slot<C, 1>();
+    return base + (wave & 1) * 32 * kEpRow;
+  } else {
+    switch (wave) {
+      case 0: return act_slot<C, 0>();
+      case 1: return act_slot<C, 1>();
+      case 2: return act_slot<C, 2>();
+      default: return act_slot<C, 3>();
+    }
+  }
+}
+
+// Writes the wave's final int32 sums fin (net of the activation sums) as y
+// (and acc when requested) through the staging region.  fin[r2][i] holds
+// rows 32 r2 + 8 (g / 4) + 4 h + g % 4 of token 32 ((i + wave) % NB) + li.
+template <class C>
+__device__ __forceinline__ void store_tile(const Desc& d, const TileState<C>& x,
+                                           v16i (&fin)[2][C::NB], int blk,
+                                           int tok0) {
+  constexpr int NB = C::NB;
+  constexpr int TP = Staging<C>::TP;
+  if constexpr (NB == 1) {
+    if (d.m - tok0 <= 16) {  // few tokens in this tile: store directly
+      store_direct<C>(d, x, fin, blk, tok0);
+      return;
+    }
+  }
+  const int lane = x.lane, h = x.h, li = lane & 31, wave = x.wave;
+  int8_t* ep = staging<C>(wave);
+  const int row = blk * 64 + 4 * (lane & 15);
+#pragma unroll
+  for (int pass_acc = 0; pass_acc < 2; ++pass_acc) {
+    if (pass_acc == 1 && d.acc == nullptr) break;
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      const int tl0 = 32 * ((i + wave) % NB);  // first token of this tile
+      const int tok = tok0 + tl0 + li;
+      const float sa =
+          pass_acc == 0 && tok < d.m ? *((gcfloat_ptr)d.sa + tok) : 0.0f;
+#pragma unroll
+      for (int p = 0; p < 32 / TP; ++p) {
+        // lanes of tokens p TP .. p TP + TP - 1 write their rows
+        if (li >= p * TP && li < (p + 1) * TP) {
+          int8_t* w = ep + (li - p * TP) * kEpRow;
+#pragma unroll
+          for (int r2 = 0; r2 < 2; ++r2)
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+              v4i v;
+#pragma unroll
+              for (int r = 0; r < 4; ++r) {
+                const int a = fin[r2][i][4 * g4 + r];
+                v[r] = pass_acc == 0
+                           ? __float_as_int(
+                                 __fmul_rn(__fmul_rn((float)a, d.sw), sa))
+                           : a;
+              }
+              *reinterpret_cast<v4i*>(w + (32 * r2 + 8 * g4 + 4 * h) * 4) = v;
+            }
+        }
+        // every lane stores 16 bytes of token p TP + 4 j + lane / 16
+#pragma unroll
+        for (int j = 0; j < TP / 4; ++j) {
+          const int t = 4 * j + (lane >> 4);
+          const int tk = tok0 + tl0 + p * TP + t;
+          if (tk < d.m) {
+            const int8_t* src = ep + t * kEpRow + 16 * (lane & 15);
+            if (pass_acc == 0)
+              store_row16(d.y, d.n, tk, row, src);
+            else
+              store_row16(d.acc, d.n, tk, row, src);
+          }
+        }
+      }
+    }
+  }
+}
+
 // Partial sums of a tile whose reduction is split: every range adds its
 // int32 partials (already net of its activation sums) into the scratch slot
 // of (block, token tile) with device-scope atomics, in the accumulator
 // layout [r2][tile][register][lane], so that each atomic instruction covers
 // 256 contiguous bytes.  The range that arrives last (arrival counter) takes
-// the totals back with an exchange that also clears the slot, and writes the
+// the totals back with an exchange that also clears the slot, and stores the
 // outputs.  Integer addition is exact and order-free.
 template <class C>
 __device__ __forceinline__ void combine_split(const Desc& d, TileState<C>& x,
-                                              int blk, int tt, int tok0,
-                                              const int* tsum, int32_t* sacc,
+                                              v16i (&fin)[2][C::NB], int blk,
+                                              int tt, int tok0, int32_t* sacc,
                                               int32_t* scnt) {
   constexpr int NB = C::NB;
-  const int lane = x.lane, h = x.h, li = lane & 31, wave = x.wave;
+  const int lane = x.lane;
   const int64_t slot = d.slot0 + (int64_t)blk * d.ntt + tt;
   int32_t* part = sacc + slot * (64 * C::BM);
 #pragma unroll
   for (int r2 = 0; r2 < 2; ++r2)
 #pragma unroll
-    for (int i = 0; i < NB; ++i) {
-      const int qs = tsum[32 * ((i + wave) % NB) + li];
+    for (int i = 0; i < NB; ++i)
 #pragma unroll
       for (int g = 0; g < 16; ++g)
-        atomicAdd(part + ((r2 * NB + i) * 16 + g) * 64 + lane,
-                  x.acc[r2][i][g] - qs);
-    }
+        atomicAdd(part + ((r2 * NB + i) * 16 + g) * 64 + lane, fin[r2][i][g]);
   // The partials travel only through device-scope atomics, performed at the
   // coherence point; waiting for them orders them before the arrival.
   __builtin_amdgcn_s_waitcnt(0);
@@ -365,17 +485,13 @@ __device__ __forceinline__ void combine_split(const Desc& d, TileState<C>& x,
 #pragma unroll
     for (int r2 = 0; r2 < 2; ++r2)
 #pragma unroll
-      for (int i = 0; i < NB; ++i) {
-        v16i tot;
+      for (int i = 0; i < NB; ++i)
 #pragma unroll
         for (int g = 0; g < 16; ++g)
-          tot[g] = atomicExch(part + ((r2 * NB + i) * 16 + g) * 64 + lane, 0);
-        const int tok = tok0 + 32 * ((i + wave) % NB) + li;
-        if (tok < d.m)
-          store_rows(d, tot, blk * 64 + 32 * r2, tok, h, 0,
-                     *((gcfloat_ptr)d.sa + tok));
-      }
+          fin[r2][i][g] =
+              atomicExch(part + ((r2 * NB + i) * 16 + g) * 64 + lane, 0);
     if (lane == 0) atomicExch(scnt + slot, 0);
+    store_tile<C>(d, x, fin, blk, tok0);
   }
   __builtin_amdgcn_s_waitcnt(0);
 }
@@ -462,21 +578,19 @@ __device__ __forceinline__ void run_tile(const Desc& d, int rt, int tt,
   __syncthreads();
 
   if (!blk_ok) return;
-  if (d.nsplit > 1) {
-    combine_split<C>(d, x, blk, tt, tok0, tsum, sacc, scnt);
-    return;
-  }
+  // sums net of the activation sums, in place
 #pragma unroll
   for (int i = 0; i < NB; ++i) {
-    const int tl = 32 * ((i + wave) % NB) + li;  // token within the tile
-    const int tok = tok0 + tl;
-    if (tok < d.m) {
-      const int qs = tsum[tl];
-      const float sa = *((gcfloat_ptr)d.sa + tok);
-      store_rows(d, x.acc[0][i], blk * 64, tok, h, qs, sa);
-      store_rows(d, x.acc[1][i], blk * 64 + 32, tok, h, qs, sa);
-    }
+    const int qs = tsum[32 * ((i + wave) % NB) + li];
+#pragma unroll
+    for (int r2 = 0; r2 < 2; ++r2)
+#pragma unroll
+      for (int g = 0; g < 16; ++g) x.acc[r2][i][g] -= qs;
   }
+  if (d.nsplit > 1)
+    combine_split<C>(d, x, x.acc, blk, tt, tok0, sacc, scnt);
+  else
+    store_tile<C>(d, x, x.acc, blk, tok0);
 }
 
 template <class C>
