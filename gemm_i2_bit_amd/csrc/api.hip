@@ -98,6 +98,7 @@ Desc make_desc(const uint8_t* packed, float s_w, int64_t n, int64_t k,
   d.nsplit = 1;
   d.split_len = d.kc;
   d.slot0 = -1;
+  d.region0 = -1;
   return d;
 }
 
@@ -156,14 +157,17 @@ PlanHeader plan_layout(const bt_problem* probs, int32_t count) {
   h.m = m;
   h.kind = bt::plan_kind(m);
   const std::vector<Split> split = plan_splits(probs, count, h.kind);
-  int64_t blocks = 0, chunks = 0, units = 0, slots = 0;
+  int64_t blocks = 0, chunks = 0, units = 0, slots = 0, regions = 0;
   for (int32_t i = 0; i < count; ++i) {
     const int64_t nblk = (probs[i].n + 63) / 64;
     blocks += nblk;
     chunks += nblk * (probs[i].k / 64);
     units += bt::kind_units(h.kind, probs[i].n, m) * split[i].nsplit;
-    if (h.kind != bt::kKindDot4 && split[i].nsplit > 1)
-      slots += nblk * ((m + bt::token_tile(m) - 1) / bt::token_tile(m));
+    if (h.kind != bt::kKindDot4 && split[i].nsplit > 1) {
+      const int64_t s = nblk * ((m + bt::token_tile(m) - 1) / bt::token_tile(m));
+      slots += s;
+      regions += s * split[i].nsplit;
+    }
   }
   h.blocks = blocks;
   h.total_chunks = chunks;
@@ -173,11 +177,13 @@ PlanHeader plan_layout(const bt_problem* probs, int32_t count) {
   h.chunk_off = up(h.desc_off + (int64_t)count * sizeof(Desc));
   h.unit_off = up(h.chunk_off + (int64_t)count * 8);
   h.sacc_off = up(h.unit_off + h.units * (int64_t)sizeof(Unit));
+  // streaming kind: one 64-bit slot (arrival count and partial total) per
+  // row, token and row block; matrix-core kinds: split-reduction regions
   const int64_t sacc_bytes = h.kind == bt::kKindDot4
-                                 ? blocks * m * 64 * 4
-                                 : slots * bt::split_slot_ints(m) * 4;
+                                 ? blocks * m * 64 * 8
+                                 : regions * bt::split_region_ints(m) * 4;
   h.scnt_off = up(h.sacc_off + sacc_bytes);
-  const int64_t scnt_bytes = (h.kind == bt::kKindDot4 ? blocks : slots) * 4;
+  const int64_t scnt_bytes = h.kind == bt::kKindDot4 ? 0 : slots * 4;
   h.bytes = up(h.scnt_off + scnt_bytes);
   return h;
 }
@@ -202,7 +208,8 @@ int32_t check_group(const bt_problem* probs, int32_t count) {
     int64_t units = 0;
     for (int32_t i = 0; i < count; ++i)
       units += bt::kind_units(kind, probs[i].n, probs[i].m) * split[i].nsplit;
-    if (units >= INT32_MAX / 2) return BT_E_SHAPE;
+    // units bound the split regions (at most 4 per unit) and counters
+    if (units >= INT32_MAX / 8) return BT_E_SHAPE;
   }
   return BT_OK;
 }
@@ -293,7 +300,7 @@ int32_t bt_grouped_plan(const bt_problem* probs, int32_t count, void* plan,
   const std::vector<Split> split = plan_splits(probs, count, h.kind);
   int64_t chunk0 = 0;
   int64_t blk0 = 0;
-  int64_t slot0 = 0;
+  int64_t slot0 = 0, region0 = 0;
   for (int32_t i = 0; i < count; ++i) {
     const bt_problem& p = probs[i];
     Desc d = make_desc(p.packed, p.s_w, p.n, p.k, p.m, p.x_q, p.s_a, p.y,
@@ -304,8 +311,10 @@ int32_t bt_grouped_plan(const bt_problem* probs, int32_t count, void* plan,
       d.nsplit = split[i].nsplit;
       d.split_len = split[i].len;
       if (d.nsplit > 1) {
-        d.slot0 = slot0;
+        d.slot0 = (int32_t)slot0;
+        d.region0 = (int32_t)region0;
         slot0 += (int64_t)d.nblk * d.ntt;
+        region0 += (int64_t)d.nblk * d.ntt * d.nsplit;
       }
     }
     memcpy(out + h.desc_off + (int64_t)i * sizeof(Desc), &d, sizeof(d));

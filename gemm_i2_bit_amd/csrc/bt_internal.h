@@ -28,11 +28,13 @@ struct alignas(16) Desc {
   int32_t kc;         // k / 64 = chunks per row block
   // matrix-core kinds: the reduction of every tile is split into nsplit
   // ranges of split_len chunks (even; the last range may be shorter); with
-  // nsplit > 1, 64-row block b and token tile t combine their partial sums
-  // in scratch slot slot0 + b * ntt + t
+  // nsplit > 1, 64-row block b and token tile t count the arrivals of their
+  // ranges in counter slot0 + b * ntt + t, and range r leaves its partial
+  // sums in scratch region region0 + (b * ntt + t) * nsplit + r
   int32_t nsplit;
   int32_t split_len;
-  int64_t slot0;
+  int32_t slot0;
+  int32_t region0;
 };
 static_assert(sizeof(Desc) == 96, "Desc is 96 bytes");
 
@@ -46,10 +48,13 @@ struct Unit {
 
 // Host-side header at the start of a grouped plan image.  Layout:
 //   PlanHeader | Desc[count] | int64 chunk0[count] | Unit[units] |
-//   int32 scratch_acc[slots * slot ints] | int32 scratch_cnt[slots]
-// The streaming kind has units = 0 and one slot of m * 64 ints per row block.
-// The matrix-core kinds have one slot of 64 * token_tile ints per (row block,
-// token tile) of the problems whose reduction is split, and none otherwise.
+//   int32 scratch_acc[...] | int32 scratch_cnt[...]
+// The streaming kind has units = 0, one slot of m * 64 int64 (arrival count
+// in the high half, partial total in the low half) per row block, and no
+// counters.
+// The matrix-core kinds have, for the problems whose reduction is split, one
+// region of 64 * token_tile ints per (row block, token tile, range) and one
+// counter per (row block, token tile); none otherwise.
 struct PlanHeader {
   uint32_t magic;
   int32_t count;
@@ -89,8 +94,8 @@ inline int64_t kind_units(int kind, int64_t n, int64_t m) {
   const int bm = token_tile(m);
   return (n + 255) / 256 * ((m + bm - 1) / bm);
 }
-// int32 entries of one split-reduction scratch slot (64 rows x token tile)
-inline int64_t split_slot_ints(int64_t m) { return 64 * token_tile(m); }
+// int32 entries of one split-reduction scratch region (64 rows x token tile)
+inline int64_t split_region_ints(int64_t m) { return 64 * token_tile(m); }
 #ifndef BT_STREAM_WG_PER_CU
 #define BT_STREAM_WG_PER_CU 2
 #endif

@@ -452,55 +452,66 @@ __device__ __forceinline__ void store_tile(const Desc& d, const TileState<C>& x,
   }
 }
 
-// Partial sums of a tile whose reduction is split: every range adds its
-// int32 partials (already net of its activation sums) into the scratch slot
-// of (block, token tile) with device-scope atomics, in the accumulator
-// layout [r2][tile][register][lane], so that each atomic instruction covers
-// 256 contiguous bytes.  The range that arrives last (arrival counter) takes
-// the totals back with an exchange that also clears the slot, and stores the
+// Partial sums of a tile whose reduction is split over nsplit ranges: range
+// ks stores its int32 partials (already net of its activation sums) in its
+// own scratch region, in the accumulator layout [r2][tile][register][lane]
+// so that each store covers 256 contiguous bytes, with device-scope stores
+// that write through to the coherence point.  Once they are complete it
+// counts its arrival with one device-scope atomic; the range that arrives
+// last reads the other ranges' regions with device-scope loads, adds them
+// to its own sums, clears the counter for the next launch and stores the
 // outputs.  Integer addition is exact and order-free.
 template <class C>
 __device__ __forceinline__ void combine_split(const Desc& d, TileState<C>& x,
                                               v16i (&fin)[2][C::NB], int blk,
-                                              int tt, int tok0, int32_t* sacc,
-                                              int32_t* scnt) {
+                                              int tt, int ks, int tok0,
+                                              int32_t* sacc, int32_t* scnt) {
   constexpr int NB = C::NB;
+  constexpr int64_t R = 64 * C::BM;  // ints per region
   const int lane = x.lane;
-  const int64_t slot = d.slot0 + (int64_t)blk * d.ntt + tt;
-  int32_t* part = sacc + slot * (64 * C::BM);
+  const int64_t tile = (int64_t)blk * d.ntt + tt;
+  const int64_t slot = d.slot0 + tile;
+  int32_t* regions = sacc + (d.region0 + tile * d.nsplit) * R;
+  int32_t* own = regions + ks * R;
 #pragma unroll
   for (int r2 = 0; r2 < 2; ++r2)
 #pragma unroll
     for (int i = 0; i < NB; ++i)
 #pragma unroll
       for (int g = 0; g < 16; ++g)
-        atomicAdd(part + ((r2 * NB + i) * 16 + g) * 64 + lane, fin[r2][i][g]);
-  // The partials travel only through device-scope atomics, performed at the
-  // coherence point; waiting for them orders them before the arrival.
+        __hip_atomic_store(own + ((r2 * NB + i) * 16 + g) * 64 + lane,
+                           fin[r2][i][g], __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+  // the partials are at the coherence point before the arrival is counted
   __builtin_amdgcn_s_waitcnt(0);
   int arrived = 0;
   if (lane == 0) arrived = atomicAdd(scnt + slot, 1);
   arrived = __builtin_amdgcn_readfirstlane(arrived);
   if (arrived == d.nsplit - 1) {
+    for (int r = 0; r < d.nsplit; ++r) {
+      if (r == ks) continue;
+      const int32_t* other = regions + r * R;
 #pragma unroll
-    for (int r2 = 0; r2 < 2; ++r2)
+      for (int r2 = 0; r2 < 2; ++r2)
 #pragma unroll
-      for (int i = 0; i < NB; ++i)
+        for (int i = 0; i < NB; ++i)
 #pragma unroll
-        for (int g = 0; g < 16; ++g)
-          fin[r2][i][g] =
-              atomicExch(part + ((r2 * NB + i) * 16 + g) * 64 + lane, 0);
+          for (int g = 0; g < 16; ++g)
+            fin[r2][i][g] += __hip_atomic_load(
+                other + ((r2 * NB + i) * 16 + g) * 64 + lane, __ATOMIC_RELAXED,
+                __HIP_MEMORY_SCOPE_AGENT);
+    }
     if (lane == 0) atomicExch(scnt + slot, 0);
     store_tile<C>(d, x, fin, blk, tok0);
   }
-  __builtin_amdgcn_s_waitcnt(0);
 }
 
 // One workgroup tile: weight rows [256 rt, 256 rt + 256) x tokens
-// [BM tt, BM tt + BM), reduction over chunks [c_begin, c_end).
+// [BM tt, BM tt + BM), reduction over chunks [c_begin, c_end) (range ks of
+// the problem's split).
 template <class C>
 __device__ __forceinline__ void run_tile(const Desc& d, int rt, int tt,
-                                         int c_begin, int c_end,
+                                         int ks, int c_begin, int c_end,
                                          int32_t* sacc, int32_t* scnt) {
   constexpr int NB = C::NB;
   int* tsum = tsum_array<C>();
@@ -588,7 +599,7 @@ __device__ __forceinline__ void run_tile(const Desc& d, int rt, int tt,
       for (int g = 0; g < 16; ++g) x.acc[r2][i][g] -= qs;
   }
   if (d.nsplit > 1)
-    combine_split<C>(d, x, x.acc, blk, tt, tok0, sacc, scnt);
+    combine_split<C>(d, x, x.acc, blk, tt, ks, tok0, sacc, scnt);
   else
     store_tile<C>(d, x, x.acc, blk, tok0);
 }
@@ -596,7 +607,7 @@ __device__ __forceinline__ void run_tile(const Desc& d, int rt, int tt,
 template <class C>
 __global__ __launch_bounds__(256, 2) void tiled_kernel(Desc d, int ntt) {
   const int u = blockIdx.x;
-  run_tile<C>(d, u / ntt, u % ntt, 0, d.k >> 6, nullptr, nullptr);
+  run_tile<C>(d, u / ntt, u % ntt, 0, 0, d.k >> 6, nullptr, nullptr);
 }
 
 // Unit sub-index: (256-row tile * ntt + token tile) * nsplit + range.
@@ -611,7 +622,7 @@ __global__ __launch_bounds__(256, 2) void tiled_grouped_kernel(
   const int ks = u.sub % d.nsplit;
   const int c_begin = ks * d.split_len;
   const int c_end = min(c_begin + d.split_len, d.k >> 6);
-  run_tile<C>(d, tile / ntt, tile % ntt, c_begin, c_end, sacc, scnt);
+  run_tile<C>(d, tile / ntt, tile % ntt, ks, c_begin, c_end, sacc, scnt);
 }
 
 template <class C>

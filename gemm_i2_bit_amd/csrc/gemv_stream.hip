@@ -25,10 +25,10 @@
 //    subtracts the token's activation sum (sum (c - 1) q = sum c q - sum q;
 //    bitnet.cpp CPU tutorial §1.1 for the sign-and-accumulate product).
 //  * A row block cut by a wave-range boundary is shared by 2+ waves: each
-//    adds its int32 partial sums into a scratch slot with device-scope
-//    atomics (integer addition is exact and order-free), the last to arrive
-//    (arrival counter) reads the total, writes the outputs and clears the
-//    slot and counter for the next launch.
+//    adds its partial sums into 64-bit scratch slots that also count the
+//    arrivals (one device-scope atomic with return per row and token); the
+//    lane that completes the count holds the total, writes the output and
+//    clears the slot for the next launch.
 #include "bt_internal.h"
 
 namespace bt {
@@ -143,6 +143,7 @@ struct Stream {
   int32_t* sacc;
   int32_t* scnt;
   int qsum[TOK];
+  float sav[TOK];    // the tokens' activation scales (read once per problem)
 
   // Next group after g in a segment ending at problem-local chunk s1.
   __device__ __forceinline__ Group next(Group g, int s1) const {
@@ -232,15 +233,8 @@ struct Stream {
   }
 
   __device__ __forceinline__ void write_rows(int rb, const int (&sum)[TOK]) {
-    const int row = rb * 64 + (threadIdx.x & 63);
-    if (row >= n) return;
 #pragma unroll
-    for (int t = 0; t < TOK; ++t) {
-      const int acc = sum[t] - qsum[t];
-      const size_t o = (size_t)t * n + row;
-      if (accout != nullptr) accout[o] = acc;
-      y[o] = __fmul_rn(__fmul_rn((float)acc, sw), sa[t]);
-    }
+    for (int t = 0; t < TOK; ++t) write_one(rb, t, sum[t]);
   }
 
   // Row block rb lies entirely in this wave's range: write its outputs.
@@ -252,34 +246,45 @@ struct Stream {
     write_rows(rb, sum);
   }
 
-  // This wave holds only part of row block rb (partial sums in sum[]): add
-  // them into the block's scratch slot; the last contributor writes the
-  // outputs.
+  // One output of row block rb, token t (lane = row).
+  __device__ __forceinline__ void write_one(int rb, int t, int sum) {
+    const int row = rb * 64 + (threadIdx.x & 63);
+    if (row >= n) return;
+    const int acc = sum - qsum[t];
+    const size_t o = (size_t)t * n + row;
+    if (accout != nullptr) accout[o] = acc;
+    y[o] = __fmul_rn(__fmul_rn((float)acc, sw), sav[t]);
+  }
+
+  // This wave holds only part of row block rb (partial sums in sum[]).  Each
+  // (row, token) of the block has a 64-bit scratch slot holding
+  // (arrivals << 32) + partial total: one atomic add with return of
+  // (1 << 32) + partial adds this wave's share and counts it, and the lane
+  // that sees the arrival count reach the number of contributors holds the
+  // total (the partial totals stay below 2^31 in magnitude, so the two
+  // fields decode exactly), writes the output and clears the slot for the
+  // next launch.  Integer addition is exact and order-free; no lane waits
+  // for another, and nothing else is read back.
   __device__ __forceinline__ void finish_partial(int rb, int (&sum)[TOK]) {
     const int lane = threadIdx.x & 63;
     const int64_t first = chunk0 + (int64_t)rb * kc;
     const int64_t last = first + kc - 1;
     const int64_t slot = (int64_t)blk0 + rb;
-    int32_t* part = sacc + slot * (TOK * 64);
+    unsigned long long* sp =
+        reinterpret_cast<unsigned long long*>(sacc) + slot * (TOK * 64);
+    const int64_t contributors = owner(last, W, T) - owner(first, W, T) + 1;
 #pragma unroll
-    for (int t = 0; t < TOK; ++t) atomicAdd(part + t * 64 + lane, sum[t]);
-    // The partial sums travel only through device-scope atomics, which are
-    // performed at the coherence point; waiting for this wave's atomics to
-    // complete orders them before its arrival.  (A full agent fence would
-    // also write back and invalidate the L2 of the XCD, which nothing here
-    // needs.)
-    __builtin_amdgcn_s_waitcnt(0);
-    const int contributors = (int)(owner(last, W, T) - owner(first, W, T) + 1);
-    int arrived = 0;
-    if (lane == 0) arrived = atomicAdd(scnt + slot, 1);
-    arrived = __builtin_amdgcn_readfirstlane(arrived);
-    if (arrived == contributors - 1) {
-#pragma unroll
-      for (int t = 0; t < TOK; ++t) sum[t] = atomicExch(part + t * 64 + lane, 0);
-      if (lane == 0) atomicExch(scnt + slot, 0);
-      write_rows(rb, sum);
+    for (int t = 0; t < TOK; ++t) {
+      const int64_t delta = ((int64_t)1 << 32) + (int64_t)sum[t];
+      const int64_t now =
+          (int64_t)atomicAdd(sp + t * 64 + lane, (unsigned long long)delta) +
+          delta;
+      const int64_t arrivals = (now + ((int64_t)1 << 31)) >> 32;
+      if (arrivals == contributors) {
+        write_one(rb, t, (int)(now - (contributors << 32)));
+        atomicExch(sp + t * 64 + lane, 0ull);  // at the coherence point too
+      }
     }
-    __builtin_amdgcn_s_waitcnt(0);
   }
 
   // Sum of each token's activations (needed when finishing rows).  All
@@ -339,6 +344,8 @@ struct Stream {
     load_group(A, g, last);
     load_group(B, pg, last);
     activation_sums();  // its loads queue behind the first two groups
+#pragma unroll
+    for (int t = 0; t < TOK; ++t) sav[t] = sa[t];
     while (true) {
       g.uniform();
       pg.uniform();

@@ -149,11 +149,10 @@ def desc(img, p, i):
     s_w = raw[40:44].view(np.float32)[0]
     n, k, m, nblk, ntt = raw[44:64].view(np.int32)
     chunk0 = raw[64:72].view(np.int64)[0]
-    blk0, kc, nsplit, split_len = raw[72:88].view(np.int32)
-    slot0 = raw[88:96].view(np.int64)[0]
+    blk0, kc, nsplit, split_len, slot0, region0 = raw[72:96].view(np.int32)
     return dict(ptrs=ptrs, s_w=s_w, n=n, k=k, m=m, nblk=nblk, ntt=ntt,
                 chunk0=chunk0, blk0=blk0, kc=kc, nsplit=nsplit,
-                split_len=split_len, slot0=slot0)
+                split_len=split_len, slot0=slot0, region0=region0)
 
 
 def test_grouped_plan_layout_stream(L):
@@ -173,9 +172,10 @@ def test_grouped_plan_layout_stream(L):
     for off in ("desc_off", "chunk_off", "unit_off", "sacc_off", "scnt_off",
                 "bytes"):
         assert p[off] % 256 == 0
-    # scratch: 64 int32 partial sums per row block and token, one counter
-    assert p["scnt_off"] - p["sacc_off"] >= sum(nblk) * 64 * 4
-    assert p["bytes"] - p["scnt_off"] >= sum(nblk) * 4
+    # scratch: one 64-bit slot (arrival count, partial total) per row of
+    # every row block and token
+    assert p["scnt_off"] - p["sacc_off"] >= sum(nblk) * 64 * 8
+    assert p["bytes"] >= p["scnt_off"]
     assert not img[p["sacc_off"]:].any()
     # problems keep their order; chunk and block offsets are prefix sums
     prefix_c = np.cumsum([0] + [b * c for b, c in zip(nblk, kc)])[:-1]
@@ -226,15 +226,14 @@ def test_grouped_plan_layout_prefill(L):
     rest = u[tiles[0] + tiles[1]:]
     assert rest[:, 0].tolist() == [2] * (tiles[2] * 3)
     assert rest[:, 1].tolist() == list(range(tiles[2] * 3))
-    for i, (nsplit, length, slot0) in enumerate([(1, 40, -1), (1, 40, -1),
-                                                 (3, 36, 0)]):
+    for i, want in enumerate([(1, 40, -1, -1), (1, 40, -1, -1),
+                              (3, 36, 0, 0)]):
         d = desc(img, p, i)
-        assert (d["nsplit"], d["split_len"], d["slot0"]) == (nsplit, length,
-                                                             slot0)
-    # one scratch slot (64 rows x 128 tokens of int32) and one counter per
-    # (64-row block, token tile) of the split problem
+        assert (d["nsplit"], d["split_len"], d["slot0"], d["region0"]) == want
+    # per (64-row block, token tile) of the split problem: one region of
+    # 64 rows x 128 tokens of int32 per range, and one counter
     slots = 40 * 4
-    assert p["scnt_off"] - p["sacc_off"] >= slots * 64 * 128 * 4
+    assert p["scnt_off"] - p["sacc_off"] >= slots * 3 * 64 * 128 * 4
     assert p["bytes"] - p["scnt_off"] >= slots * 4
     assert not img[p["sacc_off"]:].any()  # the scratch area starts at zero
 
