@@ -2,8 +2,8 @@
 """Benchmark of the ternary W1.58A8 hot path on one MI355X.
 
 A step is one pass of the per-token path over a whole synthetic weight set:
-per-token int8 quantization of every projection's activations (bt_quant_act,
-one launch per distinct input length) and every ternary product with its
+per-token int8 quantization of every projection's activations (one
+bt_quant_act_many launch) and every ternary product with its
 rescale (one grouped launch, bt_gemm_grouped).  Packing is the offline
 conversion step and runs before timing.  Inputs are resident in HBM when the
 timed region starts.
@@ -120,8 +120,9 @@ class WorkSet:
 
     # the step ------------------------------------------------------------
     def quant(self):
-        for k in self.ks:
-            self.bt.bt_quant_act(self.x[k], self.xq[k], self.sa[k])
+        self.bt.bt_quant_act_many([self.x[k] for k in self.ks],
+                                  [self.xq[k] for k in self.ks],
+                                  [self.sa[k] for k in self.ks])
 
     def product(self):
         if self.mode == "grouped":

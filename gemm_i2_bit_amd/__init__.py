@@ -3,8 +3,8 @@ library.  Argument marshalling only: every step of the product runs in the
 library's HIP kernels.  PyTorch supplies device memory and streams.
 
 Functions carry the C ABI's names (see include/bt.h for the contract):
-bt_pack_i2s, bt_quant_act, bt_gemv, bt_gemm, bt_grouped_plan,
-bt_gemm_grouped, bt_packed_bytes, bt_status_str.
+bt_pack_i2s, bt_quant_act, bt_quant_act_many, bt_gemv, bt_gemm,
+bt_grouped_plan, bt_gemm_grouped, bt_packed_bytes, bt_status_str.
 """
 from __future__ import annotations
 
@@ -18,6 +18,9 @@ LIB_PATH = os.path.join(_HERE, "libbt.so")
 
 BT_OK, BT_E_NULL, BT_E_SHAPE, BT_E_ALIGN, BT_E_ARG, BT_E_HIP, BT_E_ARCH = (
     0, -1, -2, -3, -4, -5, -6)
+
+BT_MAX_M = 1 << 24
+BT_MAX_QUANT_JOBS = 16
 
 _lib = None
 
@@ -34,6 +37,12 @@ class bt_problem(ctypes.Structure):
                 ("acc", ctypes.c_void_p), ("s_w", ctypes.c_float),
                 ("n", ctypes.c_int32), ("k", ctypes.c_int32),
                 ("m", ctypes.c_int32)]
+
+
+class bt_quant_job(ctypes.Structure):
+    _fields_ = [("x", ctypes.c_void_p), ("x_q", ctypes.c_void_p),
+                ("s_a", ctypes.c_void_p), ("m", ctypes.c_int64),
+                ("k", ctypes.c_int64)]
 
 
 def lib() -> ctypes.CDLL:
@@ -55,6 +64,8 @@ def lib() -> ctypes.CDLL:
         L.bt_pack_i2s.restype = i32
         L.bt_quant_act.argtypes = [p, i64, i64, p, p, p]
         L.bt_quant_act.restype = i32
+        L.bt_quant_act_many.argtypes = [p, i32, p]
+        L.bt_quant_act_many.restype = i32
         L.bt_gemv.argtypes = [p, f32, i64, i64, p, p, p, p, p]
         L.bt_gemv.restype = i32
         L.bt_gemm.argtypes = [p, f32, i64, i64, i64, p, p, p, p, p]
@@ -144,6 +155,32 @@ def bt_quant_act(x, x_q=None, s_a=None, stream=None):
                               _dev(s_a, torch.float32, "s_a"),
                               _stream(stream)), "bt_quant_act")
     return x_q, s_a
+
+
+def bt_quant_act_many(xs, x_qs=None, s_as=None, stream=None):
+    """Several fp32 [m_j, k_j] (GPU) in one launch -> lists of int8 x_q and
+    fp32 s_a, each as bt_quant_act would give."""
+    torch = _torch()
+    xs = [x.unsqueeze(0) if x.dim() == 1 else x for x in xs]
+    if x_qs is None:
+        x_qs = [torch.empty(x.shape, dtype=torch.int8, device=x.device)
+                for x in xs]
+    if s_as is None:
+        s_as = [torch.empty(x.shape[0], dtype=torch.float32, device=x.device)
+                for x in xs]
+    if not (len(xs) == len(x_qs) == len(s_as)):
+        raise ValueError("xs, x_qs and s_as differ in length")
+    arr = (bt_quant_job * max(len(xs), 1))()
+    for j, (x, q, s) in enumerate(zip(xs, x_qs, s_as)):
+        m, k = x.shape
+        if q.numel() != m * k or s.numel() != m:
+            raise ValueError(f"job {j}: x_q or s_a has the wrong size")
+        arr[j] = bt_quant_job(_dev(x, torch.float32, "x"),
+                              _dev(q, torch.int8, "x_q"),
+                              _dev(s, torch.float32, "s_a"), m, k)
+    _check(lib().bt_quant_act_many(arr, len(xs), _stream(stream)),
+           "bt_quant_act_many")
+    return x_qs, s_as
 
 
 def _outputs(m, n, device, y, acc, want_acc):

@@ -261,6 +261,26 @@ int32_t bt_quant_act(const float* x, int64_t m, int64_t k, int8_t* x_q,
       bt::launch_quant(x, m, k, x_q, s_a, static_cast<hipStream_t>(stream)));
 }
 
+int32_t bt_quant_act_many(const bt_quant_job* jobs, int32_t count,
+                          void* stream) {
+  if (!jobs) return BT_E_NULL;
+  if (count < 1 || count > BT_MAX_QUANT_JOBS) return BT_E_ARG;
+  int64_t rows = 0;
+  for (int32_t j = 0; j < count; ++j) {
+    const bt_quant_job& q = jobs[j];
+    if (!q.x || !q.x_q || !q.s_a) return BT_E_NULL;
+    if (!m_ok(q.m) || !k_ok(q.k)) return BT_E_SHAPE;
+    if (!aligned(q.x, 16) || !aligned(q.x_q, 16) || !aligned(q.s_a, 4))
+      return BT_E_ALIGN;
+    rows += q.m;
+  }
+  if (rows > BT_MAX_M) return BT_E_SHAPE;
+  const int32_t arch = check_arch();
+  if (arch != BT_OK) return arch;
+  return hip_status(
+      bt::launch_quant_many(jobs, count, static_cast<hipStream_t>(stream)));
+}
+
 int32_t bt_gemm(const uint8_t* packed, float s_w, int64_t n, int64_t k,
                 int64_t m, const int8_t* x_q, const float* s_a, float* y,
                 int32_t* acc, void* stream) {

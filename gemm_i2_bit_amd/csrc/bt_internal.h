@@ -106,6 +106,9 @@ hipError_t launch_pack(const int8_t* t, int64_t n, int64_t k, uint8_t* packed,
                        int32_t* n_invalid, hipStream_t s);
 hipError_t launch_quant(const float* x, int64_t m, int64_t k, int8_t* xq,
                         float* sa, hipStream_t s);
+constexpr int kMaxQuantJobs = BT_MAX_QUANT_JOBS;
+hipError_t launch_quant_many(const bt_quant_job* jobs, int32_t count,
+                             hipStream_t s);
 hipError_t launch_dot4(const Desc& d, hipStream_t s);
 hipError_t launch_stream_grouped(const Desc* descs, const int64_t* chunk0,
                                  int32_t count, int64_t total_chunks, int m,

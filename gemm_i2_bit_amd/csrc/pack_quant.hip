@@ -9,6 +9,8 @@
 // "技术实现细节"), one absmax scale per token; the rounding and scale
 // formula (round half to even, x * (127 / a), clamp +-127, a >= 1e-5) are the
 // readings stated in bt.h.
+#include <string.h>
+
 #include "bt_internal.h"
 
 namespace bt {
@@ -80,42 +82,97 @@ __global__ __launch_bounds__(256) void pack_kernel(const int8_t* __restrict__ t,
   }
 }
 
-// One workgroup per token row.  Pass 1: absmax; pass 2: scale, round half to
-// even, clamp, store int8 (4 per 32-bit store).
+// Quantizes one token row of length k (one workgroup of 256 threads).  Rows
+// of up to kRegRow inputs stay in registers between the absmax and the
+// rounding (one read of the row); longer rows are read twice.  Both passes
+// take the same operations in the same precision: fp32 absmax, one correctly
+// rounded 127 / a, an fp32 product, round half to even, clamp +-127.
+constexpr int kRegVec = 8;                     // float4 per thread held
+constexpr int64_t kRegRow = 256 * 4 * kRegVec;  // 8192 inputs
+
+__device__ __forceinline__ uint32_t quant4(const float4& v, float inv) {
+  const float e[4] = {v.x, v.y, v.z, v.w};
+  uint32_t packed4 = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    float r = rintf(__fmul_rn(e[j], inv));  // round half to even
+    r = fminf(fmaxf(r, -127.0f), 127.0f);
+    packed4 |= ((uint32_t)(int32_t)r & 0xffu) << (8 * j);
+  }
+  return packed4;
+}
+
+__device__ __forceinline__ void quant_row(const float* __restrict__ x,
+                                          int64_t k, int8_t* __restrict__ xq,
+                                          float* __restrict__ sa, int64_t row,
+                                          float* part) {
+  const float4* xr = reinterpret_cast<const float4*>(x + row * k);
+  int32_t* qr = reinterpret_cast<int32_t*>(xq + row * k);
+  const int64_t k4 = k >> 2;
+  const int tid = threadIdx.x;
+  float amax = 0.0f;
+  float4 v[kRegVec];
+  const bool in_regs = k <= kRegRow;  // uniform
+  if (in_regs) {
+#pragma unroll
+    for (int r = 0; r < kRegVec; ++r) {
+      const int64_t i = tid + 256 * r;
+      v[r] = i < k4 ? xr[i] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+      amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v[r].x), fabsf(v[r].y)),
+                               fmaxf(fabsf(v[r].z), fabsf(v[r].w))));
+    }
+  } else {
+    for (int64_t i = tid; i < k4; i += 256) {
+      const float4 w = xr[i];
+      amax = fmaxf(amax, fmaxf(fmaxf(fabsf(w.x), fabsf(w.y)),
+                               fmaxf(fabsf(w.z), fabsf(w.w))));
+    }
+  }
+  amax = wave_max(amax);
+  if ((tid & 63) == 0) part[tid >> 6] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(part[0], part[1]), fmaxf(part[2], part[3]));
+  const float a = fmaxf(amax, 1e-5f);
+  const float inv = __fdiv_rn(127.0f, a);
+  if (in_regs) {
+#pragma unroll
+    for (int r = 0; r < kRegVec; ++r) {
+      const int64_t i = tid + 256 * r;
+      if (i < k4) qr[i] = (int32_t)quant4(v[r], inv);
+    }
+  } else {
+    for (int64_t i = tid; i < k4; i += 256) qr[i] = (int32_t)quant4(xr[i], inv);
+  }
+  if (tid == 0) sa[row] = __fdiv_rn(a, 127.0f);
+}
+
+// One workgroup per token row.
 __global__ __launch_bounds__(256) void quant_kernel(const float* __restrict__ x,
                                                     int64_t k,
                                                     int8_t* __restrict__ xq,
                                                     float* __restrict__ sa) {
   __shared__ float part[4];
-  const int64_t row = blockIdx.x;
-  const float4* xr = reinterpret_cast<const float4*>(x + row * k);
-  const int64_t k4 = k >> 2;
-  float amax = 0.0f;
-  for (int64_t i = threadIdx.x; i < k4; i += 256) {
-    const float4 v = xr[i];
-    amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)),
-                             fmaxf(fabsf(v.z), fabsf(v.w))));
-  }
-  amax = wave_max(amax);
-  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = amax;
-  __syncthreads();
-  amax = fmaxf(fmaxf(part[0], part[1]), fmaxf(part[2], part[3]));
-  const float a = fmaxf(amax, 1e-5f);
-  const float inv = __fdiv_rn(127.0f, a);
-  int32_t* qr = reinterpret_cast<int32_t*>(xq + row * k);
-  for (int64_t i = threadIdx.x; i < k4; i += 256) {
-    const float4 v = xr[i];
-    const float e[4] = {v.x, v.y, v.z, v.w};
-    uint32_t packed4 = 0;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      float r = rintf(__fmul_rn(e[j], inv));  // round half to even
-      r = fminf(fmaxf(r, -127.0f), 127.0f);
-      packed4 |= ((uint32_t)(int32_t)r & 0xffu) << (8 * j);
-    }
-    qr[i] = (int32_t)packed4;
-  }
-  if (threadIdx.x == 0) sa[row] = __fdiv_rn(a, 127.0f);
+  quant_row(x, k, xq, sa, blockIdx.x, part);
+}
+
+// Several quantizations in one launch: workgroup b takes the row
+// b - first[j] of the job j with first[j] <= b < first[j + 1].
+struct QuantJobs {
+  const float* x[kMaxQuantJobs];
+  int8_t* xq[kMaxQuantJobs];
+  float* sa[kMaxQuantJobs];
+  int64_t k[kMaxQuantJobs];
+  int64_t first[kMaxQuantJobs + 1];
+  int32_t count;
+};
+
+__global__ __launch_bounds__(256) void quant_many_kernel(QuantJobs jobs) {
+  __shared__ float part[4];
+  const int64_t b = blockIdx.x;
+  int j = 0;
+  while (j + 1 < jobs.count && jobs.first[j + 1] <= b) ++j;
+  quant_row(jobs.x[j], jobs.k[j], jobs.xq[j], jobs.sa[j], b - jobs.first[j],
+            part);
 }
 
 }  // namespace
@@ -132,6 +189,25 @@ hipError_t launch_pack(const int8_t* t, int64_t n, int64_t k, uint8_t* packed,
 hipError_t launch_quant(const float* x, int64_t m, int64_t k, int8_t* xq,
                         float* sa, hipStream_t s) {
   quant_kernel<<<dim3((unsigned)m), dim3(256), 0, s>>>(x, k, xq, sa);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_many(const bt_quant_job* jobs, int32_t count,
+                             hipStream_t s) {
+  QuantJobs q;
+  memset(&q, 0, sizeof(q));
+  int64_t rows = 0;
+  for (int32_t j = 0; j < count; ++j) {
+    q.x[j] = jobs[j].x;
+    q.xq[j] = jobs[j].x_q;
+    q.sa[j] = jobs[j].s_a;
+    q.k[j] = jobs[j].k;
+    q.first[j] = rows;
+    rows += jobs[j].m;
+  }
+  q.first[count] = rows;
+  q.count = count;
+  quant_many_kernel<<<dim3((unsigned)rows), dim3(256), 0, s>>>(q);
   return hipGetLastError();
 }
 

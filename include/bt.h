@@ -93,6 +93,24 @@ int32_t bt_pack_i2s(const int8_t* t, int64_t n, int64_t k, uint8_t* packed,
 int32_t bt_quant_act(const float* x, int64_t m, int64_t k, int8_t* x_q,
                      float* s_a, void* stream);
 
+/* Several independent quantizations in one launch, each exactly
+ * bt_quant_act(job.x, job.m, job.k, job.x_q, job.s_a): the per-token step of
+ * a decode pass whose projections read activation matrices of different
+ * widths.  jobs is a HOST array of 1 <= count <= BT_MAX_QUANT_JOBS entries,
+ * read during the call only; each job obeys the rules of bt_quant_act, and
+ * the total number of rows is at most BT_MAX_M.  Jobs must not overlap in
+ * memory. */
+#define BT_MAX_QUANT_JOBS 16
+typedef struct bt_quant_job {
+  const float* x;   /* fp32 [m, k], device, 16-byte aligned */
+  int8_t* x_q;      /* int8 [m, k], device, 16-byte aligned */
+  float* s_a;       /* fp32 [m], device, 4-byte aligned */
+  int64_t m;
+  int64_t k;
+} bt_quant_job;
+int32_t bt_quant_act_many(const bt_quant_job* jobs, int32_t count,
+                          void* stream);
+
 /* Ternary matrix-vector product (one token): bt_gemm with m = 1. */
 int32_t bt_gemv(const uint8_t* packed, float s_w, int64_t n, int64_t k,
                 const int8_t* x_q, const float* s_a, float* y, int32_t* acc,
@@ -130,10 +148,12 @@ typedef struct bt_problem {
  * size with bt_grouped_plan (pure host code, no HIP call); copy it to device
  * memory the caller owns (256-byte aligned); then call
  * bt_gemm_grouped(plan_dev, plan_host, s) as often as wanted.  The plan holds
- * the problem descriptors (pointers, shapes, scales), the work order and, for
- * m <= 4, a scratch area (int32, m * 256 bytes + 4 bytes per 64-row block)
- * in which workgroups that share a row block add their partial sums; that
- * area is zero in the host image and every complete launch leaves it zero.
+ * the problem descriptors (pointers, shapes, scales), the work order and a
+ * scratch area through which workgroups that share part of the work combine
+ * their partial sums: for m <= 4, m * 512 bytes per 64-row block; for m > 4,
+ * per-range regions and arrival counters for problems whose reduction is
+ * split.  The counters and slots are zero in the host image and every
+ * complete launch leaves them zero.
  * Hence launches that use one plan must not overlap (use one plan per
  * stream); rebuild the plan when any pointer, shape or scale changes.
  * plan_host must stay a byte-identical copy of the host image written by

@@ -36,7 +36,8 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     names = declared_functions()
-    assert {"bt_pack_i2s", "bt_quant_act", "bt_gemv", "bt_gemm",
+    assert {"bt_pack_i2s", "bt_quant_act", "bt_quant_act_many", "bt_gemv",
+            "bt_gemm",
             "bt_gemm_grouped", "bt_grouped_plan"} <= set(names)
     for name in names:
         assert hasattr(L, name), name
@@ -110,6 +111,37 @@ def test_pack_and_quant_argument_errors(L):
     assert L.bt_quant_act(P + 4, 1, 64, P, P, None) == bt.BT_E_ALIGN
     assert L.bt_quant_act(P, 1, 64, P + 4, P, None) == bt.BT_E_ALIGN
     assert L.bt_quant_act(P, 1, 64, P, P + 1, None) == bt.BT_E_ALIGN
+
+
+def quant_jobs(specs):
+    arr = (bt.bt_quant_job * max(len(specs), 1))()
+    for j, (m, k) in enumerate(specs):
+        base = P * (j + 1) * 16
+        arr[j] = bt.bt_quant_job(base, base + P, base + 2 * P, m, k)
+    return arr
+
+
+def test_quant_many_argument_errors(L):
+    ok = quant_jobs([(1, 64), (3, 128)])
+    assert L.bt_quant_act_many(None, 1, None) == bt.BT_E_NULL
+    assert L.bt_quant_act_many(ok, 0, None) == bt.BT_E_ARG
+    many = quant_jobs([(1, 64)] * (bt.BT_MAX_QUANT_JOBS + 1))
+    assert L.bt_quant_act_many(many, bt.BT_MAX_QUANT_JOBS + 1,
+                               None) == bt.BT_E_ARG
+    for field, code in (("x", bt.BT_E_NULL), ("x_q", bt.BT_E_NULL),
+                        ("s_a", bt.BT_E_NULL)):
+        arr = quant_jobs([(1, 64), (3, 128)])
+        setattr(arr[1], field, None)
+        assert L.bt_quant_act_many(arr, 2, None) == code, field
+    for j, (m, k) in enumerate([(0, 64), (1, 96), (1, 0)]):
+        arr = quant_jobs([(1, 64), (m, k)])
+        assert L.bt_quant_act_many(arr, 2, None) == bt.BT_E_SHAPE, (m, k)
+    big = quant_jobs([(bt.BT_MAX_M, 64), (1, 64)])
+    assert L.bt_quant_act_many(big, 2, None) == bt.BT_E_SHAPE
+    for field, delta in (("x", 4), ("x_q", 4), ("s_a", 1)):
+        arr = quant_jobs([(1, 64), (3, 128)])
+        setattr(arr[0], field, getattr(arr[0], field) + delta)
+        assert L.bt_quant_act_many(arr, 2, None) == bt.BT_E_ALIGN, field
 
 
 # ------------------------------------------------------------ grouped plans

@@ -20,7 +20,11 @@ bt = pytest.importorskip("gemm_i2_bit_amd")
 
 NTHREADS = min(16, os.cpu_count() or 1)
 RTOL = 1e-6
-GUARD = 4  # guard elements (16 bytes) on each side of every output
+GUARD_BYTES = 16  # guard on each side of every output (keeps alignment)
+
+
+def guard_len(dtype):
+    return GUARD_BYTES // torch.empty((), dtype=dtype).element_size()
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -37,13 +41,15 @@ def dev(a):
 
 
 def guarded(numel, dtype, fill):
-    buf = torch.full((numel + 2 * GUARD,), fill, dtype=dtype, device="cuda:0")
-    return buf, buf[GUARD:GUARD + numel]
+    g = guard_len(dtype)
+    buf = torch.full((numel + 2 * g,), fill, dtype=dtype, device="cuda:0")
+    return buf, buf[g:g + numel]
 
 
 def check_guards(buf, fill):
     host = buf.cpu()
-    head, tail = host[:GUARD], host[-GUARD:]
+    g = guard_len(buf.dtype)
+    head, tail = host[:g], host[-g:]
     if buf.dtype == torch.float32:
         assert torch.isnan(head).all() and torch.isnan(tail).all(), \
             "write outside the output"
@@ -123,6 +129,8 @@ def quant_cases():
         ("ties", ties),
         ("zero_tiny", zero_tiny),
         ("quarter_steps", np.round(wl.x_normal(rng, (4, 256)) * 4) / 4),
+        ("held_in_registers", wl.x_normal_outliers(rng, (2, 8192))),
+        ("read_twice", wl.x_normal_outliers(rng, (2, 8256))),
     ]
 
 
@@ -134,6 +142,36 @@ def test_quant_matches_oracle(name, x):
     np.testing.assert_array_equal(q_gpu.cpu().numpy(), q_ref)
     np.testing.assert_array_equal(s_gpu.cpu().numpy().view(np.uint32),
                                   s_ref.view(np.uint32))
+
+
+def check_quant_many(xs):
+    xs = [np.ascontiguousarray(x, np.float32) for x in xs]
+    qbufs = [guarded(x.size, torch.int8, 0x5A) for x in xs]
+    sbufs = [guarded(x.shape[0], torch.float32, float("nan")) for x in xs]
+    x_qs = [q.view(x.shape) for (_, q), x in zip(qbufs, xs)]
+    s_as = [s for _, s in sbufs]
+    bt.bt_quant_act_many([dev(x) for x in xs], x_qs, s_as)
+    torch.cuda.synchronize()
+    for x, q, s, (qb, _), (sb, _) in zip(xs, x_qs, s_as, qbufs, sbufs):
+        q_ref, s_ref = oracle.quant_act(x)
+        np.testing.assert_array_equal(q.cpu().numpy(), q_ref)
+        np.testing.assert_array_equal(s.cpu().numpy().view(np.uint32),
+                                      s_ref.view(np.uint32))
+        check_guards(qb, 0x5A)
+        check_guards(sb, None)
+
+
+def test_quant_many_matches_oracle():
+    """Every quantization case in one launch (rows of different lengths,
+    both the register-held and the two-read paths)."""
+    check_quant_many([x for _, x in quant_cases()])
+
+
+def test_quant_many_limits():
+    rng = np.random.default_rng(102)
+    check_quant_many([wl.x_normal(rng, (1, 2560))])
+    check_quant_many([wl.x_normal(rng, (m, 64 * (m + 1)))
+                      for m in range(1, bt.BT_MAX_QUANT_JOBS + 1)])
 
 
 # ------------------------------------------------------------- the product
