@@ -24,6 +24,11 @@
 //    block.  Codes c = trit + 1 are used as they are; the finalising wave
 //    subtracts the token's activation sum (sum (c - 1) q = sum c q - sum q;
 //    bitnet.cpp CPU tutorial §1.1 for the sign-and-accumulate product).
+//  * Finished row blocks are not stored at once: their sums wait in LDS
+//    (up to 16 / m blocks per wave) and leave in one burst when the wave's
+//    part of the problem is done, or when the staging area is full.  Writes
+//    scattered through the read stream cost far more time than their bytes
+//    (the memory has to turn the bus around for each of them).
 //  * A row block cut by a wave-range boundary is shared by 2+ waves: each
 //    adds its partial sums into 64-bit scratch slots that also count the
 //    arrivals (one device-scope atomic with return per row and token); the
@@ -43,7 +48,8 @@ typedef __attribute__((address_space(1))) int32_t* gint_ptr;
 typedef const __attribute__((address_space(1))) int* gcint_ptr;
 typedef const __attribute__((address_space(1))) float* gcfloat_ptr;
 
-constexpr int D = 8;  // chunks per load group (two groups in flight)
+
+constexpr int D = 4;  // chunks per load group (two groups in flight)
 
 __device__ __forceinline__ int sdot4(int a, int b, int c) {
   return __builtin_amdgcn_sdot4(a, b, c, false);
@@ -144,6 +150,12 @@ struct Stream {
   int32_t* scnt;
   int qsum[TOK];
   float sav[TOK];    // the tokens' activation scales (read once per problem)
+  // LDS staging of finished row blocks: kOut blocks of TOK rows of 64 sums;
+  // ocnt blocks are staged, the first of them is row block orb0, and the
+  // rest follow it (a segment finishes its whole blocks in order).
+  static constexpr int kOut = 16 / TOK;
+  int* obuf;
+  int ocnt, orb0;
 
   // Next group after g in a segment ending at problem-local chunk s1.
   __device__ __forceinline__ Group next(Group g, int s1) const {
@@ -232,18 +244,16 @@ struct Stream {
     }
   }
 
-  __device__ __forceinline__ void write_rows(int rb, const int (&sum)[TOK]) {
+  // Writes the staged row blocks and empties the staging area.
+  __device__ __forceinline__ void flush() {
+    const int lane = threadIdx.x & 63;
+    for (int i = 0; i < ocnt; ++i) {
 #pragma unroll
-    for (int t = 0; t < TOK; ++t) write_one(rb, t, sum[t]);
-  }
-
-  // Row block rb lies entirely in this wave's range: write its outputs.
-  __device__ __forceinline__ void finish_full(int rb, Acc<TOK>& a) {
-    int sum[TOK];
-#pragma unroll
-    for (int t = 0; t < TOK; ++t) sum[t] = a.total(t);
-    a.zero();
-    write_rows(rb, sum);
+      for (int t = 0; t < TOK; ++t)
+        write_one(orb0 + i, t, obuf[(i * TOK + t) * 64 + lane]);
+    }
+    orb0 += ocnt;
+    ocnt = 0;
   }
 
   // One output of row block rb, token t (lane = row).
@@ -287,16 +297,43 @@ struct Stream {
     }
   }
 
-  // Sum of each token's activations (needed when finishing rows).  All
-  // loads are issued before any is used: one round trip for k <= 4096.
-  __device__ __forceinline__ void activation_sums() {
+  // Sum of each token's activations (needed when finishing rows).  The
+  // first kActPer 16-byte pieces per lane and token are loaded before the
+  // segment's first weight groups (issue_act) and summed after those groups
+  // have been issued (finish_act): the sum then waits only for its own
+  // loads, which are older, and the weight stream keeps going.  Rows longer
+  // than kActPer KiB (rare: k > 8192 at m = 1) load the rest afterwards.
+  static constexpr int kActPer = TOK == 1 ? 8 : (TOK == 2 ? 7 : (TOK == 3 ? 4 : 3));
+  struct ActPre {
+    v4u v[TOK][kActPer];
+  };
+  __device__ __forceinline__ void issue_act(ActPre& p) const {
     const int lane = threadIdx.x & 63;
     const int n16 = k >> 4;  // 16-byte pieces per token row
 #pragma unroll
     for (int t = 0; t < TOK; ++t) {
       const gv4u_ptr q16 = (gv4u_ptr)(xq + (size_t)t * k);
+#pragma unroll
+      for (int u = 0; u < kActPer; ++u)  // clamped, unconditional
+        p.v[t][u] = q16[min(u * 64 + lane, n16 - 1)];
+    }
+  }
+  __device__ __forceinline__ void finish_act(const ActPre& p) {
+    const int lane = threadIdx.x & 63;
+    const int n16 = k >> 4;
+#pragma unroll
+    for (int t = 0; t < TOK; ++t) {
       int s = 0;
-      for (int i0 = 0; i0 < n16; i0 += 4 * 64) {
+#pragma unroll
+      for (int u = 0; u < kActPer; ++u) {
+        const int ones = u * 64 + lane < n16 ? 0x01010101 : 0;
+        s = sdot4((int)p.v[t][u].x, ones, s);
+        s = sdot4((int)p.v[t][u].y, ones, s);
+        s = sdot4((int)p.v[t][u].z, ones, s);
+        s = sdot4((int)p.v[t][u].w, ones, s);
+      }
+      const gv4u_ptr q16 = (gv4u_ptr)(xq + (size_t)t * k);
+      for (int i0 = kActPer * 64; i0 < n16; i0 += 4 * 64) {
         v4u v[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
@@ -340,23 +377,29 @@ struct Stream {
     Group pg = next(g, s1);
     Acc<TOK> a;
     a.zero();
+    ocnt = 0;
+    orb0 = head_rb + (head_cut ? 1 : 0);  // the first block finished whole
     v4u A[D], B[D];
-    load_group(A, g, last);
-    load_group(B, pg, last);
-    activation_sums();  // its loads queue behind the first two groups
+    {
+      ActPre pre;
+      issue_act(pre);
+      load_group(A, g, last);
+      load_group(B, pg, last);
+      finish_act(pre);
+    }
 #pragma unroll
     for (int t = 0; t < TOK; ++t) sav[t] = sa[t];
     while (true) {
       g.uniform();
       pg.uniform();
       consume(A, g, a);
-      if (g.c + g.cnt == kc) block_end(g.rb, head_rb, head_cut, head_sum, a);
+      group_end(g, head_rb, head_cut, head_sum, a);
       pg = next(pg, s1);
       load_group(A, pg, last);
       g = next(g, s1);
       if (g.cnt == 0) break;
       consume(B, g, a);
-      if (g.c + g.cnt == kc) block_end(g.rb, head_rb, head_cut, head_sum, a);
+      group_end(g, head_rb, head_cut, head_sum, a);
       pg = next(pg, s1);
       load_group(B, pg, last);
       g = next(g, s1);
@@ -371,19 +414,32 @@ struct Stream {
       for (int t = 0; t < TOK; ++t) sum[t] = a.total(t);
       finish_partial((s1 - 1) / kc, sum);
     }
+    flush();
   }
 
-  __device__ __forceinline__ void block_end(int rb, int head_rb,
+  // After each group: a group that ends a row block either stages the block
+  // (whole in this wave's range) or, for the cut head block, keeps its sums
+  // for the hand-off after the loop.
+  __device__ __forceinline__ void group_end(Group g, int head_rb,
                                             bool head_cut,
                                             int (&head_sum)[TOK],
                                             Acc<TOK>& a) {
-    if (head_cut && rb == head_rb) {
+    const bool end = g.c + g.cnt == kc;
+    const bool head = end && head_cut && g.rb == head_rb;
+    int sum[TOK];
 #pragma unroll
-      for (int t = 0; t < TOK; ++t) head_sum[t] = a.total(t);
-      a.zero();
-    } else {
-      finish_full(rb, a);
+    for (int t = 0; t < TOK; ++t) sum[t] = a.total(t);
+    if (head) {
+#pragma unroll
+      for (int t = 0; t < TOK; ++t) head_sum[t] = sum[t];
     }
+    if (end && !head) {
+      const int lane = threadIdx.x & 63;
+#pragma unroll
+      for (int t = 0; t < TOK; ++t) obuf[(ocnt * TOK + t) * 64 + lane] = sum[t];
+      if (++ocnt == kOut) flush();
+    }
+    if (end) a.zero();
   }
 };
 
@@ -399,6 +455,8 @@ __global__ __launch_bounds__(256) void stream_kernel(
       (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (wv >= W) return;
   Stream<TOK> st;
+  __shared__ int obuf_all[4][16 * 64];
+  st.obuf = obuf_all[threadIdx.x >> 6];
   st.lo = wv * total / W;
   st.hi = (wv + 1) * total / W;
   st.W = W;
