@@ -48,6 +48,8 @@ typedef __attribute__((address_space(1))) int32_t* gint_ptr;
 typedef const __attribute__((address_space(1))) int* gcint_ptr;
 typedef const __attribute__((address_space(1))) float* gcfloat_ptr;
 
+constexpr int kRsrcFlags = 0x00020000;  // raw buffer, 32-bit words
+
 
 constexpr int D = 4;  // chunks per load group (two groups in flight)
 
@@ -135,7 +137,7 @@ struct Group {
 template <int TOK>
 struct Stream {
   // problem
-  gv4u_ptr w;        // this lane's 16 bytes of chunk 0
+  const uint8_t* w;  // the problem's packed weights
   const int8_t* xq;
   const_fptr sa;     // scalar loads: a vector load would wait behind the
                      // weight loads in flight
@@ -171,16 +173,19 @@ struct Stream {
     return r;
   }
 
-  // Loads are unconditional (addresses clamped to chunk `last`); a clamped
-  // load re-reads a line that is already cached.
-  __device__ __forceinline__ void load_group(v4u (&buf)[D], Group g,
-                                             int last) const {
+  // Loads are unconditional: they go through a buffer resource that spans
+  // exactly the group's g.cnt chunks, so slots past g.cnt (and every slot of
+  // the empty group after the last) read as zero without touching memory.
+  // Streamed once: non-temporal.
+  __device__ __forceinline__ void load_group(v4u (&buf)[D], Group g) const {
     const int start = g.rb * kc + g.c;
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(w + (size_t)start * 1024), 0, g.cnt * 1024, kRsrcFlags);
+    const int lane16 = (threadIdx.x & 63) * 16;
 #pragma unroll
-    for (int j = 0; j < D; ++j) {
-      const int L = min(start + j, last);
-      buf[j] = __builtin_nontemporal_load(w + (size_t)L * 64);
-    }
+    for (int j = 0; j < D; ++j)
+      buf[j] = __builtin_bit_cast(
+          v4u, __builtin_amdgcn_raw_buffer_load_b128(r, lane16 + j * 1024, 0, 2));
   }
 
   // The 64 activation bytes of input chunk c for every token (SGPRs).
@@ -196,13 +201,11 @@ struct Stream {
     }
   }
 
-  // Chunk with activations qc; keep = 0 discards it (all codes 0, which
-  // contribute nothing) without a branch: the masks are scalar registers.
+  // Chunk wv with activations qc.  A chunk past the group's end reads as
+  // zero bytes: codes 0, which contribute nothing.
   __device__ __forceinline__ void dot_chunk(const v4u& wv, const QChunk& qc,
-                                            uint32_t keep,
                                             Acc<TOK>& a) const {
-    const uint32_t m0 = 0x03030303u & keep, m1 = 0x0C0C0C0Cu & keep,
-                   m2 = 0x30303030u & keep;
+    const uint32_t m0 = 0x03030303u, m1 = 0x0C0C0C0Cu, m2 = 0x30303030u;
     const uint32_t words[4] = {wv.x, wv.y, wv.z, wv.w};
 #pragma unroll
     for (int t = 0; t < TOK; ++t) {
@@ -220,8 +223,8 @@ struct Stream {
     }
   }
 
-  // All D chunks are consumed unconditionally (chunks past g.cnt are masked
-  // out and read a clamped activation chunk), so the compiler keeps every
+  // All D chunks are consumed unconditionally (chunks past g.cnt read as
+  // zero and use a clamped activation chunk), so the compiler keeps every
   // load of the group ahead of the first use instead of sinking loads into
   // branches.  Chunks go in runs of P: the run's activations are requested
   // together (one wait per run), and an opaque zero on their addresses plus
@@ -239,7 +242,7 @@ struct Stream {
       for (int r = 0; r < P; ++r) load_q(q[r], min(g.c + j + r, kc - 1), pin);
 #pragma unroll
       for (int r = 0; r < P; ++r)
-        dot_chunk(buf[j + r], q[r], j + r < g.cnt ? 0xFFFFFFFFu : 0u, a);
+        dot_chunk(buf[j + r], q[r], a);
       a.pin();
     }
   }
@@ -269,30 +272,50 @@ struct Stream {
   // This wave holds only part of row block rb (partial sums in sum[]).  Each
   // (row, token) of the block has a 64-bit scratch slot holding
   // (arrivals << 32) + partial total: one atomic add with return of
-  // (1 << 32) + partial adds this wave's share and counts it, and the lane
-  // that sees the arrival count reach the number of contributors holds the
-  // total (the partial totals stay below 2^31 in magnitude, so the two
-  // fields decode exactly), writes the output and clears the slot for the
-  // next launch.  Integer addition is exact and order-free; no lane waits
-  // for another, and nothing else is read back.
-  __device__ __forceinline__ void finish_partial(int rb, int (&sum)[TOK]) {
-    const int lane = threadIdx.x & 63;
-    const int64_t first = chunk0 + (int64_t)rb * kc;
-    const int64_t last = first + kc - 1;
-    const int64_t slot = (int64_t)blk0 + rb;
-    unsigned long long* sp =
-        reinterpret_cast<unsigned long long*>(sacc) + slot * (TOK * 64);
-    const int64_t contributors = owner(last, W, T) - owner(first, W, T) + 1;
+  // (1 << 32) + partial adds this wave's share and counts it.  The lane that
+  // sees the arrival count reach the number of contributors holds the total
+  // (the partial totals stay below 2^31 in magnitude, so the two fields
+  // decode exactly); it writes the output and clears the slot for the next
+  // launch.  Integer addition is exact and order-free; no lane waits for
+  // another.  A wave has at most two such blocks (the first and the last of
+  // its range); the atomics of both are issued, without a branch (a block
+  // that is not cut adds 0 to its own slot, which changes nothing), before
+  // settle looks at what either returned, so the round trips overlap.
+  struct HandOff {
+    uint64_t ret[TOK];  // what the atomics returned (slot before the add)
+    int64_t delta[TOK];
+    int rb;
+  };
+
+  __device__ __forceinline__ unsigned long long* slot_of(int rb) const {
+    return reinterpret_cast<unsigned long long*>(sacc) +
+           ((int64_t)blk0 + rb) * (TOK * 64) + (threadIdx.x & 63);
+  }
+
+  __device__ __forceinline__ void hand_off(HandOff& h, int rb,
+                                           const int (&sum)[TOK],
+                                           bool on) const {
+    unsigned long long* sp = slot_of(rb);
 #pragma unroll
     for (int t = 0; t < TOK; ++t) {
-      const int64_t delta = ((int64_t)1 << 32) + (int64_t)sum[t];
-      const int64_t now =
-          (int64_t)atomicAdd(sp + t * 64 + lane, (unsigned long long)delta) +
-          delta;
+      h.delta[t] = on ? ((int64_t)1 << 32) + (int64_t)sum[t] : 0;
+      h.ret[t] = atomicAdd(sp + t * 64, (unsigned long long)h.delta[t]);
+    }
+    h.rb = rb;
+  }
+
+  __device__ __forceinline__ void settle(const HandOff& h) {
+    const int64_t first = chunk0 + (int64_t)h.rb * kc;
+    const int64_t last = first + kc - 1;
+    const int64_t contributors = owner(last, W, T) - owner(first, W, T) + 1;
+    unsigned long long* sp = slot_of(h.rb);
+#pragma unroll
+    for (int t = 0; t < TOK; ++t) {
+      const int64_t now = (int64_t)h.ret[t] + h.delta[t];
       const int64_t arrivals = (now + ((int64_t)1 << 31)) >> 32;
       if (arrivals == contributors) {
-        write_one(rb, t, (int)(now - (contributors << 32)));
-        atomicExch(sp + t * 64 + lane, 0ull);  // at the coherence point too
+        write_one(h.rb, t, (int)(now - (contributors << 32)));
+        atomicExch(sp + t * 64, 0ull);  // at the coherence point too
       }
     }
   }
@@ -353,17 +376,16 @@ struct Stream {
   }
 
   // Stream chunks [s0, s1) of the current problem (problem-local indices) in
-  // groups of D chunks, double buffered: while group i is consumed, group
-  // i + 1 is in flight.  Every load is unconditional (clamped), so the wait
-  // before each group is a fixed count (the other buffer's D loads), and the
-  // only other memory operations in the loop are the output stores at the
-  // end of each whole row block.  A row block cut by the range (at most the
-  // first and the last) keeps its partial sums in registers; their atomic
-  // hand-off happens after the loop.
+  // groups of up to D chunks, double buffered: while group i is consumed,
+  // group i + 1 is in flight.  Every load is unconditional (range-checked),
+  // so the wait before each group is a fixed count (the other buffer's D
+  // loads); the loop's only other memory operations are LDS writes and the
+  // occasional burst of a full staging area.  A row block cut by the range
+  // (at most the first and the last) keeps its partial sums in registers;
+  // their atomic hand-off happens after the loop.
   __device__ __forceinline__ void segment(int s0, int s1) {
     s0 = __builtin_amdgcn_readfirstlane(s0);
     s1 = __builtin_amdgcn_readfirstlane(s1);
-    const int last = s1 - 1;
     const int head_rb = s0 / kc;
     const bool head_cut = s0 != head_rb * kc;  // first block starts early
     int head_sum[TOK];
@@ -383,8 +405,8 @@ struct Stream {
     {
       ActPre pre;
       issue_act(pre);
-      load_group(A, g, last);
-      load_group(B, pg, last);
+      load_group(A, g);
+      load_group(B, pg);
       finish_act(pre);
     }
 #pragma unroll
@@ -395,26 +417,31 @@ struct Stream {
       consume(A, g, a);
       group_end(g, head_rb, head_cut, head_sum, a);
       pg = next(pg, s1);
-      load_group(A, pg, last);
+      load_group(A, pg);
       g = next(g, s1);
       if (g.cnt == 0) break;
       consume(B, g, a);
       group_end(g, head_rb, head_cut, head_sum, a);
       pg = next(pg, s1);
-      load_group(B, pg, last);
+      load_group(B, pg);
       g = next(g, s1);
       if (g.cnt == 0) break;
     }
-    // the cut head block's sums were stashed only if it also ended here;
-    // otherwise it is the last block and still sits in the accumulators
-    if (head_cut && (head_rb + 1) * kc <= s1) finish_partial(head_rb, head_sum);
-    if (s1 % kc != 0) {  // the range ends inside the last row block
-      int sum[TOK];
-#pragma unroll
-      for (int t = 0; t < TOK; ++t) sum[t] = a.total(t);
-      finish_partial((s1 - 1) / kc, sum);
-    }
+    // The staged blocks go first; then both hand-offs are issued, and only
+    // then are the atomics' results looked at.  The cut head block's sums
+    // were stashed only if it also ended here; otherwise it is the last
+    // block and still sits in the accumulators.
     flush();
+    const bool head_off = head_cut && (head_rb + 1) * kc <= s1;
+    const bool tail_off = s1 % kc != 0;  // the range ends inside a block
+    int tail_sum[TOK];
+#pragma unroll
+    for (int t = 0; t < TOK; ++t) tail_sum[t] = a.total(t);
+    HandOff hh, ht;
+    hand_off(hh, head_rb, head_sum, head_off);
+    hand_off(ht, (s1 - 1) / kc, tail_sum, tail_off);
+    if (head_off) settle(hh);
+    if (tail_off) settle(ht);
   }
 
   // After each group: a group that ends a row block either stages the block
@@ -468,7 +495,7 @@ __global__ __launch_bounds__(256) void stream_kernel(
   int64_t pos = st.lo;
   while (pos < st.hi && p < count) {
     const Desc& d = descs[p];
-    st.w = (gv4u_ptr)(d.w) + (threadIdx.x & 63);
+    st.w = d.w;
     st.xq = d.xq;
     st.sa = (const_fptr)d.sa;
     st.y = (gfloat_ptr)d.y;
