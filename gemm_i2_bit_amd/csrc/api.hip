@@ -385,7 +385,7 @@ int32_t bt_gemm_grouped(const void* plan_dev, const void* plan_host,
   return hip_status(bt::launch_stream_grouped(
       descs, reinterpret_cast<const int64_t*>(base + h.chunk_off), h.count,
       h.total_chunks, h.m, reinterpret_cast<int32_t*>(mut + h.sacc_off),
-      reinterpret_cast<int32_t*>(mut + h.scnt_off), (int)wgs, s));
+      (int)wgs, s));
 }
 
 }  // extern "C"

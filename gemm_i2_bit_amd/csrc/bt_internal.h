@@ -112,7 +112,7 @@ hipError_t launch_quant_many(const bt_quant_job* jobs, int32_t count,
 hipError_t launch_dot4(const Desc& d, hipStream_t s);
 hipError_t launch_stream_grouped(const Desc* descs, const int64_t* chunk0,
                                  int32_t count, int64_t total_chunks, int m,
-                                 int32_t* sacc, int32_t* scnt, int workgroups,
+                                 int32_t* sacc, int workgroups,
                                  hipStream_t s);
 hipError_t launch_tiled(const Desc& d, hipStream_t s);
 hipError_t launch_tiled_grouped(const Desc* descs, const Unit* units,

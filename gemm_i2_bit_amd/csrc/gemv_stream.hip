@@ -12,7 +12,7 @@
 //    chunk L % kc.
 //  * The grid is persistent (a few workgroups per CU).  Wave w of W streams
 //    chunks [w T / W, (w + 1) T / W) (W <= T): every wave reads the same
-//    number of bytes, whatever the problem shapes, so the launch ends evenly.
+//    number of bytes, whatever the problem shapes.
 //  * Lane l of a wave owns row 64 rb + l; for chunk L it loads 16 bytes with
 //    one non-temporal 128-bit load (the wave reads 1 contiguous KiB); a wave
 //    issues a group of D chunks, then consumes them, and the other resident
@@ -31,9 +31,9 @@
 //    (the memory has to turn the bus around for each of them).
 //  * A row block cut by a wave-range boundary is shared by 2+ waves: each
 //    adds its partial sums into 64-bit scratch slots that also count the
-//    arrivals (one device-scope atomic with return per row and token); the
-//    lane that completes the count holds the total, writes the output and
-//    clears the slot for the next launch.
+//    block's chunks seen so far (one device-scope atomic with return per row
+//    and token); the lane that completes the count holds the total, writes
+//    the output and clears the slot for the next launch.
 #include "bt_internal.h"
 
 namespace bt {
@@ -94,11 +94,6 @@ __device__ __forceinline__ int find_problem(const int64_t* chunk0, int count,
   return __builtin_amdgcn_readfirstlane(p - 1);
 }
 
-// Owner wave of global chunk x when T chunks are split over W waves.
-__device__ __forceinline__ int64_t owner(int64_t x, int64_t W, int64_t T) {
-  return ((x + 1) * W - 1) / T;
-}
-
 template <int TOK>
 struct Acc {
   int f[4][TOK];  // per 2-bit field j: sum of (4^j * code) * q
@@ -147,9 +142,8 @@ struct Stream {
   int n, k, kc, blk0;
   int64_t chunk0;
   // wave range (global chunks) and grid
-  int64_t lo, hi, W, T;
+  int64_t lo, hi;
   int32_t* sacc;
-  int32_t* scnt;
   int qsum[TOK];
   float sav[TOK];    // the tokens' activation scales (read once per problem)
   // LDS staging of finished row blocks: kOut blocks of TOK rows of 64 sums;
@@ -271,16 +265,18 @@ struct Stream {
 
   // This wave holds only part of row block rb (partial sums in sum[]).  Each
   // (row, token) of the block has a 64-bit scratch slot holding
-  // (arrivals << 32) + partial total: one atomic add with return of
-  // (1 << 32) + partial adds this wave's share and counts it.  The lane that
-  // sees the arrival count reach the number of contributors holds the total
-  // (the partial totals stay below 2^31 in magnitude, so the two fields
-  // decode exactly); it writes the output and clears the slot for the next
-  // launch.  Integer addition is exact and order-free; no lane waits for
-  // another.  A wave has at most two such blocks (the first and the last of
-  // its range); the atomics of both are issued, without a branch (a block
-  // that is not cut adds 0 to its own slot, which changes nothing), before
-  // settle looks at what either returned, so the round trips overlap.
+  // (chunks << 32) + partial total: one atomic add with return of
+  // (c << 32) + partial adds this wave's share, c chunks of the block's kc.
+  // The lane that sees the chunk count reach kc holds the total (the partial
+  // totals stay below 2^31 in magnitude, so the two fields decode exactly);
+  // it writes the output and clears the slot for the next launch.  Counting
+  // chunks rather than contributors makes the hand-off independent of how
+  // the stream was cut.  Integer addition is exact and order-free; no lane
+  // waits for another.  A wave has at most two such blocks per problem (the
+  // first and the last of its range); the atomics of both are issued,
+  // without a branch (a block that is not cut adds 0 to its own slot, which
+  // changes nothing), before settle looks at what either returned, so the
+  // round trips overlap.
   struct HandOff {
     uint64_t ret[TOK];  // what the atomics returned (slot before the add)
     int64_t delta[TOK];
@@ -293,28 +289,25 @@ struct Stream {
   }
 
   __device__ __forceinline__ void hand_off(HandOff& h, int rb,
-                                           const int (&sum)[TOK],
+                                           const int (&sum)[TOK], int chunks,
                                            bool on) const {
     unsigned long long* sp = slot_of(rb);
 #pragma unroll
     for (int t = 0; t < TOK; ++t) {
-      h.delta[t] = on ? ((int64_t)1 << 32) + (int64_t)sum[t] : 0;
+      h.delta[t] = on ? ((int64_t)chunks << 32) + (int64_t)sum[t] : 0;
       h.ret[t] = atomicAdd(sp + t * 64, (unsigned long long)h.delta[t]);
     }
     h.rb = rb;
   }
 
   __device__ __forceinline__ void settle(const HandOff& h) {
-    const int64_t first = chunk0 + (int64_t)h.rb * kc;
-    const int64_t last = first + kc - 1;
-    const int64_t contributors = owner(last, W, T) - owner(first, W, T) + 1;
     unsigned long long* sp = slot_of(h.rb);
 #pragma unroll
     for (int t = 0; t < TOK; ++t) {
       const int64_t now = (int64_t)h.ret[t] + h.delta[t];
-      const int64_t arrivals = (now + ((int64_t)1 << 31)) >> 32;
-      if (arrivals == contributors) {
-        write_one(h.rb, t, (int)(now - (contributors << 32)));
+      const int64_t chunks = (now + ((int64_t)1 << 31)) >> 32;
+      if (chunks == kc) {
+        write_one(h.rb, t, (int)(now - ((int64_t)kc << 32)));
         atomicExch(sp + t * 64, 0ull);  // at the coherence point too
       }
     }
@@ -438,8 +431,9 @@ struct Stream {
 #pragma unroll
     for (int t = 0; t < TOK; ++t) tail_sum[t] = a.total(t);
     HandOff hh, ht;
-    hand_off(hh, head_rb, head_sum, head_off);
-    hand_off(ht, (s1 - 1) / kc, tail_sum, tail_off);
+    const int tail_rb = (s1 - 1) / kc;
+    hand_off(hh, head_rb, head_sum, (head_rb + 1) * kc - s0, head_off);
+    hand_off(ht, tail_rb, tail_sum, s1 - max(tail_rb * kc, s0), tail_off);
     if (head_off) settle(hh);
     if (tail_off) settle(ht);
   }
@@ -470,30 +464,19 @@ struct Stream {
   }
 };
 
+// Chunks [lo, hi) of the concatenated stream, problem by problem.
 template <int TOK>
-__global__ __launch_bounds__(256) void stream_kernel(
-    const Desc* __restrict__ descs, const int64_t* __restrict__ chunk0s,
-    int count, int64_t total, int32_t* sacc, int32_t* scnt) {
-  // With fewer chunks than waves, only the first `total` waves take part, so
-  // every participating wave owns at least one chunk (the arrival count of a
-  // shared row block counts exactly the waves that hold part of it).
-  const int64_t W = min((int64_t)gridDim.x * 4, total);
-  const int64_t wv =
-      (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  if (wv >= W) return;
-  Stream<TOK> st;
-  __shared__ int obuf_all[4][16 * 64];
-  st.obuf = obuf_all[threadIdx.x >> 6];
-  st.lo = wv * total / W;
-  st.hi = (wv + 1) * total / W;
-  st.W = W;
-  st.T = total;
-  st.sacc = sacc;
-  st.scnt = scnt;
-  if (st.lo >= st.hi) return;
-  int p = find_problem(chunk0s, count, st.lo);
-  int64_t pos = st.lo;
-  while (pos < st.hi && p < count) {
+__device__ __forceinline__ void stream_range(Stream<TOK>& st,
+                                             const Desc* __restrict__ descs,
+                                             const int64_t* __restrict__ chunk0s,
+                                             int count, int64_t lo,
+                                             int64_t hi) {
+  if (lo >= hi) return;
+  st.lo = lo;
+  st.hi = hi;
+  int p = find_problem(chunk0s, count, lo);
+  int64_t pos = lo;
+  while (pos < hi && p < count) {
     const Desc& d = descs[p];
     st.w = d.w;
     st.xq = d.xq;
@@ -508,25 +491,46 @@ __global__ __launch_bounds__(256) void stream_kernel(
     st.chunk0 = d.chunk0;
     const int64_t chunks = (int64_t)d.nblk * d.kc;
     const int64_t s0 = pos - d.chunk0;
-    const int64_t s1 = min(chunks, st.hi - d.chunk0);
+    const int64_t s1 = min(chunks, hi - d.chunk0);
     st.segment((int)s0, (int)s1);
     pos = d.chunk0 + s1;
     ++p;
   }
 }
 
+// Wave wv of W streams chunks [wv T / W, (wv + 1) T / W) of the T chunks.
+// (Handing out part of the stream dynamically from a shared counter was
+// measured too: the counter's contention and the per-piece start-up cost
+// more than the uneven finish of equal ranges.)
+template <int TOK>
+__global__ __launch_bounds__(256) void stream_kernel(
+    const Desc* __restrict__ descs, const int64_t* __restrict__ chunk0s,
+    int count, int64_t total, int32_t* sacc) {
+  // With fewer chunks than waves, only the first `total` waves take part.
+  const int64_t W = min((int64_t)gridDim.x * 4, total);
+  const int64_t wv =
+      (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (wv >= W) return;
+  Stream<TOK> st;
+  __shared__ int obuf_all[4][16 * 64];
+  st.obuf = obuf_all[threadIdx.x >> 6];
+  st.sacc = sacc;
+  stream_range(st, descs, chunk0s, count, wv * total / W,
+               (wv + 1) * total / W);
+}
+
 }  // namespace
 
 hipError_t launch_stream_grouped(const Desc* descs, const int64_t* chunk0,
                                  int32_t count, int64_t total_chunks, int m,
-                                 int32_t* sacc, int32_t* scnt, int workgroups,
+                                 int32_t* sacc, int workgroups,
                                  hipStream_t s) {
   const dim3 grid((unsigned)workgroups), block(256);
   switch (m) {
-    case 1: stream_kernel<1><<<grid, block, 0, s>>>(descs, chunk0, count, total_chunks, sacc, scnt); break;
-    case 2: stream_kernel<2><<<grid, block, 0, s>>>(descs, chunk0, count, total_chunks, sacc, scnt); break;
-    case 3: stream_kernel<3><<<grid, block, 0, s>>>(descs, chunk0, count, total_chunks, sacc, scnt); break;
-    case 4: stream_kernel<4><<<grid, block, 0, s>>>(descs, chunk0, count, total_chunks, sacc, scnt); break;
+    case 1: stream_kernel<1><<<grid, block, 0, s>>>(descs, chunk0, count, total_chunks, sacc); break;
+    case 2: stream_kernel<2><<<grid, block, 0, s>>>(descs, chunk0, count, total_chunks, sacc); break;
+    case 3: stream_kernel<3><<<grid, block, 0, s>>>(descs, chunk0, count, total_chunks, sacc); break;
+    case 4: stream_kernel<4><<<grid, block, 0, s>>>(descs, chunk0, count, total_chunks, sacc); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

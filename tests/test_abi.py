@@ -204,8 +204,8 @@ def test_grouped_plan_layout_stream(L):
     for off in ("desc_off", "chunk_off", "unit_off", "sacc_off", "scnt_off",
                 "bytes"):
         assert p[off] % 256 == 0
-    # scratch: one 64-bit slot (arrival count, partial total) per row of
-    # every row block and token
+    # scratch: one 64-bit slot (chunk count, partial total) per row of every
+    # row block and token
     assert p["scnt_off"] - p["sacc_off"] >= sum(nblk) * 64 * 8
     assert p["bytes"] >= p["scnt_off"]
     assert not img[p["sacc_off"]:].any()

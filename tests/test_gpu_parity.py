@@ -278,14 +278,59 @@ def test_grouped_layers_match_oracle(m, layers):
     work = wl.decode_2b(m=m, layers=layers)
     probs, host = grouped_case(work, layers)
     plan = bt.bt_grouped_plan(probs)
-    for _ in range(2):  # the plan is reusable
+    refs = [oracle_product(t, x, s_w) for t, x, s_w in host]
+    for _ in range(2):  # the plan is reusable; each launch writes everything
+        for p in probs:
+            p["y"].fill_(float("nan"))
+            p["acc"].fill_(0x7EADBEEF)
         bt.bt_gemm_grouped(plan)
-    torch.cuda.synchronize()
-    for prob, (t, x, s_w) in zip(probs, host):
-        _, q_r, s_r, acc_r, y_r = oracle_product(t, x, s_w)
-        np.testing.assert_array_equal(prob["x_q"].cpu().numpy(), q_r)
-        np.testing.assert_array_equal(prob["acc"].cpu().numpy(), acc_r)
-        check_y(prob["y"].cpu().numpy(), y_r, acc_r)
+        torch.cuda.synchronize()
+        for prob, (_, q_r, s_r, acc_r, y_r) in zip(probs, refs):
+            np.testing.assert_array_equal(prob["x_q"].cpu().numpy(), q_r)
+            np.testing.assert_array_equal(prob["acc"].cpu().numpy(), acc_r)
+            check_y(prob["y"].cpu().numpy(), y_r, acc_r)
+
+
+@pytest.mark.parametrize("m", [1, 4])
+def test_decode_set_grouped_full_size(m):
+    """The whole 2B-shaped decode set (30 layers x 7 projections, 521 MB of
+    packed weights) in one grouped launch, as the benchmark runs it, three
+    times in a row; every output of every launch against the oracle.  To
+    keep the host side short, the 30 layers share layer 0's seven weight
+    tensors (the launch still streams 521 MB); every (layer, projection) has
+    its own activations."""
+    work = wl.decode_2b(m=m)
+    shared = {}
+    for p in work.problems():
+        if p.layer == 0:
+            t, s_w = work.weights(0, p.proj)
+            shared[p.proj] = (t, s_w, bt.bt_pack_i2s(dev(t)),
+                              oracle.pack_i2s(t)[0])
+    probs, refs = [], []
+    for p in work.problems():
+        t, s_w, packed, packed_ref = shared[p.proj]
+        x = work.activations(p.layer, p.proj)
+        x_q, s_a = bt.bt_quant_act(dev(x))
+        probs.append(dict(packed=packed, s_w=s_w, n=p.n, k=p.k, x_q=x_q,
+                          s_a=s_a,
+                          y=torch.empty((m, p.n), device="cuda:0"),
+                          acc=torch.empty((m, p.n), dtype=torch.int32,
+                                          device="cuda:0")))
+        q_r, sa_r = oracle.quant_act(x)
+        acc_r, y_r = oracle.gemm(packed_ref, s_w, p.n, p.k, q_r, sa_r,
+                                 nthreads=NTHREADS)
+        refs.append((acc_r, y_r))
+    plan = bt.bt_grouped_plan(probs)
+    for launch in range(3):
+        for p in probs:
+            p["y"].fill_(float("nan"))
+            p["acc"].fill_(0x7EADBEEF)
+        bt.bt_gemm_grouped(plan)
+        torch.cuda.synchronize()
+        for i, (prob, (acc_r, y_r)) in enumerate(zip(probs, refs)):
+            acc = prob["acc"].cpu().numpy()
+            assert np.array_equal(acc, acc_r), f"launch {launch} problem {i}"
+            check_y(prob["y"].cpu().numpy(), y_r, acc_r)
 
 
 @pytest.mark.parametrize("m", [1, 2, 3, 4, 8])
