@@ -150,15 +150,17 @@ __device__ __forceinline__ int* tsum_array() {
 constexpr int kEpRow = 272;  // bytes per token in the staging region
 
 // 16 bytes per lane of one staged token row: rows 4 (lane % 16) .. + 3 of the
-// wave's block, token `tok`.
+// wave's block, token `tok`.  Outputs are written once and not read back by
+// the launch: non-temporal stores (measured 2 us faster on the M=512 layer).
 template <typename T>
 __device__ __forceinline__ void store_row16(T* out, int n, int tok, int row,
                                             const int8_t* src) {
   T* dst = out + (size_t)tok * n + row;
   if ((n & 3) == 0 && row + 3 < n) {
-    *reinterpret_cast<__attribute__((address_space(1))) v4i*>(
-        (__attribute__((address_space(1))) T*)dst) =
-        *reinterpret_cast<const v4i*>(src);
+    __builtin_nontemporal_store(
+        *reinterpret_cast<const v4i*>(src),
+        reinterpret_cast<__attribute__((address_space(1))) v4i*>(
+            (__attribute__((address_space(1))) T*)dst));
   } else {
 #pragma unroll
     for (int r = 0; r < 4; ++r)
