@@ -100,16 +100,33 @@ class WorkSet:
                     f"({time.time() - t0:.1f} s)")
         torch.cuda.synchronize()
         self.plan = bt.bt_grouped_plan(self.problems)
+        if mode == "fused":
+            # the same products, quantizing the fp32 rows in the launch
+            fprobs = []
+            off = {k: 0 for k in ks}
+            for p in self.problems:
+                o = off[p["k"]]
+                off[p["k"]] += m
+                fprobs.append(dict(packed=p["packed"], s_w=p["s_w"], n=p["n"],
+                                   k=p["k"], x=self.x[p["k"]][o:o + m],
+                                   y=p["y"]))
+            self.fplan = bt.bt_grouped_plan_f32(fprobs)
         self.ks = ks
 
     # algorithmic bytes and ops -------------------------------------------
     def product_bytes(self):
-        """Packed weights + int8 activations + scales + fp32 outputs."""
+        """Packed weights + int8 activations + scales + fp32 outputs (fused:
+        packed weights + fp32 activations + fp32 outputs)."""
         m = self.m
+        if self.mode == "fused":
+            return sum(self.bt.bt_packed_bytes(p["n"], p["k"]) + 4 * m * p["k"]
+                       + 4 * m * p["n"] for p in self.problems)
         return sum(self.bt.bt_packed_bytes(p["n"], p["k"]) + m * p["k"] + 4 * m
                    + 4 * m * p["n"] for p in self.problems)
 
     def quant_bytes(self):
+        if self.mode == "fused":
+            return 0
         m = self.m
         return sum(5 * m * p["k"] + 4 * m for p in self.problems)
 
@@ -122,12 +139,16 @@ class WorkSet:
 
     # the step ------------------------------------------------------------
     def quant(self):
+        if self.mode == "fused":
+            return  # the product launch quantizes
         self.bt.bt_quant_act_many([self.x[k] for k in self.ks],
                                   [self.xq[k] for k in self.ks],
                                   [self.sa[k] for k in self.ks])
 
     def product(self):
-        if self.mode == "grouped":
+        if self.mode == "fused":
+            self.bt.bt_gemm_grouped(self.fplan)
+        elif self.mode == "grouped":
             self.bt.bt_gemm_grouped(self.plan)
         else:
             for p in self.problems:
@@ -220,7 +241,7 @@ def main():
     ap.add_argument("--workload", default="decode_2b_m1",
                     choices=sorted(WORKLOADS))
     ap.add_argument("--mode", default="grouped",
-                    choices=["grouped", "per-launch"])
+                    choices=["grouped", "per-launch", "fused"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the M=512 prefill figure")

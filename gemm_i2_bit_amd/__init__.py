@@ -4,7 +4,8 @@ library's HIP kernels.  PyTorch supplies device memory and streams.
 
 Functions carry the C ABI's names (see include/bt.h for the contract):
 bt_pack_i2s, bt_quant_act, bt_quant_act_many, bt_gemv, bt_gemm,
-bt_grouped_plan, bt_gemm_grouped, bt_packed_bytes, bt_status_str.
+bt_grouped_plan, bt_grouped_plan_f32, bt_gemm_grouped, bt_packed_bytes,
+bt_status_str.
 """
 from __future__ import annotations
 
@@ -21,6 +22,7 @@ BT_OK, BT_E_NULL, BT_E_SHAPE, BT_E_ALIGN, BT_E_ARG, BT_E_HIP, BT_E_ARCH = (
 
 BT_MAX_M = 1 << 24
 BT_MAX_QUANT_JOBS = 16
+BT_FUSED_MAX_MK = 16384
 
 _lib = None
 
@@ -37,6 +39,13 @@ class bt_problem(ctypes.Structure):
                 ("acc", ctypes.c_void_p), ("s_w", ctypes.c_float),
                 ("n", ctypes.c_int32), ("k", ctypes.c_int32),
                 ("m", ctypes.c_int32)]
+
+
+class bt_problem_f32(ctypes.Structure):
+    _fields_ = [("packed", ctypes.c_void_p), ("x", ctypes.c_void_p),
+                ("y", ctypes.c_void_p), ("acc", ctypes.c_void_p),
+                ("s_w", ctypes.c_float), ("n", ctypes.c_int32),
+                ("k", ctypes.c_int32), ("m", ctypes.c_int32)]
 
 
 class bt_quant_job(ctypes.Structure):
@@ -74,6 +83,10 @@ def lib() -> ctypes.CDLL:
         L.bt_grouped_plan_bytes.restype = i64
         L.bt_grouped_plan.argtypes = [p, i32, p, i64]
         L.bt_grouped_plan.restype = i32
+        L.bt_grouped_plan_f32_bytes.argtypes = [p, i32]
+        L.bt_grouped_plan_f32_bytes.restype = i64
+        L.bt_grouped_plan_f32.argtypes = [p, i32, p, i64]
+        L.bt_grouped_plan_f32.restype = i32
         L.bt_gemm_grouped.argtypes = [p, p, p]
         L.bt_gemm_grouped.restype = i32
         _lib = L
@@ -270,6 +283,39 @@ def bt_grouped_plan(problems, device=None) -> GroupedPlan:
                                  nbytes), "bt_grouped_plan")
     if device is None:
         device = problems[0]["x_q"].device
+    dev = torch.from_numpy(host).to(device)
+    return GroupedPlan(host, dev, keep)
+
+
+def bt_grouped_plan_f32(problems, device=None) -> GroupedPlan:
+    """problems: list of dicts with packed, s_w, n, k, x (fp32 activations
+    [m, k]), y and optionally acc (GPU tensors; one m <= 4 for all).  The
+    launch quantizes x itself, as bt_quant_act would."""
+    torch = _torch()
+    arr = (bt_problem_f32 * len(problems))()
+    keep = []
+    for i, p in enumerate(problems):
+        x = p["x"]
+        m = x.shape[0] if x.dim() == 2 else 1
+        if (x.numel() != m * p["k"] or p["y"].numel() != m * p["n"]
+                or p["packed"].numel() != bt_packed_bytes(p["n"], p["k"])
+                or (p.get("acc") is not None
+                    and p["acc"].numel() != m * p["n"])):
+            raise ValueError(f"problem {i} has inconsistent sizes")
+        arr[i] = bt_problem_f32(_dev(p["packed"], torch.uint8, "packed"),
+                                _dev(x, torch.float32, "x"),
+                                _dev(p["y"], torch.float32, "y"),
+                                _dev(p.get("acc"), torch.int32, "acc"),
+                                float(p["s_w"]), p["n"], p["k"], m)
+        keep.append(p)
+    nbytes = lib().bt_grouped_plan_f32_bytes(arr, len(problems))
+    if nbytes < 0:
+        raise BtError(nbytes, "bt_grouped_plan_f32_bytes")
+    host = np.zeros(nbytes, np.uint8)
+    _check(lib().bt_grouped_plan_f32(arr, len(problems), host.ctypes.data,
+                                     nbytes), "bt_grouped_plan_f32")
+    if device is None:
+        device = problems[0]["x"].device
     dev = torch.from_numpy(host).to(device)
     return GroupedPlan(host, dev, keep)
 

@@ -307,8 +307,10 @@ int64_t bt_grouped_plan_bytes(const bt_problem* probs, int32_t count) {
   return plan_layout(probs, count).bytes;
 }
 
-int32_t bt_grouped_plan(const bt_problem* probs, int32_t count, void* plan,
-                        int64_t plan_bytes) {
+// Builds a grouped plan image; with xf, the problems give fp32 activations
+// (xf[i]) that the launch quantizes itself.
+static int32_t build_plan(const bt_problem* probs, int32_t count, void* plan,
+                          int64_t plan_bytes, const float* const* xf) {
   if (!plan) return BT_E_NULL;
   const int32_t st = check_group(probs, count);
   if (st != BT_OK) return st;
@@ -316,7 +318,9 @@ int32_t bt_grouped_plan(const bt_problem* probs, int32_t count, void* plan,
   if (plan_bytes < h.bytes) return BT_E_ARG;
   unsigned char* out = static_cast<unsigned char*>(plan);
   memset(out, 0, (size_t)h.bytes);  // scratch area starts at zero
-  memcpy(out, &h, sizeof(h));
+  PlanHeader hf = h;
+  hf.fused = xf ? 1 : 0;
+  memcpy(out, &hf, sizeof(hf));
   const std::vector<Split> split = plan_splits(probs, count, h.kind);
   int64_t chunk0 = 0;
   int64_t blk0 = 0;
@@ -327,6 +331,11 @@ int32_t bt_grouped_plan(const bt_problem* probs, int32_t count, void* plan,
                        p.acc);
     d.chunk0 = chunk0;
     d.blk0 = (int32_t)blk0;
+    if (xf) {  // fused quantization: fp32 activations only
+      d.xf = xf[i];
+      d.xq = nullptr;
+      d.sa = nullptr;
+    }
     if (h.kind != bt::kKindDot4) {
       d.nsplit = split[i].nsplit;
       d.split_len = split[i].len;
@@ -349,6 +358,47 @@ int32_t bt_grouped_plan(const bt_problem* probs, int32_t count, void* plan,
   return BT_OK;
 }
 
+int32_t bt_grouped_plan(const bt_problem* probs, int32_t count, void* plan,
+                        int64_t plan_bytes) {
+  return build_plan(probs, count, plan, plan_bytes, nullptr);
+}
+
+// The fp32-activation problems as bt_problem (x in the x_q and s_a slots,
+// so that the shared checks see non-null, aligned pointers), after checks
+// of their own: m <= 4 and m * k <= BT_FUSED_MAX_MK.
+static int32_t as_problems(const bt_problem_f32* probs, int32_t count,
+                           std::vector<bt_problem>& out) {
+  if (!probs) return BT_E_NULL;
+  if (count < 1 || count > (1 << 20)) return BT_E_ARG;
+  out.resize(count);
+  for (int32_t i = 0; i < count; ++i) {
+    const bt_problem_f32& p = probs[i];
+    if (!p.x) return BT_E_NULL;
+    if (p.m < 1 || p.m > 4 || (int64_t)p.m * p.k > BT_FUSED_MAX_MK)
+      return BT_E_SHAPE;
+    out[i] = bt_problem{p.packed, reinterpret_cast<const int8_t*>(p.x), p.x,
+                        p.y, p.acc, p.s_w, p.n, p.k, p.m};
+  }
+  return BT_OK;
+}
+
+int64_t bt_grouped_plan_f32_bytes(const bt_problem_f32* probs, int32_t count) {
+  std::vector<bt_problem> q;
+  const int32_t st = as_problems(probs, count, q);
+  if (st != BT_OK) return st;
+  return bt_grouped_plan_bytes(q.data(), count);
+}
+
+int32_t bt_grouped_plan_f32(const bt_problem_f32* probs, int32_t count,
+                            void* plan, int64_t plan_bytes) {
+  std::vector<bt_problem> q;
+  const int32_t st = as_problems(probs, count, q);
+  if (st != BT_OK) return st;
+  std::vector<const float*> xf(count);
+  for (int32_t i = 0; i < count; ++i) xf[i] = probs[i].x;
+  return build_plan(q.data(), count, plan, plan_bytes, xf.data());
+}
+
 int32_t bt_gemm_grouped(const void* plan_dev, const void* plan_host,
                         void* stream) {
   if (!plan_dev || !plan_host) return BT_E_NULL;
@@ -362,7 +412,8 @@ int32_t bt_gemm_grouped(const void* plan_dev, const void* plan_host,
       h.bytes < h.scnt_off || h.scnt_off < h.sacc_off ||
       h.sacc_off < h.unit_off || h.unit_off < h.chunk_off ||
       h.chunk_off < h.desc_off + (int64_t)h.count * (int64_t)sizeof(Desc) ||
-      (h.kind != bt::kKindDot4 && h.units < 1))
+      (h.kind != bt::kKindDot4 && h.units < 1) || h.fused < 0 ||
+      h.fused > 1 || (h.fused == 1 && h.kind != bt::kKindDot4))
     return BT_E_ARG;
   const int32_t arch = check_arch();
   if (arch != BT_OK) return arch;
@@ -385,7 +436,7 @@ int32_t bt_gemm_grouped(const void* plan_dev, const void* plan_host,
   return hip_status(bt::launch_stream_grouped(
       descs, reinterpret_cast<const int64_t*>(base + h.chunk_off), h.count,
       h.total_chunks, h.m, reinterpret_cast<int32_t*>(mut + h.sacc_off),
-      (int)wgs, s));
+      (int)wgs, h.fused == 1, s));
 }
 
 }  // extern "C"

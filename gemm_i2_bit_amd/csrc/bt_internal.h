@@ -35,8 +35,10 @@ struct alignas(16) Desc {
   int32_t split_len;
   int32_t slot0;
   int32_t region0;
+  // fused-quantization plans: fp32 activations [m, k] (xq and sa are null)
+  const float* xf;
 };
-static_assert(sizeof(Desc) == 96, "Desc is 96 bytes");
+static_assert(sizeof(Desc) == 112, "Desc is 112 bytes");
 
 // One work unit of a grouped launch: problem index and a sub-index whose
 // meaning depends on the kernel: for the matrix-core kinds,
@@ -69,7 +71,8 @@ struct PlanHeader {
   int64_t bytes;       // total image size
   int64_t total_chunks;
   int64_t blocks;      // row blocks over all problems
-  int64_t pad[5];
+  int64_t fused;       // 1: the problems give fp32 activations (Desc::xf)
+  int64_t pad[4];
 };
 static_assert(sizeof(PlanHeader) == 128, "PlanHeader is 128 bytes");
 
@@ -112,8 +115,34 @@ hipError_t launch_quant_many(const bt_quant_job* jobs, int32_t count,
 hipError_t launch_dot4(const Desc& d, hipStream_t s);
 hipError_t launch_stream_grouped(const Desc* descs, const int64_t* chunk0,
                                  int32_t count, int64_t total_chunks, int m,
-                                 int32_t* sacc, int workgroups,
+                                 int32_t* sacc, int workgroups, bool fused,
                                  hipStream_t s);
+
+// A token row's scales from its absmax: a = max(amax, 1e-5), one correctly
+// rounded 127 / a for the products and s_a = a / 127 for the rescale.
+struct QScale {
+  float inv, sa;
+};
+__device__ __forceinline__ QScale quant_scale(float amax) {
+  const float a = fmaxf(amax, 1e-5f);
+  return QScale{__fdiv_rn(127.0f, a), __fdiv_rn(a, 127.0f)};
+}
+
+// Quantizes four activations with a row's 127 / a (fp32 product, round half
+// to even, clamp +-127) and packs them as 4 int8 in a little-endian word.
+// Shared by the quantization kernel and the fused streaming kernel so that
+// both produce the same bytes.
+__device__ __forceinline__ uint32_t quant4(const float4& v, float inv) {
+  const float e[4] = {v.x, v.y, v.z, v.w};
+  uint32_t packed4 = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    float r = rintf(__fmul_rn(e[j], inv));  // round half to even
+    r = fminf(fmaxf(r, -127.0f), 127.0f);
+    packed4 |= ((uint32_t)(int32_t)r & 0xffu) << (8 * j);
+  }
+  return packed4;
+}
 hipError_t launch_tiled(const Desc& d, hipStream_t s);
 hipError_t launch_tiled_grouped(const Desc* descs, const Unit* units,
                                 int64_t count, int m, int32_t* sacc,

@@ -47,6 +47,11 @@ typedef __attribute__((address_space(1))) float* gfloat_ptr;
 typedef __attribute__((address_space(1))) int32_t* gint_ptr;
 typedef const __attribute__((address_space(1))) int* gcint_ptr;
 typedef const __attribute__((address_space(1))) float* gcfloat_ptr;
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef const __attribute__((address_space(1))) v4f* gcfloat4_ptr;
+typedef __attribute__((address_space(3))) int8_t* lds_i8_ptr;
+typedef __attribute__((address_space(3))) uint32_t* lds_u32_ptr;
+typedef const __attribute__((address_space(3))) v4u* lds_cv4u_ptr;
 
 constexpr int kRsrcFlags = 0x00020000;  // raw buffer, 32-bit words
 
@@ -129,11 +134,16 @@ struct Group {
   }
 };
 
-template <int TOK>
+// FUSED: the problem gives fp32 activations; each wave quantizes the rows it
+// needs into LDS (exactly as the quantization kernel does) and reads the
+// int8 values from there instead of through scalar loads.
+template <int TOK, bool FUSED>
 struct Stream {
   // problem
   const uint8_t* w;  // the problem's packed weights
   const int8_t* xq;
+  gcfloat_ptr xf;    // FUSED: fp32 activations [TOK, k]
+  lds_i8_ptr xl;     // FUSED: this wave's LDS copy of the quantized rows
   const_fptr sa;     // scalar loads: a vector load would wait behind the
                      // weight loads in flight
   gfloat_ptr y;
@@ -187,6 +197,22 @@ struct Stream {
     int v[TOK][16];
   };
   __device__ __forceinline__ void load_q(QChunk& qc, int c, int pin) const {
+    if constexpr (FUSED) {
+      // every lane reads the same 16 bytes: LDS broadcasts them
+#pragma unroll
+      for (int t = 0; t < TOK; ++t) {
+        const lds_cv4u_ptr q = (lds_cv4u_ptr)(xl + t * k + c * 64 + pin);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const v4u v = q[i];
+          qc.v[t][4 * i + 0] = (int)v.x;
+          qc.v[t][4 * i + 1] = (int)v.y;
+          qc.v[t][4 * i + 2] = (int)v.z;
+          qc.v[t][4 * i + 3] = (int)v.w;
+        }
+      }
+      return;
+    }
 #pragma unroll
     for (int t = 0; t < TOK; ++t) {
       const_iptr q = (const_iptr)(xq + (size_t)t * k + (size_t)c * 64 + pin);
@@ -368,6 +394,78 @@ struct Stream {
     }
   }
 
+  // FUSED: quantize the problem's TOK activation rows into this wave's LDS
+  // area with the quantization kernel's arithmetic (quant_scale, quant4),
+  // taking each row's activation sum and scale on the way.  The row is read
+  // in batches of kBatch float4 per lane whose loads are all issued before
+  // any is used (one round trip per batch); a row of at most one batch
+  // stays in registers between the absmax and the quantization, longer rows
+  // are read a second time (from cache).
+  static constexpr int kBatch = 16;
+  __device__ __forceinline__ void load_batch(float4 (&v)[kBatch],
+                                             gcfloat4_ptr xr, int b0,
+                                             int n4) const {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {  // clamped: repeats change no maximum
+      const v4f f = xr[min(b0 + u * 64 + lane, n4 - 1)];
+      v[u] = make_float4(f.x, f.y, f.z, f.w);
+    }
+  }
+  __device__ __forceinline__ static float absmax4(const float4& v) {
+    return fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+  }
+  __device__ __forceinline__ void quant_batch(const float4 (&v)[kBatch],
+                                              lds_u32_ptr dst, int b0, int n4,
+                                              float inv, int& s) const {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int i = b0 + u * 64 + lane;
+      if (i < n4) {
+        const uint32_t q = quant4(v[u], inv);
+        dst[i] = q;
+        s = sdot4((int)q, 0x01010101, s);
+      }
+    }
+  }
+  __device__ __forceinline__ void quantize_rows() {
+    const int n4 = k >> 2;
+#pragma unroll
+    for (int t = 0; t < TOK; ++t) {
+      const gcfloat4_ptr xr = (gcfloat4_ptr)(xf + (size_t)t * k);
+      const lds_u32_ptr dst = (lds_u32_ptr)(xl + t * k);
+      float4 v[kBatch];
+      float amax = 0.0f;
+      load_batch(v, xr, 0, n4);
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) amax = fmaxf(amax, absmax4(v[u]));
+      for (int b0 = 64 * kBatch; b0 < n4; b0 += 64 * kBatch) {
+        float4 w[kBatch];
+        load_batch(w, xr, b0, n4);
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) amax = fmaxf(amax, absmax4(w[u]));
+      }
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1)
+        amax = fmaxf(amax, __shfl_xor(amax, off, 64));
+      const QScale qs = quant_scale(amax);
+      int s = 0;
+      quant_batch(v, dst, 0, n4, qs.inv, s);  // the first batch is still here
+      for (int b0 = 64 * kBatch; b0 < n4; b0 += 64 * kBatch) {
+        float4 w[kBatch];
+        load_batch(w, xr, b0, n4);
+        quant_batch(w, dst, b0, n4, qs.inv, s);
+      }
+      qsum[t] = wave_sum(s);
+      sav[t] = qs.sa;
+    }
+    // the rows are read back by other lanes of this wave only: LDS keeps a
+    // wave's operations in order; the clobber keeps the compiler from
+    // moving the reads above the writes
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  }
+
   // Stream chunks [s0, s1) of the current problem (problem-local indices) in
   // groups of up to D chunks, double buffered: while group i is consumed,
   // group i + 1 is in flight.  Every load is unconditional (range-checked),
@@ -395,15 +493,19 @@ struct Stream {
     ocnt = 0;
     orb0 = head_rb + (head_cut ? 1 : 0);  // the first block finished whole
     v4u A[D], B[D];
-    {
+    if constexpr (FUSED) {
+      load_group(A, g);
+      load_group(B, pg);
+      quantize_rows();
+    } else {
       ActPre pre;
       issue_act(pre);
       load_group(A, g);
       load_group(B, pg);
       finish_act(pre);
-    }
 #pragma unroll
-    for (int t = 0; t < TOK; ++t) sav[t] = sa[t];
+      for (int t = 0; t < TOK; ++t) sav[t] = sa[t];
+    }
     while (true) {
       g.uniform();
       pg.uniform();
@@ -465,8 +567,8 @@ struct Stream {
 };
 
 // Chunks [lo, hi) of the concatenated stream, problem by problem.
-template <int TOK>
-__device__ __forceinline__ void stream_range(Stream<TOK>& st,
+template <int TOK, bool FUSED>
+__device__ __forceinline__ void stream_range(Stream<TOK, FUSED>& st,
                                              const Desc* __restrict__ descs,
                                              const int64_t* __restrict__ chunk0s,
                                              int count, int64_t lo,
@@ -480,6 +582,7 @@ __device__ __forceinline__ void stream_range(Stream<TOK>& st,
     const Desc& d = descs[p];
     st.w = d.w;
     st.xq = d.xq;
+    st.xf = (gcfloat_ptr)d.xf;
     st.sa = (const_fptr)d.sa;
     st.y = (gfloat_ptr)d.y;
     st.accout = (gint_ptr)d.acc;
@@ -502,7 +605,7 @@ __device__ __forceinline__ void stream_range(Stream<TOK>& st,
 // (Handing out part of the stream dynamically from a shared counter was
 // measured too: the counter's contention and the per-piece start-up cost
 // more than the uneven finish of equal ranges.)
-template <int TOK>
+template <int TOK, bool FUSED>
 __global__ __launch_bounds__(256) void stream_kernel(
     const Desc* __restrict__ descs, const int64_t* __restrict__ chunk0s,
     int count, int64_t total, int32_t* sacc) {
@@ -511,9 +614,12 @@ __global__ __launch_bounds__(256) void stream_kernel(
   const int64_t wv =
       (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (wv >= W) return;
-  Stream<TOK> st;
+  Stream<TOK, FUSED> st;
   __shared__ int obuf_all[4][16 * 64];
   st.obuf = obuf_all[threadIdx.x >> 6];
+  // FUSED: each wave's quantized activation rows (m * k <= BT_FUSED_MAX_MK)
+  __shared__ v4u xl_all[4][FUSED ? BT_FUSED_MAX_MK / 16 : 1];
+  st.xl = (lds_i8_ptr)xl_all[threadIdx.x >> 6];
   st.sacc = sacc;
   stream_range(st, descs, chunk0s, count, wv * total / W,
                (wv + 1) * total / W);
@@ -521,19 +627,29 @@ __global__ __launch_bounds__(256) void stream_kernel(
 
 }  // namespace
 
-hipError_t launch_stream_grouped(const Desc* descs, const int64_t* chunk0,
-                                 int32_t count, int64_t total_chunks, int m,
-                                 int32_t* sacc, int workgroups,
-                                 hipStream_t s) {
+template <bool FUSED>
+hipError_t launch_stream(const Desc* descs, const int64_t* chunk0,
+                         int32_t count, int64_t total_chunks, int m,
+                         int32_t* sacc, int workgroups, hipStream_t s) {
   const dim3 grid((unsigned)workgroups), block(256);
   switch (m) {
-    case 1: stream_kernel<1><<<grid, block, 0, s>>>(descs, chunk0, count, total_chunks, sacc); break;
-    case 2: stream_kernel<2><<<grid, block, 0, s>>>(descs, chunk0, count, total_chunks, sacc); break;
-    case 3: stream_kernel<3><<<grid, block, 0, s>>>(descs, chunk0, count, total_chunks, sacc); break;
-    case 4: stream_kernel<4><<<grid, block, 0, s>>>(descs, chunk0, count, total_chunks, sacc); break;
+    case 1: stream_kernel<1, FUSED><<<grid, block, 0, s>>>(descs, chunk0, count, total_chunks, sacc); break;
+    case 2: stream_kernel<2, FUSED><<<grid, block, 0, s>>>(descs, chunk0, count, total_chunks, sacc); break;
+    case 3: stream_kernel<3, FUSED><<<grid, block, 0, s>>>(descs, chunk0, count, total_chunks, sacc); break;
+    case 4: stream_kernel<4, FUSED><<<grid, block, 0, s>>>(descs, chunk0, count, total_chunks, sacc); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+hipError_t launch_stream_grouped(const Desc* descs, const int64_t* chunk0,
+                                 int32_t count, int64_t total_chunks, int m,
+                                 int32_t* sacc, int workgroups, bool fused,
+                                 hipStream_t s) {
+  return fused ? launch_stream<true>(descs, chunk0, count, total_chunks, m,
+                                     sacc, workgroups, s)
+               : launch_stream<false>(descs, chunk0, count, total_chunks, m,
+                                      sacc, workgroups, s);
 }
 
 }  // namespace bt

@@ -90,18 +90,6 @@ __global__ __launch_bounds__(256) void pack_kernel(const int8_t* __restrict__ t,
 constexpr int kRegVec = 8;                     // float4 per thread held
 constexpr int64_t kRegRow = 256 * 4 * kRegVec;  // 8192 inputs
 
-__device__ __forceinline__ uint32_t quant4(const float4& v, float inv) {
-  const float e[4] = {v.x, v.y, v.z, v.w};
-  uint32_t packed4 = 0;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    float r = rintf(__fmul_rn(e[j], inv));  // round half to even
-    r = fminf(fmaxf(r, -127.0f), 127.0f);
-    packed4 |= ((uint32_t)(int32_t)r & 0xffu) << (8 * j);
-  }
-  return packed4;
-}
-
 __device__ __forceinline__ void quant_row(const float* __restrict__ x,
                                           int64_t k, int8_t* __restrict__ xq,
                                           float* __restrict__ sa, int64_t row,
@@ -132,8 +120,8 @@ __device__ __forceinline__ void quant_row(const float* __restrict__ x,
   if ((tid & 63) == 0) part[tid >> 6] = amax;
   __syncthreads();
   amax = fmaxf(fmaxf(part[0], part[1]), fmaxf(part[2], part[3]));
-  const float a = fmaxf(amax, 1e-5f);
-  const float inv = __fdiv_rn(127.0f, a);
+  const QScale qs = quant_scale(amax);
+  const float inv = qs.inv;
   if (in_regs) {
 #pragma unroll
     for (int r = 0; r < kRegVec; ++r) {
@@ -143,7 +131,7 @@ __device__ __forceinline__ void quant_row(const float* __restrict__ x,
   } else {
     for (int64_t i = tid; i < k4; i += 256) qr[i] = (int32_t)quant4(xr[i], inv);
   }
-  if (tid == 0) sa[row] = __fdiv_rn(a, 127.0f);
+  if (tid == 0) sa[row] = qs.sa;
 }
 
 // One workgroup per token row.

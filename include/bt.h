@@ -165,6 +165,33 @@ int32_t bt_grouped_plan(const bt_problem* probs, int32_t count, void* plan,
 int32_t bt_gemm_grouped(const void* plan_dev, const void* plan_host,
                         void* stream);
 
+/* Grouped decode product that quantizes its own activations (the per-token
+ * int8 absmax step and the ternary product in one launch: the activation
+ * quantization of "Microsoft BitNet" section "技术实现细节" fused into the
+ * GEMV).  Each problem gives fp32 activations x [m, k] instead of x_q and
+ * s_a; the launch quantizes every token row exactly as bt_quant_act would
+ * (same x_q, same s_a, bit for bit) and then computes what bt_gemm would
+ * with them.  Neither x_q nor s_a is written out.
+ *  x   fp32 [m, k], device, 16-byte aligned.
+ * Other fields and rules as in bt_problem, and further 1 <= m <= 4 and
+ * m * k <= BT_FUSED_MAX_MK (each wave keeps its problem's quantized rows in
+ * LDS); otherwise BT_E_SHAPE.  The plan is launched with bt_gemm_grouped
+ * and obeys the same rules (scratch, reuse, no overlapping launches). */
+#define BT_FUSED_MAX_MK 16384
+typedef struct bt_problem_f32 {
+  const uint8_t* packed;
+  const float* x;
+  float* y;
+  int32_t* acc; /* nullable */
+  float s_w;
+  int32_t n;
+  int32_t k;
+  int32_t m; /* every problem of one group has the same m */
+} bt_problem_f32;
+int64_t bt_grouped_plan_f32_bytes(const bt_problem_f32* probs, int32_t count);
+int32_t bt_grouped_plan_f32(const bt_problem_f32* probs, int32_t count,
+                            void* plan, int64_t plan_bytes);
+
 #ifdef __cplusplus
 }
 #endif

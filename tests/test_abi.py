@@ -155,7 +155,8 @@ def problems(specs):
 
 
 HDR_FIELDS = ["units", "desc_off", "chunk_off", "unit_off", "sacc_off",
-              "scnt_off", "bytes", "total_chunks", "blocks"]
+              "scnt_off", "bytes", "total_chunks", "blocks", "fused"]
+DESC_BYTES = 112
 
 
 def parse_plan(img):
@@ -175,16 +176,17 @@ def parse_plan(img):
 
 
 def desc(img, p, i):
-    base = p["desc_off"] + 96 * i
-    raw = img[base:base + 96]
+    base = p["desc_off"] + DESC_BYTES * i
+    raw = img[base:base + DESC_BYTES]
     ptrs = raw[:40].view(np.int64)
     s_w = raw[40:44].view(np.float32)[0]
     n, k, m, nblk, ntt = raw[44:64].view(np.int32)
     chunk0 = raw[64:72].view(np.int64)[0]
     blk0, kc, nsplit, split_len, slot0, region0 = raw[72:96].view(np.int32)
+    xf = raw[96:104].view(np.int64)[0]
     return dict(ptrs=ptrs, s_w=s_w, n=n, k=k, m=m, nblk=nblk, ntt=ntt,
                 chunk0=chunk0, blk0=blk0, kc=kc, nsplit=nsplit,
-                split_len=split_len, slot0=slot0, region0=region0)
+                split_len=split_len, slot0=slot0, region0=region0, xf=xf)
 
 
 def test_grouped_plan_layout_stream(L):
@@ -302,3 +304,64 @@ def test_binding_rejects_host_tensors(L):
     t = torch.zeros((64, 64), dtype=torch.int8)
     with pytest.raises(TypeError):
         bt.bt_pack_i2s(t, packed=torch.zeros(1024, dtype=torch.uint8))
+
+
+# ------------------------------------------------- fused-quantization plans
+def problems_f32(specs):
+    arr = (bt.bt_problem_f32 * len(specs))()
+    for i, (n, k, m) in enumerate(specs):
+        base = P * (i + 1) * 16
+        arr[i] = bt.bt_problem_f32(base, base + P, base + 2 * P, None, 0.25,
+                                   n, k, m)
+    return arr
+
+
+def test_grouped_plan_f32_layout(L):
+    specs = [(2560, 2560, 1), (2560, 6912, 1), (100, 64, 1)]
+    arr = problems_f32(specs)
+    nbytes = L.bt_grouped_plan_f32_bytes(arr, len(specs))
+    assert nbytes > 0
+    img = np.zeros(nbytes, np.uint8)
+    assert L.bt_grouped_plan_f32(arr, len(specs), img.ctypes.data,
+                                 nbytes) == 0
+    p = parse_plan(img)
+    assert p["kind"] == 0 and p["fused"] == 1 and p["units"] == 0
+    for i in range(len(specs)):
+        d = desc(img, p, i)
+        base = P * (i + 1) * 16
+        # w, xq, sa, y, acc: the int8 activations and scales are not used
+        assert d["ptrs"].tolist() == [base, 0, 0, base + 2 * P, 0]
+        assert d["xf"] == base + P
+    # the same problems through the int8 entry give an unfused plan
+    img2 = np.zeros(L.bt_grouped_plan_bytes(problems(specs), 3), np.uint8)
+    assert L.bt_grouped_plan(problems(specs), 3, img2.ctypes.data,
+                             img2.size) == 0
+    p2 = parse_plan(img2)
+    assert p2["fused"] == 0 and desc(img2, p2, 0)["xf"] == 0
+
+
+def test_grouped_plan_f32_errors(L):
+    img = np.zeros(1 << 20, np.uint8)
+    assert L.bt_grouped_plan_f32_bytes(None, 1) == bt.BT_E_NULL
+    assert L.bt_grouped_plan_f32_bytes(problems_f32([(64, 64, 1)]),
+                                       0) == bt.BT_E_ARG
+    for spec in [(64, 64, 5), (64, 64, 0), (64, 2 * 8192 + 64, 1),
+                 (64, 8192, 3), (64, 96, 1)]:
+        assert L.bt_grouped_plan_f32_bytes(problems_f32([spec]),
+                                           1) == bt.BT_E_SHAPE, spec
+    assert L.bt_grouped_plan_f32_bytes(problems_f32([(64, 16384, 1)]), 1) > 0
+    assert L.bt_grouped_plan_f32_bytes(problems_f32([(64, 4096, 4)]), 1) > 0
+    arr = problems_f32([(64, 64, 1), (64, 64, 1)])
+    arr[1].x = None
+    assert L.bt_grouped_plan_f32(arr, 2, img.ctypes.data,
+                                 img.size) == bt.BT_E_NULL
+    arr = problems_f32([(64, 64, 1), (64, 64, 1)])
+    arr[1].x = arr[1].x + 4
+    assert L.bt_grouped_plan_f32(arr, 2, img.ctypes.data,
+                                 img.size) == bt.BT_E_ALIGN
+    arr = problems_f32([(64, 64, 1), (64, 64, 2)])
+    assert L.bt_grouped_plan_f32(arr, 2, img.ctypes.data,
+                                 img.size) == bt.BT_E_SHAPE
+    arr = problems_f32([(64, 64, 1)])
+    assert L.bt_grouped_plan_f32(arr, 1, None, img.size) == bt.BT_E_NULL
+    assert L.bt_grouped_plan_f32(arr, 1, img.ctypes.data, 16) == bt.BT_E_ARG

@@ -291,14 +291,15 @@ def test_grouped_layers_match_oracle(m, layers):
             check_y(prob["y"].cpu().numpy(), y_r, acc_r)
 
 
-@pytest.mark.parametrize("m", [1, 4])
-def test_decode_set_grouped_full_size(m):
+@pytest.mark.parametrize("m,fused", [(1, False), (4, False), (1, True)])
+def test_decode_set_grouped_full_size(m, fused):
     """The whole 2B-shaped decode set (30 layers x 7 projections, 521 MB of
     packed weights) in one grouped launch, as the benchmark runs it, three
     times in a row; every output of every launch against the oracle.  To
     keep the host side short, the 30 layers share layer 0's seven weight
     tensors (the launch still streams 521 MB); every (layer, projection) has
-    its own activations."""
+    its own activations.  fused: the launch quantizes the fp32 activations
+    itself."""
     work = wl.decode_2b(m=m)
     shared = {}
     for p in work.problems():
@@ -310,17 +311,21 @@ def test_decode_set_grouped_full_size(m):
     for p in work.problems():
         t, s_w, packed, packed_ref = shared[p.proj]
         x = work.activations(p.layer, p.proj)
-        x_q, s_a = bt.bt_quant_act(dev(x))
-        probs.append(dict(packed=packed, s_w=s_w, n=p.n, k=p.k, x_q=x_q,
-                          s_a=s_a,
-                          y=torch.empty((m, p.n), device="cuda:0"),
-                          acc=torch.empty((m, p.n), dtype=torch.int32,
-                                          device="cuda:0")))
+        prob = dict(packed=packed, s_w=s_w, n=p.n, k=p.k,
+                    y=torch.empty((m, p.n), device="cuda:0"),
+                    acc=torch.empty((m, p.n), dtype=torch.int32,
+                                    device="cuda:0"))
+        if fused:
+            prob["x"] = dev(x)
+        else:
+            prob["x_q"], prob["s_a"] = bt.bt_quant_act(dev(x))
+        probs.append(prob)
         q_r, sa_r = oracle.quant_act(x)
         acc_r, y_r = oracle.gemm(packed_ref, s_w, p.n, p.k, q_r, sa_r,
                                  nthreads=NTHREADS)
         refs.append((acc_r, y_r))
-    plan = bt.bt_grouped_plan(probs)
+    plan = (bt.bt_grouped_plan_f32(probs) if fused
+            else bt.bt_grouped_plan(probs))
     for launch in range(3):
         for p in probs:
             p["y"].fill_(float("nan"))
@@ -363,6 +368,51 @@ def test_grouped_small_problems(m):
                 _, q_r, s_r, acc_r, y_r = oracle_product(t, x, s_w)
                 np.testing.assert_array_equal(prob["acc"].cpu().numpy(), acc_r)
                 check_y(prob["y"].cpu().numpy(), y_r, acc_r)
+
+
+@pytest.mark.parametrize("m", [1, 2, 3, 4])
+def test_grouped_fused_quant(m):
+    """Grouped calls that quantize their own fp32 activations: outputs equal
+    to the oracle's (which quantizes with its own code) and bit-identical to
+    the two-step path (bt_quant_act, then the grouped product); ragged and
+    tiny shapes, one-chunk rows, the longest rows that fit (m k = 16384);
+    each plan launched twice."""
+    kmax = bt.BT_FUSED_MAX_MK // m // 64 * 64
+    specs = [(512, 256), (64, 64), (70, 192), (1, 64), (130, 320),
+             (300, 2560), (200, kmax)]
+    probs, steps, refs = [], [], []
+    for i, (n, k) in enumerate(specs):
+        rng = np.random.default_rng([109, m, i])
+        t = wl.trits(rng, (n, k), wl.DECODE_2B)
+        x = wl.x_normal_outliers(rng, (m, k))
+        if i == 1:
+            x[0] = 0  # an all-zero row: amax floor, q = 0
+        s_w = wl.scale(rng, 0.01, 0.05)
+        packed = bt.bt_pack_i2s(dev(t))
+        probs.append(dict(packed=packed, s_w=s_w, n=n, k=k, x=dev(x),
+                          y=torch.empty((m, n), device="cuda:0"),
+                          acc=torch.empty((m, n), dtype=torch.int32,
+                                          device="cuda:0")))
+        x_q, s_a = bt.bt_quant_act(dev(x))
+        steps.append(dict(packed=packed, s_w=s_w, n=n, k=k, x_q=x_q, s_a=s_a,
+                          y=torch.empty((m, n), device="cuda:0"),
+                          acc=torch.empty((m, n), dtype=torch.int32,
+                                          device="cuda:0")))
+        refs.append(oracle_product(t, x, s_w))
+    plan = bt.bt_grouped_plan_f32(probs)
+    plan2 = bt.bt_grouped_plan(steps)
+    bt.bt_gemm_grouped(plan2)
+    for _ in range(2):
+        for p in probs:
+            p["y"].fill_(float("nan"))
+            p["acc"].fill_(0x7EADBEEF)
+        bt.bt_gemm_grouped(plan)
+        torch.cuda.synchronize()
+        for prob, two, (_, _, _, acc_r, y_r) in zip(probs, steps, refs):
+            np.testing.assert_array_equal(prob["acc"].cpu().numpy(), acc_r)
+            check_y(prob["y"].cpu().numpy(), y_r, acc_r)
+            assert torch.equal(prob["y"], two["y"])
+            assert torch.equal(prob["acc"], two["acc"])
 
 
 @pytest.mark.parametrize("m", [70, 130])
