@@ -401,7 +401,7 @@ struct Stream {
   // any is used (one round trip per batch); a row of at most one batch
   // stays in registers between the absmax and the quantization, longer rows
   // are read a second time (from cache).
-  static constexpr int kBatch = 16;
+  static constexpr int kBatch = 8;
   __device__ __forceinline__ void load_batch(float4 (&v)[kBatch],
                                              gcfloat4_ptr xr, int b0,
                                              int n4) const {

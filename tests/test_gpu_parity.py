@@ -469,3 +469,68 @@ def test_prefill_layer_sampled():
                                      nthreads=NTHREADS)
             np.testing.assert_array_equal(acc[:, r0:r0 + 8], acc_r)
             check_y(y[:, r0:r0 + 8], y_r, acc_r)
+
+
+def shared_weight_set(work, sample=None, launches=2, seed=110):
+    """The products of `work` in one grouped plan, the way the benchmark
+    launches them, with every layer reusing layer 0's weight tensors (the
+    launch still streams the whole set); each (layer, projection) has its
+    own activations.  Every launch is checked against the oracle: every
+    output, or, with sample = r, r sampled row groups of 8 per product (all
+    tokens)."""
+    m = work.m
+    shared = {}
+    for p in work.problems():
+        if p.layer == 0:
+            t, s_w = work.weights(0, p.proj)
+            shared[p.proj] = (t, s_w, bt.bt_pack_i2s(dev(t)))
+    probs, checks = [], []
+    for i, p in enumerate(work.problems()):
+        t, s_w, packed = shared[p.proj]
+        x = work.activations(p.layer, p.proj)
+        x_q, s_a = bt.bt_quant_act(dev(x))
+        probs.append(dict(packed=packed, s_w=s_w, n=p.n, k=p.k, x_q=x_q,
+                          s_a=s_a, y=torch.empty((m, p.n), device="cuda:0"),
+                          acc=torch.empty((m, p.n), dtype=torch.int32,
+                                          device="cuda:0")))
+        q_r, sa_r = oracle.quant_act(x)
+        if sample is None:
+            spans = [(0, p.n)]
+        else:
+            rng = np.random.default_rng([seed, i])
+            spans = [(r0, r0 + 8) for r0 in sorted(set(
+                rng.integers(0, p.n - 8, size=sample).tolist()))]
+        refs = []
+        for r0, r1 in spans:
+            pk = oracle.pack_i2s(t[r0:r1])[0]
+            refs.append((r0, r1) + tuple(oracle.gemm(
+                pk, s_w, r1 - r0, p.k, q_r, sa_r, nthreads=NTHREADS)))
+        checks.append(refs)
+    plan = bt.bt_grouped_plan(probs)
+    for launch in range(launches):
+        for p in probs:
+            p["y"].fill_(float("nan"))
+            p["acc"].fill_(0x7EADBEEF)
+        bt.bt_gemm_grouped(plan)
+        torch.cuda.synchronize()
+        for i, (prob, refs) in enumerate(zip(probs, checks)):
+            acc = prob["acc"].cpu().numpy()
+            y = prob["y"].cpu().numpy()
+            for r0, r1, acc_r, y_r in refs:
+                assert np.array_equal(acc[:, r0:r1], acc_r), \
+                    f"launch {launch} product {i} rows {r0}..{r1}"
+                check_y(y[:, r0:r1], y_r, acc_r)
+
+
+@pytest.mark.parametrize("m", [1, 64])
+def test_decode_8b_set_grouped_full_size(m):
+    """The 8B-shaped set (32 layers x 7 projections, 1.74 GB of packed
+    weights) in one grouped launch: every output at M=1, sampled rows at
+    M=64."""
+    shared_weight_set(wl.decode_8b(m), sample=None if m == 1 else 3)
+
+
+def test_prefill_layer_grouped_sampled():
+    """The M=512 layer's seven products in one grouped launch (split
+    reductions for the long down projection), as the benchmark runs it."""
+    shared_weight_set(wl.prefill_2b(512), sample=4)
