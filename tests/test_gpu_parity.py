@@ -272,8 +272,8 @@ def grouped_case(work, layers):
     return probs, host
 
 
-@pytest.mark.parametrize("m,layers", [(1, 2), (3, 2), (8, 2), (32, 2),
-                                      (64, 1), (130, 1)])
+@pytest.mark.parametrize("m,layers", [(1, 2), (3, 2), (8, 2), (16, 2),
+                                      (32, 2), (40, 1), (64, 1), (130, 1)])
 def test_grouped_layers_match_oracle(m, layers):
     work = wl.decode_2b(m=m, layers=layers)
     probs, host = grouped_case(work, layers)
@@ -338,7 +338,7 @@ def test_decode_set_grouped_full_size(m, fused):
             check_y(prob["y"].cpu().numpy(), y_r, acc_r)
 
 
-@pytest.mark.parametrize("m", [1, 2, 3, 4, 8])
+@pytest.mark.parametrize("m", [1, 2, 3, 4, 5, 8, 32, 33, 64])
 def test_grouped_small_problems(m):
     """Grouped calls with fewer 1 KiB chunks than waves (tiny shapes, ragged
     rows, k of one chunk): row blocks shared by many waves; each plan is
