@@ -22,6 +22,9 @@ DEVICE_FLAGS = [
     "-ffp-contract=off",
     # packed fp32 instructions are kept out of every kernel
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # kernel arguments arrive in SGPRs at dispatch (the code object keeps a
+    # prologue that loads them where the firmware does not preload)
+    "-mllvm", "-amdgpu-kernarg-preload-count=16",
     "-Wall", "-Wno-unused-function",
     "-I", INCLUDE, "-I", CSRC,
 ]
