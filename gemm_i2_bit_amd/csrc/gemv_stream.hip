@@ -602,9 +602,13 @@ __device__ __forceinline__ void stream_range(Stream<TOK, FUSED>& st,
 }
 
 // Wave wv of W streams chunks [wv T / W, (wv + 1) T / W) of the T chunks.
-// (Handing out part of the stream dynamically from a shared counter was
-// measured too: the counter's contention and the per-piece start-up cost
-// more than the uneven finish of equal ranges.)
+// Waves of one launch finish several microseconds apart (whole XCDs run
+// slower or faster from launch to launch), but the launch is bound by the
+// total bytes over the aggregate HBM rate: a wave that ends early leaves its
+// share of the bandwidth to the others.  Handing out the stream's tail
+// dynamically (from shared counters, or through a claiming wave per
+// workgroup with work stealing across XCDs) evened out the ends and made
+// the launch slower, not faster.
 template <int TOK, bool FUSED>
 __global__ __launch_bounds__(256) void stream_kernel(
     const Desc* __restrict__ descs, const int64_t* __restrict__ chunk0s,
