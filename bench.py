@@ -51,9 +51,12 @@ def log(*a):
 
 
 def kernel_sources_sha():
+    """Hash of the kernel sources and of the build script (its compiler
+    flags shape the kernels too)."""
     h = hashlib.sha256()
     for f in sorted(glob.glob(os.path.join(ROOT, "gemm_i2_bit_amd", "csrc",
-                                           "*"))):
+                                           "*"))) + [
+            os.path.join(ROOT, "gemm_i2_bit_amd", "build.py")]:
         with open(f, "rb") as fh:
             h.update(os.path.basename(f).encode())
             h.update(fh.read())
