@@ -159,6 +159,101 @@ class WorkSet:
                                 p["x_q"], p["s_a"], y=p["y"])
 
 
+class ChainSet:
+    """One token through the layer-chained decode of a workload's weights
+    (workloads.CHAIN_PHASES): per layer, four dependent phases, each one
+    quantization launch of the phase's input and one grouped launch of the
+    products that read it (fused: one grouped launch that quantizes its fp32
+    input itself).  Nothing runs ahead of its input."""
+
+    def __init__(self, work: wl.Workload, torch, bt, layers=None,
+                 fused=False):
+        self.torch, self.bt = torch, bt
+        self.fused = fused
+        dev = torch.device("cuda:0")
+        self.layers = work.layers if layers is None else layers
+        self.x0 = torch.from_numpy(wl.chain_input(work)).to(dev)
+        self.phases = []  # (input [1, k], x_q, s_a, plan, names, layer)
+        self.y = []       # per layer: projection -> output [1, n]
+        self.bytes = 0
+        x = self.x0
+        for l in range(self.layers):
+            ys, packed = {}, {}
+            for proj in wl.PROJ_NAMES:
+                t, s_w = work.weights(l, proj)
+                packed[proj] = (bt.bt_pack_i2s(torch.from_numpy(t).to(dev)),
+                                float(s_w))
+                ys[proj] = torch.empty((1, t.shape[0]), dtype=torch.float32,
+                                       device=dev)
+                del t
+            for src, dsts in wl.CHAIN_PHASES:
+                xin = x if src == "x" else ys[src]
+                k = xin.shape[1]
+                x_q = torch.empty((1, k), dtype=torch.int8, device=dev)
+                s_a = torch.empty(1, dtype=torch.float32, device=dev)
+                probs = [dict(packed=packed[d][0], s_w=packed[d][1],
+                              n=ys[d].shape[1], k=k, x_q=x_q, s_a=s_a,
+                              x=xin, y=ys[d]) for d in dsts]
+                plan = (bt.bt_grouped_plan_f32(probs) if fused
+                        else bt.bt_grouped_plan(probs))
+                self.phases.append((xin, x_q, s_a, plan, dsts, l))
+                self.bytes += 5 * k + 4 + sum(
+                    bt.bt_packed_bytes(p["n"], k) + k + 4 + 4 * p["n"]
+                    for p in probs)
+            self.y.append(ys)
+            x = ys[wl.CHAIN_OUT]
+        self.out = x
+        torch.cuda.synchronize()
+
+    def launches(self):
+        return (1 if self.fused else 2) * len(self.phases)
+
+    def step(self):
+        for xin, x_q, s_a, plan, _, _ in self.phases:
+            if not self.fused:
+                self.bt.bt_quant_act(xin, x_q, s_a)
+            self.bt.bt_gemm_grouped(plan)
+
+    def capture(self):
+        """The token as one HIP graph (captured after a warm-up pass on a
+        side stream)."""
+        torch = self.torch
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            self.step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            self.step()
+        torch.cuda.synchronize()
+        return g
+
+
+def run_chain(cs: ChainSet, tokens: int, warmup: int, torch):
+    """Per-token wall time of the chained decode, eager and graph-replayed
+    (ms)."""
+    for _ in range(warmup):
+        cs.step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(tokens):
+        cs.step()
+    torch.cuda.synchronize()
+    eager = (time.perf_counter() - t0) / tokens * 1e3
+    g = cs.capture()
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(tokens):
+        g.replay()
+    torch.cuda.synchronize()
+    graph = (time.perf_counter() - t0) / tokens * 1e3
+    return eager, graph
+
+
 def run_timed(ws: WorkSet, steps: int, warmup: int, torch):
     """Time `steps` whole steps (quantize + product); then time the product
     kernel alone over `steps` back-to-back launches (HIP events on the
@@ -327,6 +422,20 @@ def main():
             "frac_int8_peak": round(tops_k / INT8_PEAK_TOPS, 4)}
         del pws
         torch.cuda.empty_cache()
+        if work.name.startswith("decode_2b_m1"):
+            chained = {"workload": "decode_2b chained, M=1 (one token, every "
+                                   "dependency kept)"}
+            for fused in (False, True):
+                cs = ChainSet(work, torch, bt, fused=fused)
+                eager, graph = run_chain(cs, 20, 3, torch)
+                chained["fused" if fused else "two_launch"] = {
+                    "layers": cs.layers, "launches_per_token": cs.launches(),
+                    "ms_per_token_eager": round(eager, 4),
+                    "ms_per_token_graph": round(graph, 4),
+                    "tokens_per_s_graph": round(1e3 / graph, 1)}
+                del cs
+                torch.cuda.empty_cache()
+            out["chained_decode"] = chained
 
     if args.calibrate_copy:
         n = 256 << 20

@@ -134,3 +134,18 @@ def gemm(packed, s_w, n: int, k: int, q, s_a, nthreads: int = 1, rows=None):
     if rc != 0:
         raise ValueError(f"oracle_gemm failed with {rc}")
     return acc, y
+
+
+def rescale_f32(acc, s_w, s_a):
+    """O5 in the method's own precision: y = ((float)acc * s_w) * s_a, two
+    fp32 multiplies left to right (config C1 writes the rescale in that
+    order; bitnet.cpp CPU tutorial §1.1 for the integer product it scales).
+    The fp64 ``y`` of ``gemm`` is the exact value; this is the fp32 result a
+    consumer of the output sees, e.g. the next quantization of a chained
+    decode."""
+    acc = np.asarray(acc)
+    a32 = acc.astype(np.float32)
+    if not np.array_equal(a32.astype(np.int64), acc.astype(np.int64)):
+        raise ValueError("accumulator not exact in fp32")
+    s_a = np.asarray(s_a, np.float32).reshape(-1, 1)
+    return (a32 * np.float32(s_w)).astype(np.float32) * s_a

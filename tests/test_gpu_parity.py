@@ -534,3 +534,61 @@ def test_prefill_layer_grouped_sampled():
     """The M=512 layer's seven products in one grouped launch (split
     reductions for the long down projection), as the benchmark runs it."""
     shared_weight_set(wl.prefill_2b(512), sample=4)
+
+
+# ------------------------------------------------------- layer-chained decode
+def oracle_chain(work, layers):
+    """The chained decode on the CPU: every phase quantizes its input (O3),
+    multiplies (O4) and rescales in fp32 (O5), and the fp32 outputs feed the
+    next phase as they would on the GPU."""
+    x = wl.chain_input(work)
+    outs = []
+    for l in range(layers):
+        ys = {}
+        for src, dsts in wl.CHAIN_PHASES:
+            xin = x if src == "x" else ys[src]
+            q, s_a = oracle.quant_act(xin)
+            for d in dsts:
+                t, s_w = work.weights(l, d)
+                p, bad = oracle.pack_i2s(t)
+                assert bad == 0
+                acc, _ = oracle.gemm(p, s_w, t.shape[0], t.shape[1], q, s_a,
+                                     nthreads=NTHREADS)
+                ys[d] = oracle.rescale_f32(acc, s_w, s_a)
+        outs.append(ys)
+        x = ys[wl.CHAIN_OUT]
+    return outs
+
+
+@pytest.mark.parametrize("fused", [False, True])
+def test_chained_decode_matches_oracle(fused):
+    """Two 2B-shaped layers chained phase by phase (two launches per phase,
+    or one launch that quantizes its fp32 input): every output of every
+    projection equals the oracle's bit for bit (each phase's fp32 output is
+    the next phase's input), eagerly and on each replay of the token captured
+    as a HIP graph, with eager launches between the replays."""
+    import bench
+    work = wl.decode_2b(1)
+    cs = bench.ChainSet(work, torch, bt, layers=2, fused=fused)
+    cs.step()
+    torch.cuda.synchronize()
+    ref = oracle_chain(work, 2)
+
+    def check(label):
+        for l in range(2):
+            for proj in wl.PROJ_NAMES:
+                got = cs.y[l][proj].cpu().numpy()
+                assert np.array_equal(got, ref[l][proj]), (label, l, proj)
+
+    check("eager")
+    graph = cs.capture()
+    for rep in range(3):
+        for ys in cs.y:
+            for t in ys.values():
+                t.fill_(float("nan"))
+        graph.replay()
+        torch.cuda.synchronize()
+        check(f"replay {rep}")
+        cs.step()
+        torch.cuda.synchronize()
+        check(f"eager after replay {rep}")

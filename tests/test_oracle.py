@@ -391,3 +391,30 @@ def test_rescale_close_to_exact_product(orc):
             else:
                 err = abs((Fraction(float(y[i, r])) - exact) / exact)
                 assert err < Fraction(1, 2 ** 50)
+
+
+def test_rescale_f32_is_two_correctly_rounded_products(orc):
+    """rescale_f32 against exact rationals: each fp32 product of two fp32
+    values is exact in a double, so rounding the exact rational once to fp32
+    is the correctly rounded fp32 multiply; two of them, left to right."""
+    rng = np.random.default_rng(22)
+    acc = rng.integers(-1_000_000, 1_000_001, size=(3, 40)).astype(np.int32)
+    acc[0, :3] = [0, 1, -1]
+    s_w = np.float32(0.0213)
+    s_a = rng.random(3).astype(np.float32) * np.float32(0.7) + np.float32(1e-4)
+    y = orc.rescale_f32(acc, s_w, s_a)
+    assert y.dtype == np.float32
+    for i in range(3):
+        for j in range(acc.shape[1]):
+            p1 = Fraction(int(acc[i, j])) * Fraction(float(s_w))
+            assert Fraction(float(p1)) == p1  # exact in a double
+            r1 = np.float32(float(p1))
+            p2 = Fraction(float(r1)) * Fraction(float(s_a[i]))
+            assert Fraction(float(p2)) == p2
+            assert y[i, j] == np.float32(float(p2))
+
+
+def test_rescale_f32_powers_of_two_exact(orc):
+    acc = np.array([[5, -7, 0, 123456]], np.int32)
+    y = orc.rescale_f32(acc, np.float32(0.25), np.array([0.125], np.float32))
+    assert y.tolist() == [[5 / 32, -7 / 32, 0.0, 123456 / 32]]

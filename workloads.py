@@ -148,6 +148,32 @@ def decode_8b(m: int = 1, layers: int = 32) -> Workload:
                     0.005, 0.03, "student_t")
 
 
+# ----------------------------------------------------- layer-chained decode
+# One token through the layers with every dependency kept: within a layer
+# each phase quantizes an earlier output of the same layer (the layer input
+# for the first phase) and runs the products that read it; the last output
+# is the next layer's input.  Attention, the residual adds and the gated
+# activation lie outside the ternary product, so the query output stands in
+# for the attention output and the up output for the gated product.
+CHAIN_PHASES = (("x", ("q", "k", "v")),
+                ("q", ("o",)),
+                ("o", ("gate", "up")),
+                ("up", ("down",)))
+CHAIN_OUT = "down"
+
+
+def chain_input(work: Workload, m: int = 1):
+    """The first layer's input for the layer-chained decode of a workload's
+    weights: [m, hidden] drawn like that workload's activations."""
+    rng = np.random.default_rng([work.seed, 1 << 20, 0, 1, m])
+    shape = (m, work.shapes["q"][0])
+    if work.x_kind == "outliers":
+        return x_normal_outliers(rng, shape)
+    if work.x_kind == "student_t":
+        return x_student_t(rng, shape)
+    return x_normal(rng, shape)
+
+
 def single_gemv():
     """The small single-GEMV case: M=1, K=256, N=512, seed 0, uniform trits
     drawn first, then x ~ N(0, 1); s_w = 0.02."""
