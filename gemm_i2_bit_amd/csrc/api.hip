@@ -105,8 +105,11 @@ Desc make_desc(const uint8_t* packed, float s_w, int64_t n, int64_t k,
 // Reduction split of each problem of a matrix-core plan.  Prefill tiles are
 // bound by the matrix cores and one tile runs per workgroup, so a problem
 // with a long reduction would finish last: its tiles are cut into ranges of
-// about the shortest problem's chunk count (an even number of chunks, so
-// that only the last range of a row can end on an odd chunk).
+// about the shortest problem's chunk count, but not below kMinSplit chunks
+// (a tiny problem in the plan must not cut the others into ranges whose
+// set-up and combining outweigh their work), and always an even number of
+// chunks, so that only the last range of a row can end on an odd chunk.
+constexpr int32_t kMinSplit = 32;
 struct Split {
   int32_t nsplit, len;
 };
@@ -116,6 +119,7 @@ std::vector<Split> plan_splits(const bt_problem* probs, int32_t count,
   int32_t kc_min = INT32_MAX;
   for (int32_t i = 0; i < count; ++i)
     kc_min = std::min(kc_min, (int32_t)(probs[i].k / 64));
+  kc_min = std::max(kc_min, kMinSplit);
   for (int32_t i = 0; i < count; ++i) {
     const int32_t kc = probs[i].k / 64;
     int32_t ns = 1;

@@ -370,6 +370,55 @@ def test_grouped_small_problems(m):
                 check_y(prob["y"].cpu().numpy(), y_r, acc_r)
 
 
+@pytest.mark.parametrize("m", [1, 4, 8, 130])
+def test_grouped_extremes(m):
+    """Grouped calls at the largest k (65536, the int32 extreme of all +1
+    weights against all 127 activations), with all -1 and all-zero rows, an
+    all-zero token and a second, one-chunk problem in the same plan: a row
+    block of 1024 chunks is cut among many waves (m <= 4) or split into
+    reduction ranges (prefill sizes)."""
+    k, n = 65536, 70
+    rng = np.random.default_rng([111, m])
+    t = wl.trits(rng, (n, k), wl.DECODE_2B)
+    t[0] = 1
+    t[1] = -1
+    t[2] = 0
+    x = wl.x_normal(rng, (m, k))
+    x[0] = 1.0
+    if m > 1:
+        x[1] = -1.0
+    if m > 2:
+        x[2] = 0.0
+    t2 = wl.trits(rng, (64, 64))
+    x2 = wl.x_normal(rng, (m, 64))
+    cases = [(t, x, np.float32(1.0)), (t2, x2, np.float32(0.02))]
+    probs = []
+    for tt, xx, s_w in cases:
+        x_q, s_a = bt.bt_quant_act(dev(xx))
+        probs.append(dict(packed=bt.bt_pack_i2s(dev(tt)), s_w=s_w,
+                          n=tt.shape[0], k=tt.shape[1], x_q=x_q, s_a=s_a,
+                          y=torch.full((m, tt.shape[0]), float("nan"),
+                                       device="cuda:0"),
+                          acc=torch.full((m, tt.shape[0]), 0x7EADBEEF,
+                                         dtype=torch.int32, device="cuda:0")))
+    plan = bt.bt_grouped_plan(probs)
+    for _ in range(2):
+        for p in probs:
+            p["y"].fill_(float("nan"))
+        bt.bt_gemm_grouped(plan)
+        torch.cuda.synchronize()
+        for prob, (tt, xx, s_w) in zip(probs, cases):
+            _, _, _, acc_r, y_r = oracle_product(tt, xx, s_w)
+            acc = prob["acc"].cpu().numpy()
+            np.testing.assert_array_equal(acc, acc_r)
+            check_y(prob["y"].cpu().numpy(), y_r, acc_r)
+        acc = probs[0]["acc"].cpu().numpy()
+        assert acc[0, 0] == 127 * k and acc[0, 1] == -127 * k
+        assert (acc[:, 2] == 0).all()
+        if m > 2:
+            assert (acc[2] == 0).all()
+
+
 @pytest.mark.parametrize("m", [1, 2, 3, 4])
 def test_grouped_fused_quant(m):
     """Grouped calls that quantize their own fp32 activations: outputs equal
@@ -417,9 +466,9 @@ def test_grouped_fused_quant(m):
 
 @pytest.mark.parametrize("m", [70, 130])
 @pytest.mark.parametrize("specs", [
-    [(300, 576), (200, 2368)],            # 37 chunks cut into 4 ranges
-    [(300, 576), (200, 2368), (64, 64)],  # one-chunk rows: 19 ranges of 2
-])
+    [(300, 2048), (200, 8384)],            # 131 chunks: 3 x 34 and 29
+    [(300, 2048), (200, 8384), (64, 64)],  # plus one-chunk rows, which do
+])                                         # not shorten the ranges
 def test_grouped_split_ranges(m, specs):
     """Grouped prefill-sized calls whose long reductions are cut into ranges
     combined through the plan's scratch slots (odd chunk counts, partial row
