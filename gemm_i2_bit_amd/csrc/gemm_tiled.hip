@@ -258,6 +258,7 @@ struct TileState {
   v4i wreg[C::kRegW ? C::NS : 1][2];  // register ring of weight words
   v16i acc[2][C::NB];
   int tsum_part;
+  float sav[C::NB];  // activation scale of the lane's token in each tile
 };
 
 // Loads of stage st into ring slot S: activation loads, then the wave's two
@@ -340,7 +341,7 @@ __device__ __forceinline__ void store_direct(const Desc& d,
   for (int i = 0; i < C::NB; ++i) {
     const int tok = tok0 + 32 * ((i + wave) % C::NB) + li;
     if (tok >= d.m) continue;
-    const float sa = *((gcfloat_ptr)d.sa + tok);
+    const float sa = x.sav[i];
 #pragma unroll
     for (int r2 = 0; r2 < 2; ++r2)
 #pragma unroll
@@ -413,8 +414,7 @@ __device__ __forceinline__ void store_tile(const Desc& d, const TileState<C>& x,
     for (int i = 0; i < NB; ++i) {
       const int tl0 = 32 * ((i + wave) % NB);  // first token of this tile
       const int tok = tok0 + tl0 + li;
-      const float sa =
-          pass_acc == 0 && tok < d.m ? *((gcfloat_ptr)d.sa + tok) : 0.0f;
+      const float sa = x.sav[i];
 #pragma unroll
       for (int p = 0; p < 32 / TP; ++p) {
         // lanes of tokens p TP .. p TP + TP - 1 write their rows
@@ -573,6 +573,14 @@ __device__ __forceinline__ void run_tile(const Desc& d, int rt, int tt,
 #pragma unroll
     for (int i = 0; i < NB; ++i) x.acc[r2][i] = v16i{0};
   x.tsum_part = 0;
+  // the epilogue's activation scales, requested now so that the end of the
+  // tile does not wait for them (older than every load of the ring, so the
+  // ring's wait counts are unchanged)
+#pragma unroll
+  for (int i = 0; i < NB; ++i) {
+    const int tok = tok0 + 32 * ((i + wave) % NB) + li;
+    x.sav[i] = tok < d.m ? *((gcfloat_ptr)d.sa + tok) : 0.0f;
+  }
 
   // Prologue: stages 0 .. NS-2 in flight.  Every stage issues one more (past
   // the end they read out of range or unused rows and are never consumed),
