@@ -73,30 +73,92 @@ __device__ __forceinline__ int wave_sum(int v) {
          __builtin_amdgcn_readlane(v, 32) + __builtin_amdgcn_readlane(v, 48);
 }
 
-// Index of the last problem whose first chunk is <= pos (chunk0 ascending).
-// Every lane reads 4 entries per round, so up to 256 problems take a single
-// memory round trip.
-__device__ __forceinline__ int find_problem(const int64_t* chunk0, int count,
-                                            int64_t pos) {
+// Index of the last problem whose first chunk is <= pos (chunk0 ascending),
+// with what a wave needs to start streaming it.  Every lane reads 4 entries
+// per round, so up to 256 problems take a single memory round trip; in the
+// first round each lane also reads its entries' weight and activation
+// pointers and shape, so that the wave's first loads do not wait for a
+// second, dependent descriptor read.
+struct ProbStart {
+  int p;
+  bool have;  // the fields below are filled (the problem is among the first
+              // 256)
+  int kc, nblk;
+  int64_t chunk0;
+  const uint8_t* w;
+  const void* x;  // int8 (xq) or, for fused plans, fp32 (xf) activations
+};
+
+// Lane l's 64-bit value (the readlane builtin moves 32 bits).
+__device__ __forceinline__ int64_t read64(int64_t v, int l) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, l);
+  const uint32_t hi =
+      (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)((uint64_t)v >> 32), l);
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+template <bool FUSED>
+__device__ __forceinline__ ProbStart find_problem(const Desc* descs,
+                                                  const int64_t* chunk0,
+                                                  int count, int64_t pos) {
   const int lane = threadIdx.x & 63;
   int p = 0;
-  for (int base = 0; base < count; base += 256) {
-    int64_t v[4];
+  int64_t v[4];
+  const uint8_t* wp[4];
+  const void* xp[4];
+  int kc[4], nb[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int i = u * 64 + lane;
+    const bool ok = i < count;
+    const Desc& d = descs[ok ? i : 0];
+    v[u] = ok ? chunk0[i] : INT64_MAX;
+    wp[u] = d.w;
+    xp[u] = FUSED ? (const void*)d.xf : (const void*)d.xq;
+    kc[u] = d.kc;
+    nb[u] = d.nblk;
+  }
+  bool more = true;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const uint64_t mask = __ballot(v[u] <= pos);
+    p += __popcll(mask);
+    more = more && mask == ~0ull;
+  }
+  ProbStart r;
+  r.have = !more || count <= 256;
+  for (int base = 256; more && base < count; base += 256) {
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int i = base + u * 64 + lane;
       v[u] = i < count ? chunk0[i] : INT64_MAX;
     }
-    bool more = true;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const uint64_t mask = __ballot(v[u] <= pos);
       p += __popcll(mask);
       more = more && mask == ~0ull;
     }
-    if (!more) break;
   }
-  return __builtin_amdgcn_readfirstlane(p - 1);
+  r.p = __builtin_amdgcn_readfirstlane(p - 1);
+  r.w = nullptr;
+  r.x = nullptr;
+  r.kc = r.nblk = 0;
+  r.chunk0 = 0;
+  if (r.have) {
+    const int u = r.p >> 6, l = r.p & 63;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (j == u) {
+        r.kc = __builtin_amdgcn_readlane(kc[j], l);
+        r.nblk = __builtin_amdgcn_readlane(nb[j], l);
+        r.chunk0 = read64(v[j], l);
+        r.w = (const uint8_t*)read64((int64_t)wp[j], l);
+        r.x = (const void*)read64((int64_t)xp[j], l);
+      }
+    }
+  }
+  return r;
 }
 
 template <int TOK>
@@ -576,27 +638,45 @@ __device__ __forceinline__ void stream_range(Stream<TOK, FUSED>& st,
   if (lo >= hi) return;
   st.lo = lo;
   st.hi = hi;
-  int p = find_problem(chunk0s, count, lo);
+  const ProbStart ps = find_problem<FUSED>(descs, chunk0s, count, lo);
+  int p = ps.p;
   int64_t pos = lo;
+  bool first = ps.have;
   while (pos < hi && p < count) {
     const Desc& d = descs[p];
-    st.w = d.w;
-    st.xq = d.xq;
-    st.xf = (gcfloat_ptr)d.xf;
+    int64_t chunks;
+    if (first) {
+      // start from the lookup's fields; the rest of the descriptor is read
+      // alongside the first loads and used only after them
+      st.w = ps.w;
+      if constexpr (FUSED)
+        st.xf = (gcfloat_ptr)ps.x;
+      else
+        st.xq = (const int8_t*)ps.x;
+      st.kc = ps.kc;
+      st.k = ps.kc * 64;
+      st.chunk0 = ps.chunk0;
+      chunks = (int64_t)ps.nblk * ps.kc;
+      first = false;
+    } else {
+      st.w = d.w;
+      st.xq = d.xq;
+      st.xf = (gcfloat_ptr)d.xf;
+      st.kc = d.kc;
+      st.k = d.k;
+      st.chunk0 = d.chunk0;
+      chunks = (int64_t)d.nblk * d.kc;
+    }
     st.sa = (const_fptr)d.sa;
     st.y = (gfloat_ptr)d.y;
     st.accout = (gint_ptr)d.acc;
     st.sw = d.sw;
     st.n = d.n;
-    st.k = d.k;
-    st.kc = d.kc;
     st.blk0 = d.blk0;
-    st.chunk0 = d.chunk0;
-    const int64_t chunks = (int64_t)d.nblk * d.kc;
-    const int64_t s0 = pos - d.chunk0;
-    const int64_t s1 = min(chunks, hi - d.chunk0);
+    const int64_t s0 = pos - st.chunk0;
+    const int64_t s1 = min(chunks, hi - st.chunk0);
     st.segment((int)s0, (int)s1);
-    pos = d.chunk0 + s1;
+    pos = st.chunk0 + s1;
     ++p;
   }
 }
