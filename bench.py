@@ -36,6 +36,7 @@ INT8_PEAK_TOPS = 5000.0        # MI355X dense int8 matrix peak
 WORKLOADS = {
     "decode_2b_m1": lambda: wl.decode_2b(1),
     "decode_2b_m2": lambda: wl.decode_2b(2),
+    "decode_2b_m3": lambda: wl.decode_2b(3),
     "decode_2b_m4": lambda: wl.decode_2b(4),
     "decode_2b_m8": lambda: wl.decode_2b(8),
     "decode_2b_m16": lambda: wl.decode_2b(16),

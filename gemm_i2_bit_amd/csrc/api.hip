@@ -136,13 +136,12 @@ std::vector<Split> plan_splits(const bt_problem* probs, int32_t count,
 // reduction range) first, so that the longest units start early and the
 // launch ends on short ones.
 std::vector<Unit> plan_units(const bt_problem* probs, int32_t count, int m,
-                             const std::vector<Split>& split) {
+                             int kind, const std::vector<Split>& split) {
   std::vector<int32_t> order(count);
   for (int32_t i = 0; i < count; ++i) order[i] = i;
   std::stable_sort(order.begin(), order.end(), [&](int32_t a, int32_t b) {
     return split[a].len > split[b].len;
   });
-  const int kind = bt::plan_kind(m);
   std::vector<Unit> units;
   for (int32_t p : order) {
     const int64_t per = bt::kind_units(kind, probs[p].n, m) * split[p].nsplit;
@@ -151,15 +150,23 @@ std::vector<Unit> plan_units(const bt_problem* probs, int32_t count, int m,
   return units;
 }
 
+// 1 KiB chunks of packed weights over every problem of a group.
+int64_t group_chunks(const bt_problem* probs, int32_t count) {
+  int64_t chunks = 0;
+  for (int32_t i = 0; i < count; ++i)
+    chunks += (probs[i].n + 63) / 64 * (probs[i].k / 64);
+  return chunks;
+}
+
 // Plan image layout (see PlanHeader).  Offsets are 256-byte aligned.
-PlanHeader plan_layout(const bt_problem* probs, int32_t count) {
+PlanHeader plan_layout(const bt_problem* probs, int32_t count, bool fused) {
   PlanHeader h;
   memset(&h, 0, sizeof(h));
   const int m = probs[0].m;
   h.magic = bt::kPlanMagic;
   h.count = count;
   h.m = m;
-  h.kind = bt::plan_kind(m);
+  h.kind = bt::group_kind(m, group_chunks(probs, count), fused);
   const std::vector<Split> split = plan_splits(probs, count, h.kind);
   int64_t blocks = 0, chunks = 0, units = 0, slots = 0, regions = 0;
   for (int32_t i = 0; i < count; ++i) {
@@ -192,7 +199,7 @@ PlanHeader plan_layout(const bt_problem* probs, int32_t count) {
   return h;
 }
 
-int32_t check_group(const bt_problem* probs, int32_t count) {
+int32_t check_group(const bt_problem* probs, int32_t count, bool fused) {
   if (!probs) return BT_E_NULL;
   if (count < 1 || count > (1 << 20)) return BT_E_ARG;
   int64_t blocks = 0;
@@ -206,7 +213,8 @@ int32_t check_group(const bt_problem* probs, int32_t count) {
   }
   // grid, scratch slots and unit indices stay within 32-bit ranges
   if (blocks * ((probs[0].m + 31) / 32) >= INT32_MAX / 64) return BT_E_SHAPE;
-  const int kind = bt::plan_kind(probs[0].m);
+  const int kind =
+      bt::group_kind(probs[0].m, group_chunks(probs, count), fused);
   if (kind != bt::kKindDot4) {
     const std::vector<Split> split = plan_splits(probs, count, kind);
     int64_t units = 0;
@@ -305,10 +313,17 @@ int32_t bt_gemv(const uint8_t* packed, float s_w, int64_t n, int64_t k,
   return bt_gemm(packed, s_w, n, k, 1, x_q, s_a, y, acc, stream);
 }
 
-int64_t bt_grouped_plan_bytes(const bt_problem* probs, int32_t count) {
-  const int32_t st = check_group(probs, count);
+// Size of the plan image of a group (fused: the problems give fp32
+// activations), or a negative status.
+static int64_t plan_bytes_of(const bt_problem* probs, int32_t count,
+                             bool fused) {
+  const int32_t st = check_group(probs, count, fused);
   if (st != BT_OK) return st;
-  return plan_layout(probs, count).bytes;
+  return plan_layout(probs, count, fused).bytes;
+}
+
+int64_t bt_grouped_plan_bytes(const bt_problem* probs, int32_t count) {
+  return plan_bytes_of(probs, count, false);
 }
 
 // Builds a grouped plan image; with xf, the problems give fp32 activations
@@ -316,9 +331,10 @@ int64_t bt_grouped_plan_bytes(const bt_problem* probs, int32_t count) {
 static int32_t build_plan(const bt_problem* probs, int32_t count, void* plan,
                           int64_t plan_bytes, const float* const* xf) {
   if (!plan) return BT_E_NULL;
-  const int32_t st = check_group(probs, count);
+  const bool fused = xf != nullptr;
+  const int32_t st = check_group(probs, count, fused);
   if (st != BT_OK) return st;
-  const PlanHeader h = plan_layout(probs, count);
+  const PlanHeader h = plan_layout(probs, count, fused);
   if (plan_bytes < h.bytes) return BT_E_ARG;
   unsigned char* out = static_cast<unsigned char*>(plan);
   memset(out, 0, (size_t)h.bytes);  // scratch area starts at zero
@@ -356,7 +372,8 @@ static int32_t build_plan(const bt_problem* probs, int32_t count, void* plan,
     blk0 += d.nblk;
   }
   if (h.kind != bt::kKindDot4) {
-    const std::vector<Unit> units = plan_units(probs, count, h.m, split);
+    const std::vector<Unit> units =
+        plan_units(probs, count, h.m, h.kind, split);
     memcpy(out + h.unit_off, units.data(), units.size() * sizeof(Unit));
   }
   return BT_OK;
@@ -390,7 +407,7 @@ int64_t bt_grouped_plan_f32_bytes(const bt_problem_f32* probs, int32_t count) {
   std::vector<bt_problem> q;
   const int32_t st = as_problems(probs, count, q);
   if (st != BT_OK) return st;
-  return bt_grouped_plan_bytes(q.data(), count);
+  return plan_bytes_of(q.data(), count, true);
 }
 
 int32_t bt_grouped_plan_f32(const bt_problem_f32* probs, int32_t count,
@@ -411,7 +428,8 @@ int32_t bt_gemm_grouped(const void* plan_dev, const void* plan_host,
   memcpy(&h, plan_host, sizeof(h));
   if (h.magic != bt::kPlanMagic || h.count < 1 || h.blocks < 1 ||
       h.total_chunks < 1 ||
-      h.m < 1 || h.m > BT_MAX_M || h.kind != bt::plan_kind(h.m) ||
+      h.m < 1 || h.m > BT_MAX_M || h.fused < 0 || h.fused > 1 ||
+      h.kind != bt::group_kind(h.m, h.total_chunks, h.fused == 1) ||
       h.desc_off != 256 ||
       h.bytes < h.scnt_off || h.scnt_off < h.sacc_off ||
       h.sacc_off < h.unit_off || h.unit_off < h.chunk_off ||

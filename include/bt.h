@@ -150,10 +150,15 @@ typedef struct bt_problem {
  * bt_gemm_grouped(plan_dev, plan_host, s) as often as wanted.  The plan holds
  * the problem descriptors (pointers, shapes, scales), the work order and a
  * scratch area through which workgroups that share part of the work combine
- * their partial sums: for m <= 4, m * 512 bytes per 64-row block; for m > 4,
- * per-range regions and arrival counters for problems whose reduction is
- * split.  The counters and slots are zero in the host image and every
- * complete launch leaves them zero.
+ * their partial sums: with packed dot products, m * 512 bytes per 64-row
+ * block; on the matrix cores, per-range regions and arrival counters for
+ * problems whose reduction is split.  The counters and slots are zero in the
+ * host image and every complete launch leaves them zero.
+ * Kernel choice: m = 1 and 2 stream the weights through packed dot products;
+ * so do m = 3 and 4 in plans of fewer than 32768 chunks (32 MiB of packed
+ * weights), while larger plans at m = 3, 4 and every plan at m > 4 use the
+ * int8 matrix cores (at m = 3, 4 the dot products of a large plan are bound
+ * by the vector ALUs, not by the weight stream).
  * Hence launches that use one plan must not overlap (use one plan per
  * stream); rebuild the plan when any pointer, shape or scale changes.
  * plan_host must stay a byte-identical copy of the host image written by

@@ -365,3 +365,32 @@ def test_grouped_plan_f32_errors(L):
     arr = problems_f32([(64, 64, 1)])
     assert L.bt_grouped_plan_f32(arr, 1, None, img.size) == bt.BT_E_NULL
     assert L.bt_grouped_plan_f32(arr, 1, img.ctypes.data, 16) == bt.BT_E_ARG
+
+
+def test_grouped_plan_kind_by_m_and_size(L):
+    """m = 1, 2 stream; m = 3, 4 stream for small plans and use the matrix
+    cores from 32768 chunks on; fused plans always stream."""
+    def kind(specs, f32=False):
+        arr = (problems_f32 if f32 else problems)(specs)
+        nb = (L.bt_grouped_plan_f32_bytes if f32
+              else L.bt_grouped_plan_bytes)(arr, len(specs))
+        assert nb > 0
+        img = np.zeros(nb, np.uint8)
+        build = L.bt_grouped_plan_f32 if f32 else L.bt_grouped_plan
+        assert build(arr, len(specs), img.ctypes.data, nb) == 0
+        p = parse_plan(img)
+        return p["kind"], p["total_chunks"], p["fused"]
+
+    big = [(8192, 16384)] * 2         # 2 x 128 x 256 = 65536 chunks
+    edge = [(4096, 8192)]             # 64 x 128 = 8192 chunks
+    for m in (1, 2):
+        assert kind([(n, k, m) for n, k in big])[0] == 0
+    for m in (3, 4):
+        assert kind([(n, k, m) for n, k in big]) == (1, 65536, 0)
+        assert kind([(n, k, m) for n, k in edge])[0] == 0
+        assert kind([(n, k, m) for n, k in edge * 4]) == (1, 32768, 0)
+        assert kind([(n, k, m) for n, k in edge * 3])[0] == 0
+        # fused: rows of at most 16384 / m inputs, always the streaming kind
+        k = 16384 // m // 64 * 64
+        assert kind([(65536, k, m)], f32=True) == (0, 1024 * (k // 64), 1)
+    assert kind([(64, 64, 5)])[0] == 1
