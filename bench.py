@@ -255,6 +255,52 @@ def run_chain(cs: ChainSet, tokens: int, warmup: int, torch):
     return eager, graph
 
 
+def lut_ablation(torch, bt, reps=30):
+    """Single-token products with dot products (bt_gemv) and with lookup
+    tables (bt_gemv_lut) on random packed weights: microseconds per call,
+    averaged over back-to-back calls replayed from a HIP graph (so that the
+    host's call rate does not set the time)."""
+    dev = torch.device("cuda:0")
+    shapes = [(2560, 2560), (6912, 2560), (2560, 6912), (131072, 4096)]
+    out = {}
+    for n, k in shapes:
+        valid = torch.tensor([b for b in range(256)
+                              if all((b >> (2 * j)) & 3 != 3 for j in range(4))],
+                             dtype=torch.uint8, device=dev)  # no code 3
+        packed = valid[torch.randint(0, valid.numel(),
+                                     (bt.bt_packed_bytes(n, k),), device=dev)]
+        x_q = torch.randint(-127, 128, (k,), dtype=torch.int8, device=dev)
+        s_a = torch.ones(1, device=dev)
+        y = torch.empty((1, n), device=dev)
+        res = {}
+        for name, fn in (("dot4_us", bt.bt_gemv), ("lut_us", bt.bt_gemv_lut)):
+            side = torch.cuda.Stream()
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):
+                for _ in range(3):
+                    fn(packed, 0.02, n, k, x_q, s_a, y=y)
+            torch.cuda.current_stream().wait_stream(side)
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for _ in range(reps):
+                    fn(packed, 0.02, n, k, x_q, s_a, y=y)
+            g.replay()
+            torch.cuda.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            res[name] = round(e0.elapsed_time(e1) / reps * 1e3, 2)
+            del g
+        res["weight_bytes"] = packed.numel()
+        out[f"{n}x{k}"] = res
+        del packed
+    return out
+
+
 def run_timed(ws: WorkSet, steps: int, warmup: int, torch):
     """Time `steps` whole steps (quantize + product); then time the product
     kernel alone over `steps` back-to-back launches (HIP events on the
@@ -437,6 +483,7 @@ def main():
                 del cs
                 torch.cuda.empty_cache()
             out["chained_decode"] = chained
+            out["lut_ablation"] = lut_ablation(torch, bt)
 
     if args.calibrate_copy:
         n = 256 << 20

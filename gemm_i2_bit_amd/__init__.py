@@ -77,6 +77,8 @@ def lib() -> ctypes.CDLL:
         L.bt_quant_act_many.restype = i32
         L.bt_gemv.argtypes = [p, f32, i64, i64, p, p, p, p, p]
         L.bt_gemv.restype = i32
+        L.bt_gemv_lut.argtypes = [p, f32, i64, i64, p, p, p, p, p]
+        L.bt_gemv_lut.restype = i32
         L.bt_gemm.argtypes = [p, f32, i64, i64, i64, p, p, p, p, p]
         L.bt_gemm.restype = i32
         L.bt_grouped_plan_bytes.argtypes = [p, i32]
@@ -241,6 +243,24 @@ def bt_gemv(packed, s_w, n: int, k: int, x_q, s_a, y=None, acc=None,
                          _dev(y, torch.float32, "y"),
                          _dev(acc, torch.int32, "acc"), _stream(stream)),
            "bt_gemv")
+    return y, acc
+
+
+def bt_gemv_lut(packed, s_w, n: int, k: int, x_q, s_a, y=None, acc=None,
+                want_acc: bool = False, stream=None):
+    """bt_gemv computed with lookup tables (for comparison)."""
+    torch = _torch()
+    if x_q.numel() != k or s_a.numel() != 1:
+        raise ValueError("x_q or s_a has the wrong size")
+    if packed.numel() != bt_packed_bytes(n, k):
+        raise ValueError("packed has the wrong size")
+    y, acc = _outputs(1, n, x_q.device, y, acc, want_acc)
+    _check(lib().bt_gemv_lut(_dev(packed, torch.uint8, "packed"), float(s_w),
+                             n, k, _dev(x_q, torch.int8, "x_q"),
+                             _dev(s_a, torch.float32, "s_a"),
+                             _dev(y, torch.float32, "y"),
+                             _dev(acc, torch.int32, "acc"), _stream(stream)),
+           "bt_gemv_lut")
     return y, acc
 
 

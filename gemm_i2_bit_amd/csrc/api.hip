@@ -313,6 +313,17 @@ int32_t bt_gemv(const uint8_t* packed, float s_w, int64_t n, int64_t k,
   return bt_gemm(packed, s_w, n, k, 1, x_q, s_a, y, acc, stream);
 }
 
+int32_t bt_gemv_lut(const uint8_t* packed, float s_w, int64_t n, int64_t k,
+                    const int8_t* x_q, const float* s_a, float* y,
+                    int32_t* acc, void* stream) {
+  const int32_t st = check_problem(packed, s_w, n, k, 1, x_q, s_a, y, acc);
+  if (st != BT_OK) return st;
+  const int32_t arch = check_arch();
+  if (arch != BT_OK) return arch;
+  const Desc d = make_desc(packed, s_w, n, k, 1, x_q, s_a, y, acc);
+  return hip_status(bt::launch_lut(d, static_cast<hipStream_t>(stream)));
+}
+
 // Size of the plan image of a group (fused: the problems give fp32
 // activations), or a negative status.
 static int64_t plan_bytes_of(const bt_problem* probs, int32_t count,

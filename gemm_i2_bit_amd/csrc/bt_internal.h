@@ -127,6 +127,7 @@ constexpr int kMaxQuantJobs = BT_MAX_QUANT_JOBS;
 hipError_t launch_quant_many(const bt_quant_job* jobs, int32_t count,
                              hipStream_t s);
 hipError_t launch_dot4(const Desc& d, hipStream_t s);
+hipError_t launch_lut(const Desc& d, hipStream_t s);  // m = 1 only
 hipError_t launch_stream_grouped(const Desc* descs, const int64_t* chunk0,
                                  int32_t count, int64_t total_chunks, int m,
                                  int32_t* sacc, int workgroups, bool fused,

@@ -116,6 +116,16 @@ int32_t bt_gemv(const uint8_t* packed, float s_w, int64_t n, int64_t k,
                 const int8_t* x_q, const float* s_a, float* y, int32_t* acc,
                 void* stream);
 
+/* The same product as bt_gemv (same arguments, rules and results, bit for
+ * bit), computed with lookup tables instead of dot products: the table
+ * method of the CPU kernels in "BitNet 1 位 LLM 独立推理引擎：位串行 GEMM 内核
+ * 与 LUT 优化工程实践" (body: TL1 turns two weights into a 4-bit index into
+ * precomputed tables of their ternary combinations).  Kept for comparison
+ * only: on gfx950 it is slower than bt_gemv. */
+int32_t bt_gemv_lut(const uint8_t* packed, float s_w, int64_t n, int64_t k,
+                    const int8_t* x_q, const float* s_a, float* y,
+                    int32_t* acc, void* stream);
+
 /* Ternary matrix product: acc[i, r] = sum_k trit(r, k) * x_q[i, k] (exact
  * int32) and y[i, r] = ((float)acc[i, r] * s_w) * s_a[i].
  *  packed  bt_packed_bytes(n, k) bytes from bt_pack_i2s, device, 16-aligned.

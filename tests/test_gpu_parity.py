@@ -251,6 +251,33 @@ def test_gemv_entry_matches_gemm():
     np.testing.assert_array_equal(a1.cpu().numpy(), acc_r)
 
 
+@pytest.mark.parametrize("n,k", [(200, 192), (64, 64), (130, 2560),
+                                 (70, 6912), (66, 65536)])
+def test_gemv_lut_matches_oracle(n, k):
+    """The lookup-table GEMV: the oracle's accumulators exactly (all +1, all
+    -1 and zero rows against all-127 activations at the largest k), and the
+    dot-product GEMV's outputs bit for bit."""
+    rng = np.random.default_rng([112, n, k])
+    t = wl.trits(rng, (n, k), wl.DECODE_2B)
+    x = wl.x_normal_outliers(rng, (1, k))
+    if k == 65536:
+        t[0], t[1], t[2] = 1, -1, 0
+        x[0] = 1.0
+    s_w = wl.scale(rng, 0.01, 0.05)
+    packed = bt.bt_pack_i2s(dev(t))
+    x_q, s_a = bt.bt_quant_act(dev(x))
+    y1, a1 = bt.bt_gemv_lut(packed, s_w, n, k, x_q[0], s_a, want_acc=True)
+    y2, a2 = bt.bt_gemv(packed, s_w, n, k, x_q[0], s_a, want_acc=True)
+    torch.cuda.synchronize()
+    _, _, _, acc_r, y_r = oracle_product(t, x, s_w)
+    np.testing.assert_array_equal(a1.cpu().numpy(), acc_r)
+    check_y(y1.cpu().numpy(), y_r, acc_r)
+    assert torch.equal(a1, a2) and torch.equal(y1, y2)
+    if k == 65536:
+        assert acc_r[0, 0] == 127 * k and acc_r[0, 1] == -127 * k
+        assert acc_r[0, 2] == 0
+
+
 # ------------------------------------------------------------ grouped calls
 def grouped_case(work, layers):
     """Upload, pack and quantize `layers` layers of a workload; return the
