@@ -389,7 +389,11 @@ def main():
                     choices=["grouped", "per-launch", "fused"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true",
-                    help="skip the M=512 prefill figure")
+                    help="skip the M=512 prefill, chained-decode and "
+                         "lookup-table figures")
+    ap.add_argument("--no-chain", action="store_true",
+                    help="skip the chained-decode and lookup-table figures "
+                         "(keeps the M=512 prefill figure)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one plain 256 MiB device copy, so that a "
@@ -469,7 +473,7 @@ def main():
             "frac_int8_peak": round(tops_k / INT8_PEAK_TOPS, 4)}
         del pws
         torch.cuda.empty_cache()
-        if work.name.startswith("decode_2b_m1"):
+        if work.name.startswith("decode_2b_m1") and not args.no_chain:
             chained = {"workload": "decode_2b chained, M=1 (one token, every "
                                    "dependency kept)"}
             for fused in (False, True):
