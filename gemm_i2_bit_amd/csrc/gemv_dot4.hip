@@ -11,16 +11,18 @@
 // so raw 2-bit codes feed v_dot4 directly and one activation sum per token is
 // subtracted at the end.
 //
-// Single-problem mapping (gfx950, wave64): a workgroup of 4 waves owns one
-// 64-row block;
-// lane l of every wave owns row 64 b + l, and the 4 waves split the block's
-// 16-byte chunks (64 inputs each) into 4 contiguous ranges.  For a chunk, the
+// Single-problem mapping (gfx950, wave64): a workgroup of WAVES waves owns
+// one 64-row block; lane l of every wave owns row 64 b + l, and the waves
+// split the block's 16-byte chunks (64 inputs each) into WAVES contiguous
+// ranges.  WAVES grows with the reduction (4, 8 or 16 waves, at least 4
+// chunks each) so that a matrix with few, long rows still puts enough loads
+// in flight: 2560 x 6912 has only 40 row blocks.  For a chunk, the
 // 64 lanes read one contiguous KiB (one 128-bit load each) and all need the
 // same 64 activation bytes per token, which are wave-uniform and live in
 // scalar registers.  Within a 32-bit word of codes, the four 2-bit fields are
 // masked in place: field j holds 4^j * code, so each field has its own int32
 // accumulator and the fields are combined with exact shifts at the end.
-// Partial sums of the 4 waves meet in LDS; wave 0 applies the rescale.
+// Partial sums of the waves meet in LDS; wave 0 applies the rescale.
 // Grouped calls use the persistent streaming kernel instead.
 #include "bt_internal.h"
 
@@ -39,7 +41,7 @@ __device__ __forceinline__ int wave_sum(int v) {
   return v;
 }
 
-template <int TOK>
+template <int TOK, int WAVES>
 __device__ __forceinline__ void dot4_block(const Desc& d, int rb,
                                            int (*red)[TOK][64]) {
   const int lane = threadIdx.x & 63;
@@ -48,8 +50,8 @@ __device__ __forceinline__ void dot4_block(const Desc& d, int rb,
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int k = d.k;
   const int kc = k >> 6;
-  const int c0 = (kc * wave) >> 2;
-  const int c1 = (kc * (wave + 1)) >> 2;
+  const int c0 = kc * wave / WAVES;
+  const int c1 = kc * (wave + 1) / WAVES;
   const int kq = k >> 2;  // activation row length in 32-bit words
 
   const v4u* wp =
@@ -99,8 +101,9 @@ __device__ __forceinline__ void dot4_block(const Desc& d, int rb,
     if (row < d.n) {
 #pragma unroll
       for (int t = 0; t < TOK; ++t) {
-        const int acc = red[0][t][lane] + red[1][t][lane] + red[2][t][lane] +
-                        red[3][t][lane];
+        int acc = 0;
+#pragma unroll
+        for (int w = 0; w < WAVES; ++w) acc += red[w][t][lane];
         const size_t o = (size_t)t * d.n + row;
         if (d.acc != nullptr) d.acc[o] = acc;
         d.y[o] = __fmul_rn(__fmul_rn((float)acc, d.sw), d.sa[t]);
@@ -109,24 +112,32 @@ __device__ __forceinline__ void dot4_block(const Desc& d, int rb,
   }
 }
 
-template <int TOK>
-__global__ __launch_bounds__(256) void dot4_kernel(Desc d) {
-  __shared__ int red[4][TOK][64];
-  dot4_block<TOK>(d, blockIdx.x, red);
+template <int TOK, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void dot4_kernel(Desc d) {
+  __shared__ int red[WAVES][TOK][64];
+  dot4_block<TOK, WAVES>(d, blockIdx.x, red);
+}
+
+template <int WAVES>
+hipError_t launch_waves(const Desc& d, hipStream_t s) {
+  const dim3 grid((unsigned)d.nblk), block(64 * WAVES);
+  switch (d.m) {
+    case 1: dot4_kernel<1, WAVES><<<grid, block, 0, s>>>(d); break;
+    case 2: dot4_kernel<2, WAVES><<<grid, block, 0, s>>>(d); break;
+    case 3: dot4_kernel<3, WAVES><<<grid, block, 0, s>>>(d); break;
+    case 4: dot4_kernel<4, WAVES><<<grid, block, 0, s>>>(d); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_dot4(const Desc& d, hipStream_t s) {
-  const dim3 grid((unsigned)d.nblk), block(256);
-  switch (d.m) {
-    case 1: dot4_kernel<1><<<grid, block, 0, s>>>(d); break;
-    case 2: dot4_kernel<2><<<grid, block, 0, s>>>(d); break;
-    case 3: dot4_kernel<3><<<grid, block, 0, s>>>(d); break;
-    case 4: dot4_kernel<4><<<grid, block, 0, s>>>(d); break;
-    default: return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
+  // at least 4 chunks per wave
+  if (d.kc >= 64) return launch_waves<16>(d, s);
+  if (d.kc >= 32) return launch_waves<8>(d, s);
+  return launch_waves<4>(d, s);
 }
 
 }  // namespace bt
