@@ -126,6 +126,14 @@ hipError_t launch_quant(const float* x, int64_t m, int64_t k, int8_t* xq,
 constexpr int kMaxQuantJobs = BT_MAX_QUANT_JOBS;
 hipError_t launch_quant_many(const bt_quant_job* jobs, int32_t count,
                              hipStream_t s);
+// Waves per 64-row block of the single-problem kernels: enough for about
+// 2048 waves in all (8 per CU) when the matrix has few row blocks, at least
+// 4 chunks of 64 inputs per wave, and 4, 8 or 16 waves.
+inline int row_block_waves(int64_t nblk, int kc) {
+  int w = 4;
+  while (w < 16 && nblk * w < 2048 && kc >= 4 * (2 * w)) w *= 2;
+  return w;
+}
 hipError_t launch_dot4(const Desc& d, hipStream_t s);
 hipError_t launch_lut(const Desc& d, hipStream_t s);  // m = 1 only
 hipError_t launch_stream_grouped(const Desc* descs, const int64_t* chunk0,

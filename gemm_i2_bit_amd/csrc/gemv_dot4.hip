@@ -14,9 +14,9 @@
 // Single-problem mapping (gfx950, wave64): a workgroup of WAVES waves owns
 // one 64-row block; lane l of every wave owns row 64 b + l, and the waves
 // split the block's 16-byte chunks (64 inputs each) into WAVES contiguous
-// ranges.  WAVES grows with the reduction (4, 8 or 16 waves, at least 4
-// chunks each) so that a matrix with few, long rows still puts enough loads
-// in flight: 2560 x 6912 has only 40 row blocks.  For a chunk, the
+// ranges.  A matrix with few row blocks gets more waves per block (4, 8 or
+// 16, at least 4 chunks each), so that it still puts enough loads in flight:
+// 2560 x 6912 has only 40 row blocks.  For a chunk, the
 // 64 lanes read one contiguous KiB (one 128-bit load each) and all need the
 // same 64 activation bytes per token, which are wave-uniform and live in
 // scalar registers.  Within a 32-bit word of codes, the four 2-bit fields are
@@ -134,10 +134,11 @@ hipError_t launch_waves(const Desc& d, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_dot4(const Desc& d, hipStream_t s) {
-  // at least 4 chunks per wave
-  if (d.kc >= 64) return launch_waves<16>(d, s);
-  if (d.kc >= 32) return launch_waves<8>(d, s);
-  return launch_waves<4>(d, s);
+  switch (row_block_waves(d.nblk, d.kc)) {
+    case 16: return launch_waves<16>(d, s);
+    case 8: return launch_waves<8>(d, s);
+    default: return launch_waves<4>(d, s);
+  }
 }
 
 }  // namespace bt

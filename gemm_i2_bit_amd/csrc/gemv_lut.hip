@@ -11,16 +11,17 @@
 // the index is read straight from the packed weights: index = c0 + 4 c1 with
 // codes c = trit + 1, 9 of its 16 values reachable.
 //
-// Mapping (wave64): a workgroup of 4 waves owns one 64-row block, lane l of
-// every wave owns row 64 b + l, and the waves split the block's chunks into
-// 4 contiguous ranges (as the dot-product kernel does).  A wave walks its
-// range in tiles of 2 chunks (128 inputs, 64 pairs): lane p first writes the
-// 16 table entries (c0 - 1) x[k0] + (c1 - 1) x[k1] of pair p into the wave's
-// LDS table, then every lane adds, for each of the 64 pairs, the entry its
-// row's index selects.  Entry e of pair p sits at e * 66 + p (16-bit): 66
+// Mapping (wave64): a workgroup of 4, 8 or 16 waves owns one 64-row block,
+// lane l of every wave owns row 64 b + l, and the waves split the block's
+// chunks into contiguous ranges (as the dot-product kernel does, with the
+// same number of waves).  A wave walks its range in tiles of 2 chunks (128
+// inputs, 64 pairs): lane p first writes the 16 table entries
+// (c0 - 1) x[k0] + (c1 - 1) x[k1] of pair p into the wave's LDS table, then
+// every lane adds, for each of the 64 pairs, the entry its row's index
+// selects.  Entry e of pair p sits at e * 66 + p (16-bit): 66
 // entries span 33 banks, so the 16 indices of one pair fall in 16 different
 // banks and the lanes' reads of one pair never conflict.  The sums are exact
-// int32; the 4 waves' partials meet in LDS and wave 0 applies the rescale.
+// int32; the waves' partials meet in LDS and wave 0 applies the rescale.
 #include "bt_internal.h"
 
 namespace bt {
@@ -29,19 +30,19 @@ namespace {
 typedef unsigned v4u __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) int16_t* lds_i16_ptr;
 
-constexpr int kTilePairs = 64;  // 2 chunks of 64 inputs
 constexpr int kStride = 66;     // 16-bit entries between two indices
 
-__global__ __launch_bounds__(256) void lut_kernel(Desc d) {
-  __shared__ int16_t table[4][16 * kStride];
-  __shared__ int red[4][64];
+template <int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void lut_kernel(Desc d) {
+  __shared__ int16_t table[WAVES][16 * kStride];
+  __shared__ int red[WAVES][64];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int rb = blockIdx.x;
   const int k = d.k;
   const int kc = k >> 6;
-  const int c0 = (kc * wave) >> 2;
-  const int c1 = (kc * (wave + 1)) >> 2;
+  const int c0 = kc * wave / WAVES;
+  const int c1 = kc * (wave + 1) / WAVES;
   const v4u* wp =
       reinterpret_cast<const v4u*>(d.w + (size_t)rb * 16 * (size_t)k) + lane;
   const lds_i16_ptr t = (lds_i16_ptr)table[wave];
@@ -85,8 +86,9 @@ __global__ __launch_bounds__(256) void lut_kernel(Desc d) {
   if (wave == 0) {
     const int row = rb * 64 + lane;
     if (row < d.n) {
-      const int total = red[0][lane] + red[1][lane] + red[2][lane] +
-                        red[3][lane];
+      int total = 0;
+#pragma unroll
+      for (int w = 0; w < WAVES; ++w) total += red[w][lane];
       if (d.acc != nullptr) d.acc[row] = total;
       d.y[row] = __fmul_rn(__fmul_rn((float)total, d.sw), d.sa[0]);
     }
@@ -97,7 +99,13 @@ __global__ __launch_bounds__(256) void lut_kernel(Desc d) {
 
 hipError_t launch_lut(const Desc& d, hipStream_t s) {
   if (d.m != 1) return hipErrorInvalidValue;
-  lut_kernel<<<dim3((unsigned)d.nblk), dim3(256), 0, s>>>(d);
+  const dim3 grid((unsigned)d.nblk);
+  // the dot-product kernel's choice of waves per row block
+  switch (row_block_waves(d.nblk, d.kc)) {
+    case 16: lut_kernel<16><<<grid, dim3(1024), 0, s>>>(d); break;
+    case 8: lut_kernel<8><<<grid, dim3(512), 0, s>>>(d); break;
+    default: lut_kernel<4><<<grid, dim3(256), 0, s>>>(d); break;
+  }
   return hipGetLastError();
 }
 
