@@ -149,18 +149,26 @@ __device__ __forceinline__ int* tsum_array() {
 // lanes x 16 bytes).  The region reuses the ring, which is idle by then.
 constexpr int kEpRow = 272;  // bytes per token in the staging region
 
-// 16 bytes per lane of one staged token row: rows 4 (lane % 16) .. + 3 of the
-// wave's block, token `tok`.  Outputs are written once and not read back by
-// the launch: non-temporal stores (measured 2 us faster on the M=512 layer).
-template <typename T>
+// 16 bytes of outputs (rows row .. row + 3 of token `tok`) from one lane.
+// Outputs are written once and not read back by the launch.  NT: a
+// non-temporal store, for the staged epilogue whose 16 lanes write a token's
+// 256 contiguous bytes at once (measured 2 us faster on the M=512 layer);
+// direct stores, which cover 32 bytes of a token per instruction, go through
+// the L2 so that the pieces of a segment merge there before they reach
+// memory (non-temporal ones were 6-9 % slower at 3 and 16 tokens).
+template <typename T, bool NT>
 __device__ __forceinline__ void store_row16(T* out, int n, int tok, int row,
                                             const int8_t* src) {
   T* dst = out + (size_t)tok * n + row;
+  typedef __attribute__((address_space(1))) v4i* gv4i_ptr;
   if ((n & 3) == 0 && row + 3 < n) {
-    __builtin_nontemporal_store(
-        *reinterpret_cast<const v4i*>(src),
-        reinterpret_cast<__attribute__((address_space(1))) v4i*>(
-            (__attribute__((address_space(1))) T*)dst));
+    const v4i v = *reinterpret_cast<const v4i*>(src);
+    const gv4i_ptr p =
+        reinterpret_cast<gv4i_ptr>((__attribute__((address_space(1))) T*)dst);
+    if constexpr (NT)
+      __builtin_nontemporal_store(v, p);
+    else
+      *p = v;
   } else {
 #pragma unroll
     for (int r = 0; r < 4; ++r)
@@ -353,10 +361,11 @@ __device__ __forceinline__ void store_direct(const Desc& d,
           a[r] = fin[r2][i][4 * g4 + r];
           v[r] = __float_as_int(__fmul_rn(__fmul_rn((float)a[r], d.sw), sa));
         }
-        store_row16(d.y, d.n, tok, row, reinterpret_cast<const int8_t*>(&v));
+        store_row16<float, false>(d.y, d.n, tok, row,
+                                  reinterpret_cast<const int8_t*>(&v));
         if (d.acc)
-          store_row16(d.acc, d.n, tok, row,
-                      reinterpret_cast<const int8_t*>(&a));
+          store_row16<int32_t, false>(d.acc, d.n, tok, row,
+                                      reinterpret_cast<const int8_t*>(&a));
       }
   }
 }
@@ -444,9 +453,9 @@ __device__ __forceinline__ void store_tile(const Desc& d, const TileState<C>& x,
           if (tk < d.m) {
             const int8_t* src = ep + t * kEpRow + 16 * (lane & 15);
             if (pass_acc == 0)
-              store_row16(d.y, d.n, tk, row, src);
+              store_row16<float, true>(d.y, d.n, tk, row, src);
             else
-              store_row16(d.acc, d.n, tk, row, src);
+              store_row16<int32_t, true>(d.acc, d.n, tk, row, src);
           }
         }
       }
