@@ -88,18 +88,22 @@ inline int plan_kind(int64_t m) {
   return m <= kDot4MaxM ? kKindDot4
                         : (m < kPrefillMinM ? kKindMfma : kKindPrefill);
 }
-// Kind of a grouped plan.  At m = 3 and 4 the packed dot products of a large
-// plan are bound by the vector ALUs (4 dot products per 16 inputs and token)
-// rather than by the weight stream, and the matrix cores are faster: 97 us
-// against 124-136 us at m = 3 and 99 us against 142-158 us at m = 4 over a
-// 521 MB decode set.  Small plans (one 17 MB layer) stay faster on the dot
-// products, whose launch starts streaming sooner.  Plans that quantize their
-// own activations always stream.
+// Kind of a grouped plan.  From 2 tokens on, the packed dot products of a
+// large plan are bound by the vector ALUs (4 dot products per 16 inputs and
+// token) rather than by the weight stream, and the matrix cores are faster
+// over a 521 MB decode set: 87 against 96-103 us at m = 2, 93 against
+// 124-136 us at m = 3, 98 against 142-158 us at m = 4.  Smaller plans stay
+// faster on the dot products, whose launch starts streaming sooner (one
+// 17 MB layer at m = 4; 87 MB at m = 2).  Plans that quantize their own
+// activations always stream.
 constexpr int64_t kSkinnyMfmaChunks = 32768;  // 32 MiB of packed weights
+constexpr int64_t kPairMfmaChunks = 131072;   // 128 MiB, for m = 2
 inline int group_kind(int64_t m, int64_t total_chunks, bool fused) {
-  if (fused || m <= 2) return plan_kind(m);
-  if (m <= kDot4MaxM)
-    return total_chunks >= kSkinnyMfmaChunks ? kKindMfma : kKindDot4;
+  if (fused || m <= 1) return plan_kind(m);
+  if (m <= kDot4MaxM) {
+    const int64_t from = m == 2 ? kPairMfmaChunks : kSkinnyMfmaChunks;
+    return total_chunks >= from ? kKindMfma : kKindDot4;
+  }
   return plan_kind(m);
 }
 // tokens per workgroup tile of the matrix-core kernels

@@ -368,8 +368,8 @@ def test_grouped_plan_f32_errors(L):
 
 
 def test_grouped_plan_kind_by_m_and_size(L):
-    """m = 1, 2 stream; m = 3, 4 stream for small plans and use the matrix
-    cores from 32768 chunks on; fused plans always stream."""
+    """m = 1 streams; m = 2 streams below 131072 chunks and m = 3, 4 below
+    32768, larger plans use the matrix cores; fused plans always stream."""
     def kind(specs, f32=False):
         arr = (problems_f32 if f32 else problems)(specs)
         nb = (L.bt_grouped_plan_f32_bytes if f32
@@ -385,6 +385,8 @@ def test_grouped_plan_kind_by_m_and_size(L):
     edge = [(4096, 8192)]             # 64 x 128 = 8192 chunks
     for m in (1, 2):
         assert kind([(n, k, m) for n, k in big])[0] == 0
+    assert kind([(n, k, 1) for n, k in big * 2])[0] == 0
+    assert kind([(n, k, 2) for n, k in big * 2]) == (1, 131072, 0)
     for m in (3, 4):
         assert kind([(n, k, m) for n, k in big]) == (1, 65536, 0)
         assert kind([(n, k, m) for n, k in edge])[0] == 0
