@@ -90,7 +90,7 @@ struct Cfg {
   static_assert(kActLoads * 1024 <= kActSlot, "slot holds every load");
   static_assert(kYounger < 64, "vmcnt range");
 };
-using CfgS32 = Cfg<32, 6, true>;
+using CfgS32 = Cfg<32, 4, true>;
 using CfgS64 = Cfg<64, 4, true>;
 using CfgP128 = Cfg<128, 3, false>;
 
