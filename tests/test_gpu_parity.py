@@ -318,11 +318,14 @@ def test_grouped_layers_match_oracle(m, layers):
             check_y(prob["y"].cpu().numpy(), y_r, acc_r)
 
 
-@pytest.mark.parametrize("m,fused", [(1, False), (4, False), (1, True)])
+@pytest.mark.parametrize("m,fused", [(1, False), (2, False), (4, False),
+                                     (8, False), (32, False), (1, True)])
 def test_decode_set_grouped_full_size(m, fused):
     """The whole 2B-shaped decode set (30 layers x 7 projections, 521 MB of
     packed weights) in one grouped launch, as the benchmark runs it, three
-    times in a row; every output of every launch against the oracle.  To
+    times in a row; every output of every launch against the oracle.  M=1
+    streams with dot products; M=2 and 4 (sets this large) and the batched
+    decode sizes M=8 and 32 run on the matrix cores.  To
     keep the host side short, the 30 layers share layer 0's seven weight
     tensors (the launch still streams 521 MB); every (layer, projection) has
     its own activations.  fused: the launch quantizes the fp32 activations
