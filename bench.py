@@ -470,7 +470,8 @@ def main():
             "product_kernel_ms": round(pk_avg, 5),
             "tops_step": round(pws.ops() / (pwall / 20) / 1e12, 2),
             "tops_kernel": round(tops_k, 2),
-            "frac_int8_peak": round(tops_k / INT8_PEAK_TOPS, 4)}
+            "frac_int8_peak": round(tops_k / INT8_PEAK_TOPS, 4),
+            "traffic": load_traffic(pw.name, sha, pws.product_bytes())}
         del pws
         torch.cuda.empty_cache()
         if work.name.startswith("decode_2b_m1") and not args.no_chain:
