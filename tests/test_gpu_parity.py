@@ -131,6 +131,7 @@ def quant_cases():
         ("quarter_steps", np.round(wl.x_normal(rng, (4, 256)) * 4) / 4),
         ("held_in_registers", wl.x_normal_outliers(rng, (2, 8192))),
         ("read_twice", wl.x_normal_outliers(rng, (2, 8256))),
+        ("read_twice_longest", wl.x_normal_outliers(rng, (1, 65536))),
     ]
 
 
