@@ -215,6 +215,15 @@ struct Stream {
   int64_t chunk0;
   // wave range (global chunks) and grid
   int64_t lo, hi;
+  // the neighbouring waves' ranges [prev_lo, lo) and [hi, next_hi), and
+  // whether they belong to this workgroup
+  int64_t prev_lo, next_hi;
+  bool prev_in_wg, next_in_wg;
+  // cut blocks shared with a neighbour of this workgroup and no one else:
+  // their partial sums meet in LDS after the stream (see stream_kernel)
+  bool head_local, tail_local;
+  int tail_rb_local;
+  int head_keep[TOK], tail_keep[TOK];
   int32_t* sacc;
   int qsum[TOK];
   float sav[TOK];    // the tokens' activation scales (read once per problem)
@@ -360,11 +369,9 @@ struct Stream {
   // it writes the output and clears the slot for the next launch.  Counting
   // chunks rather than contributors makes the hand-off independent of how
   // the stream was cut.  Integer addition is exact and order-free; no lane
-  // waits for another.  A wave has at most two such blocks per problem (the
-  // first and the last of its range); the atomics of both are issued,
-  // without a branch (a block that is not cut adds 0 to its own slot, which
-  // changes nothing), before settle looks at what either returned, so the
-  // round trips overlap.
+  // waits for another.  A wave has at most two such blocks (the first and
+  // the last of its range).  Blocks shared only by two waves of one
+  // workgroup do not come here: they meet in LDS (see stream_kernel).
   struct HandOff {
     uint64_t ret[TOK];  // what the atomics returned (slot before the add)
     int64_t delta[TOK];
@@ -377,12 +384,12 @@ struct Stream {
   }
 
   __device__ __forceinline__ void hand_off(HandOff& h, int rb,
-                                           const int (&sum)[TOK], int chunks,
-                                           bool on) const {
+                                           const int (&sum)[TOK],
+                                           int chunks) const {
     unsigned long long* sp = slot_of(rb);
 #pragma unroll
     for (int t = 0; t < TOK; ++t) {
-      h.delta[t] = on ? ((int64_t)chunks << 32) + (int64_t)sum[t] : 0;
+      h.delta[t] = ((int64_t)chunks << 32) + (int64_t)sum[t];
       h.ret[t] = atomicAdd(sp + t * 64, (unsigned long long)h.delta[t]);
     }
     h.rb = rb;
@@ -535,7 +542,7 @@ struct Stream {
   // loads); the loop's only other memory operations are LDS writes and the
   // occasional burst of a full staging area.  A row block cut by the range
   // (at most the first and the last) keeps its partial sums in registers;
-  // their atomic hand-off happens after the loop.
+  // their hand-off happens after the loop.
   __device__ __forceinline__ void segment(int s0, int s1) {
     s0 = __builtin_amdgcn_readfirstlane(s0);
     s1 = __builtin_amdgcn_readfirstlane(s1);
@@ -589,15 +596,35 @@ struct Stream {
     // were stashed only if it also ended here; otherwise it is the last
     // block and still sits in the accumulators.
     flush();
-    const bool head_off = head_cut && (head_rb + 1) * kc <= s1;
-    const bool tail_off = s1 % kc != 0;  // the range ends inside a block
+    bool head_off = head_cut && (head_rb + 1) * kc <= s1;
+    bool tail_off = s1 % kc != 0;  // the range ends inside a block
     int tail_sum[TOK];
 #pragma unroll
     for (int t = 0; t < TOK; ++t) tail_sum[t] = a.total(t);
-    HandOff hh, ht;
     const int tail_rb = (s1 - 1) / kc;
-    hand_off(hh, head_rb, head_sum, (head_rb + 1) * kc - s0, head_off);
-    hand_off(ht, tail_rb, tail_sum, s1 - max(tail_rb * kc, s0), tail_off);
+    // A cut block that only this wave and its neighbour in the workgroup
+    // share (it starts inside the neighbour's range or this one's and ends
+    // inside the other) skips the atomics: both waves reach the same
+    // decision from the same ranges.
+    if (head_off && prev_in_wg && chunk0 + (int64_t)head_rb * kc >= prev_lo) {
+      head_local = true;
+#pragma unroll
+      for (int t = 0; t < TOK; ++t) head_keep[t] = head_sum[t];
+      head_off = false;
+    }
+    if (tail_off && next_in_wg && tail_rb * kc >= s0 &&
+        chunk0 + (int64_t)(tail_rb + 1) * kc <= next_hi) {
+      tail_local = true;
+      tail_rb_local = tail_rb;
+#pragma unroll
+      for (int t = 0; t < TOK; ++t) tail_keep[t] = tail_sum[t];
+      tail_off = false;
+    }
+    // Only blocks that are cut take the atomics; both are issued before
+    // either result is looked at, so the round trips overlap.
+    HandOff hh, ht;
+    if (head_off) hand_off(hh, head_rb, head_sum, (head_rb + 1) * kc - s0);
+    if (tail_off) hand_off(ht, tail_rb, tail_sum, s1 - max(tail_rb * kc, s0));
     if (head_off) settle(hh);
     if (tail_off) settle(ht);
   }
@@ -695,18 +722,43 @@ __global__ __launch_bounds__(256) void stream_kernel(
     int count, int64_t total, int32_t* sacc) {
   // With fewer chunks than waves, only the first `total` waves take part.
   const int64_t W = min((int64_t)gridDim.x * 4, total);
-  const int64_t wv =
-      (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  if (wv >= W) return;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t wv = (int64_t)blockIdx.x * 4 + wave;
   Stream<TOK, FUSED> st;
   __shared__ int obuf_all[4][16 * 64];
-  st.obuf = obuf_all[threadIdx.x >> 6];
+  st.obuf = obuf_all[wave];
   // FUSED: each wave's quantized activation rows (m * k <= BT_FUSED_MAX_MK)
   __shared__ v4u xl_all[4][FUSED ? BT_FUSED_MAX_MK / 16 : 1];
-  st.xl = (lds_i8_ptr)xl_all[threadIdx.x >> 6];
+  st.xl = (lds_i8_ptr)xl_all[wave];
   st.sacc = sacc;
-  stream_range(st, descs, chunk0s, count, wv * total / W,
-               (wv + 1) * total / W);
+  st.head_local = false;
+  st.tail_local = false;
+  if (wv < W) {
+    // the neighbours share this workgroup only if they take part too
+    st.prev_lo = wv > 0 ? (wv - 1) * total / W : 0;
+    st.next_hi = wv + 1 < W ? (wv + 2) * total / W : total;
+    st.prev_in_wg = wave > 0;
+    st.next_in_wg = wave < 3 && wv + 1 < W;
+    stream_range(st, descs, chunk0s, count, wv * total / W,
+                 (wv + 1) * total / W);
+  }
+  // Cut blocks shared by two waves of this workgroup only: the wave that
+  // holds the block's last chunks leaves its partial sums in its (now
+  // empty) staging area, and the wave that holds the first chunks adds them
+  // to its own and writes the outputs.  Every wave of the workgroup reaches
+  // this barrier, including those without a range.
+  const int lane = threadIdx.x & 63;
+  if (st.head_local) {
+#pragma unroll
+    for (int t = 0; t < TOK; ++t) st.obuf[t * 64 + lane] = st.head_keep[t];
+  }
+  __syncthreads();
+  if (st.tail_local) {
+    const int* other = obuf_all[wave + 1];
+#pragma unroll
+    for (int t = 0; t < TOK; ++t)
+      st.write_one(st.tail_rb_local, t, st.tail_keep[t] + other[t * 64 + lane]);
+  }
 }
 
 }  // namespace
