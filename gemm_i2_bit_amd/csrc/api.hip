@@ -463,15 +463,16 @@ int32_t bt_gemm_grouped(const void* plan_dev, const void* plan_host,
   const int cus = cu_count();
   if (cus <= 0) return BT_E_HIP;
   unsigned char* mut = const_cast<unsigned char*>(base);
-  // at least a group of 4 chunks per wave (4 waves per workgroup): a wave's
-  // set-up and hand-offs cost about what streaming a few chunks does, so
-  // small plans (one phase of a chained decode) run on fewer, fuller waves
+  // at least a group of 4 chunks per wave (counted in workgroups of 4 waves;
+  // the launch may regroup the same waves): a wave's set-up and hand-offs
+  // cost about what streaming a few chunks does, so small plans (one phase
+  // of a chained decode) run on fewer, fuller waves
   const int64_t wgs = std::min<int64_t>((int64_t)cus * bt::kStreamWgPerCu,
                                         (h.total_chunks + 15) / 16);
   return hip_status(bt::launch_stream_grouped(
       descs, reinterpret_cast<const int64_t*>(base + h.chunk_off), h.count,
       h.total_chunks, h.m, reinterpret_cast<int32_t*>(mut + h.sacc_off),
-      (int)wgs, h.fused == 1, s));
+      (int)wgs, h.fused == 1, wgs == (int64_t)cus * bt::kStreamWgPerCu, s));
 }
 
 }  // extern "C"

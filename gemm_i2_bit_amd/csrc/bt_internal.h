@@ -140,10 +140,11 @@ inline int row_block_waves(int64_t nblk, int kc) {
 }
 hipError_t launch_dot4(const Desc& d, hipStream_t s);
 hipError_t launch_lut(const Desc& d, hipStream_t s);  // m = 1 only
+// full: the grid fills every CU (workgroups == CUs * kStreamWgPerCu)
 hipError_t launch_stream_grouped(const Desc* descs, const int64_t* chunk0,
                                  int32_t count, int64_t total_chunks, int m,
                                  int32_t* sacc, int workgroups, bool fused,
-                                 hipStream_t s);
+                                 bool full, hipStream_t s);
 
 // A token row's scales from its absmax: a = max(amax, 1e-5), one correctly
 // rounded 127 / a for the products and s_a = a / 127 for the rescale.

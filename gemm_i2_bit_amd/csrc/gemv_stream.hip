@@ -716,19 +716,27 @@ __device__ __forceinline__ void stream_range(Stream<TOK, FUSED>& st,
 // dynamically (from shared counters, or through a claiming wave per
 // workgroup with work stealing across XCDs) evened out the ends and made
 // the launch slower, not faster.
-template <int TOK, bool FUSED>
-__global__ __launch_bounds__(256) void stream_kernel(
+//
+// WPW waves per workgroup: 8 for a full grid with int8 activations (one
+// workgroup per CU, the same 8 waves per CU as two of 4), so that 7 of every
+// 8 range boundaries fall inside a workgroup and their cut blocks meet in
+// LDS; 4 for smaller plans, which then spread over more CUs, and when the
+// launch quantizes (the LDS copies of the rows, 16 KiB per wave, leave room
+// for no more).
+template <int TOK, bool FUSED, int WPW>
+__global__ __launch_bounds__(64 * WPW) void stream_kernel(
     const Desc* __restrict__ descs, const int64_t* __restrict__ chunk0s,
     int count, int64_t total, int32_t* sacc) {
+  static_assert(WPW == 4 || (WPW == 8 && !FUSED), "workgroup shape");
   // With fewer chunks than waves, only the first `total` waves take part.
-  const int64_t W = min((int64_t)gridDim.x * 4, total);
+  const int64_t W = min((int64_t)gridDim.x * WPW, total);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int64_t wv = (int64_t)blockIdx.x * 4 + wave;
+  const int64_t wv = (int64_t)blockIdx.x * WPW + wave;
   Stream<TOK, FUSED> st;
-  __shared__ int obuf_all[4][16 * 64];
+  __shared__ int obuf_all[WPW][16 * 64];
   st.obuf = obuf_all[wave];
   // FUSED: each wave's quantized activation rows (m * k <= BT_FUSED_MAX_MK)
-  __shared__ v4u xl_all[4][FUSED ? BT_FUSED_MAX_MK / 16 : 1];
+  __shared__ v4u xl_all[WPW][FUSED ? BT_FUSED_MAX_MK / 16 : 1];
   st.xl = (lds_i8_ptr)xl_all[wave];
   st.sacc = sacc;
   st.head_local = false;
@@ -738,7 +746,7 @@ __global__ __launch_bounds__(256) void stream_kernel(
     st.prev_lo = wv > 0 ? (wv - 1) * total / W : 0;
     st.next_hi = wv + 1 < W ? (wv + 2) * total / W : total;
     st.prev_in_wg = wave > 0;
-    st.next_in_wg = wave < 3 && wv + 1 < W;
+    st.next_in_wg = wave < WPW - 1 && wv + 1 < W;
     stream_range(st, descs, chunk0s, count, wv * total / W,
                  (wv + 1) * total / W);
   }
@@ -763,16 +771,18 @@ __global__ __launch_bounds__(256) void stream_kernel(
 
 }  // namespace
 
-template <bool FUSED>
+// `workgroups` counts 4-wave workgroups; with WPW = 8 the same waves are
+// regrouped in half as many.
+template <bool FUSED, int WPW>
 hipError_t launch_stream(const Desc* descs, const int64_t* chunk0,
                          int32_t count, int64_t total_chunks, int m,
                          int32_t* sacc, int workgroups, hipStream_t s) {
-  const dim3 grid((unsigned)workgroups), block(256);
+  const dim3 grid((unsigned)((workgroups * 4 + WPW - 1) / WPW)), block(64 * WPW);
   switch (m) {
-    case 1: stream_kernel<1, FUSED><<<grid, block, 0, s>>>(descs, chunk0, count, total_chunks, sacc); break;
-    case 2: stream_kernel<2, FUSED><<<grid, block, 0, s>>>(descs, chunk0, count, total_chunks, sacc); break;
-    case 3: stream_kernel<3, FUSED><<<grid, block, 0, s>>>(descs, chunk0, count, total_chunks, sacc); break;
-    case 4: stream_kernel<4, FUSED><<<grid, block, 0, s>>>(descs, chunk0, count, total_chunks, sacc); break;
+    case 1: stream_kernel<1, FUSED, WPW><<<grid, block, 0, s>>>(descs, chunk0, count, total_chunks, sacc); break;
+    case 2: stream_kernel<2, FUSED, WPW><<<grid, block, 0, s>>>(descs, chunk0, count, total_chunks, sacc); break;
+    case 3: stream_kernel<3, FUSED, WPW><<<grid, block, 0, s>>>(descs, chunk0, count, total_chunks, sacc); break;
+    case 4: stream_kernel<4, FUSED, WPW><<<grid, block, 0, s>>>(descs, chunk0, count, total_chunks, sacc); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -781,11 +791,14 @@ hipError_t launch_stream(const Desc* descs, const int64_t* chunk0,
 hipError_t launch_stream_grouped(const Desc* descs, const int64_t* chunk0,
                                  int32_t count, int64_t total_chunks, int m,
                                  int32_t* sacc, int workgroups, bool fused,
-                                 hipStream_t s) {
-  return fused ? launch_stream<true>(descs, chunk0, count, total_chunks, m,
-                                     sacc, workgroups, s)
-               : launch_stream<false>(descs, chunk0, count, total_chunks, m,
-                                      sacc, workgroups, s);
+                                 bool full, hipStream_t s) {
+  if (fused)
+    return launch_stream<true, 4>(descs, chunk0, count, total_chunks, m, sacc,
+                                  workgroups, s);
+  return full ? launch_stream<false, 8>(descs, chunk0, count, total_chunks, m,
+                                        sacc, workgroups, s)
+              : launch_stream<false, 4>(descs, chunk0, count, total_chunks, m,
+                                        sacc, workgroups, s);
 }
 
 }  // namespace bt
