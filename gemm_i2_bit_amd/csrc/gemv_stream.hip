@@ -29,11 +29,16 @@
 //    part of the problem is done, or when the staging area is full.  Writes
 //    scattered through the read stream cost far more time than their bytes
 //    (the memory has to turn the bus around for each of them).
-//  * A row block cut by a wave-range boundary is shared by 2+ waves: each
-//    adds its partial sums into 64-bit scratch slots that also count the
-//    block's chunks seen so far (one device-scope atomic with return per row
-//    and token); the lane that completes the count holds the total, writes
-//    the output and clears the slot for the next launch.
+//  * A row block cut by a wave-range boundary is shared by 2+ waves.  When
+//    only two waves of one workgroup share it, their partial sums meet in
+//    LDS at the end of the launch.  Otherwise each wave adds its partial
+//    sums into 64-bit scratch slots that also count the block's chunks seen
+//    so far (one device-scope atomic with return per row and token); the
+//    lane that completes the count holds the total, writes the output and
+//    clears the slot for the next launch.  The atomics are read-modify-writes
+//    at the coherence point and cost far more than their bytes, so a full
+//    grid runs 8-wave workgroups, one per CU, keeping 7 of every 8 cuts in
+//    LDS.
 #include "bt_internal.h"
 
 namespace bt {
