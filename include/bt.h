@@ -164,16 +164,16 @@ typedef struct bt_problem {
  * block; on the matrix cores, per-range regions and arrival counters for
  * problems whose reduction is split.  The counters and slots are zero in the
  * host image and every complete launch leaves them zero.
+ * Hence launches that use one plan must not overlap (use one plan per
+ * stream); rebuild the plan when any pointer, shape or scale changes.
+ * plan_host must stay a byte-identical copy of the host image written by
+ * bt_grouped_plan (only its header is read by bt_gemm_grouped).
  * Kernel choice: m = 1 streams the weights through packed dot products; so
  * do m = 2 in plans of fewer than 131072 chunks (128 MiB of packed weights)
  * and m = 3, 4 in plans of fewer than 32768 chunks (32 MiB), while larger
  * plans at m = 2..4 and every plan at m > 4 use the int8 matrix cores (the
  * dot products of a large plan are then bound by the vector ALUs, not by the
  * weight stream).
- * Hence launches that use one plan must not overlap (use one plan per
- * stream); rebuild the plan when any pointer, shape or scale changes.
- * plan_host must stay a byte-identical copy of the host image written by
- * bt_grouped_plan (only its header is read by bt_gemm_grouped).
  * bt_grouped_plan_bytes returns the size, or a negative status. */
 int64_t bt_grouped_plan_bytes(const bt_problem* probs, int32_t count);
 int32_t bt_grouped_plan(const bt_problem* probs, int32_t count, void* plan,
