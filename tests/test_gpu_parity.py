@@ -450,6 +450,42 @@ def test_grouped_extremes(m):
             assert (acc[2] == 0).all()
 
 
+@pytest.mark.parametrize("m", [1, 3])
+def test_grouped_full_grid_cuts(m):
+    """A plan large enough to fill every CU (more than 16 chunks per
+    workgroup slot), so the streaming kernel runs its widest workgroups:
+    row blocks of 1024 chunks (k = 65536) cut among a hundred waves and more
+    (the atomic hand-off), next to blocks of 4 chunks (k = 256) shared by two
+    neighbouring waves (combined inside the workgroup); three launches in a
+    row, every output against the oracle."""
+    rng = np.random.default_rng([112, m])
+    cases = []
+    for n, k in ((640, 65536), (4096, 256)):
+        cases.append((wl.trits(rng, (n, k), wl.DECODE_2B),
+                      wl.x_normal(rng, (m, k)),
+                      np.float32(rng.uniform(0.01, 0.05))))
+    probs = []
+    for tt, xx, s_w in cases:
+        x_q, s_a = bt.bt_quant_act(dev(xx))
+        probs.append(dict(packed=bt.bt_pack_i2s(dev(tt)), s_w=s_w,
+                          n=tt.shape[0], k=tt.shape[1], x_q=x_q, s_a=s_a,
+                          y=torch.empty((m, tt.shape[0]), device="cuda:0"),
+                          acc=torch.empty((m, tt.shape[0]), dtype=torch.int32,
+                                          device="cuda:0")))
+    refs = [oracle_product(tt, xx, s_w)[3:] for tt, xx, s_w in cases]
+    plan = bt.bt_grouped_plan(probs)
+    for launch in range(3):
+        for p in probs:
+            p["y"].fill_(float("nan"))
+            p["acc"].fill_(0x7EADBEEF)
+        bt.bt_gemm_grouped(plan)
+        torch.cuda.synchronize()
+        for i, (prob, (acc_r, y_r)) in enumerate(zip(probs, refs)):
+            acc = prob["acc"].cpu().numpy()
+            assert np.array_equal(acc, acc_r), f"launch {launch} problem {i}"
+            check_y(prob["y"].cpu().numpy(), y_r, acc_r)
+
+
 @pytest.mark.parametrize("m", [1, 2, 3, 4])
 def test_grouped_fused_quant(m):
     """Grouped calls that quantize their own fp32 activations: outputs equal
