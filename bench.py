@@ -10,17 +10,23 @@ timed region starts.
 
 Default workload: the 2B-shaped decode set at M=1 (30 layers x 7 projections,
 0.52 GB of packed weights, larger than the 256 MB Infinity Cache).  Prints
-one JSON line (rank 0, one GPU).
+one JSON line (rank 0, one GPU).  Unless --no-extra is given the line also
+carries the other configurations: the single small GEMV (latency), batched
+decode at M = 8/16/32 over the same weights, the M=512 prefill layer, the
+8B-shaped set at M = 1 and 64, one launch per product beside the grouped
+launch, the measured streaming-read ceiling, the layer-chained decode and the
+lookup-table comparison.
 """
 from __future__ import annotations
 
 import argparse
-import hashlib
 import glob
+import hashlib
 import json
 import os
 import sys
 import time
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 
@@ -51,6 +57,10 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def host_threads():
+    return int(os.environ.get("OMP_NUM_THREADS", 0) or os.cpu_count() or 1)
+
+
 def kernel_sources_sha():
     """Hash of the kernel sources and of the build script (its compiler
     flags shape the kernels too)."""
@@ -64,14 +74,45 @@ def kernel_sources_sha():
     return h.hexdigest()[:16]
 
 
-class WorkSet:
-    """Device buffers, plan and step function for one workload."""
+class PackedSet:
+    """Every (layer, projection) weight tensor of a workload's weight seed,
+    packed on the GPU once and shared by the workloads that read the same
+    weights (the decode set at every M, the chained decode).  The trits are
+    drawn on several host threads (each tensor has its own generator, so the
+    values do not depend on the threads).  The trits of the first
+    `keep_layers` layers stay on the host for the CPU baseline."""
 
-    def __init__(self, work: wl.Workload, torch, bt, mode="grouped"):
+    def __init__(self, work: wl.Workload, torch, bt, keep_layers=1):
         self.work = work
-        self.torch = torch
-        self.bt = bt
-        self.mode = mode
+        dev = torch.device("cuda:0")
+        keys = [(p.layer, p.proj) for p in work.problems()]
+        self.packed, self.s_w, self.trits = {}, {}, {}
+        t0 = time.time()
+        done = 0
+        with ThreadPoolExecutor(max(1, min(16, host_threads()))) as ex:
+            for i in range(0, len(keys), 32):
+                batch = keys[i:i + 32]
+                for key, (t, s_w) in zip(batch, ex.map(
+                        lambda kk: work.weights(*kk), batch)):
+                    self.packed[key] = bt.bt_pack_i2s(
+                        torch.from_numpy(t).to(dev))
+                    self.s_w[key] = float(s_w)
+                    if key[0] < keep_layers:
+                        self.trits[key] = t
+                    del t
+                done += len(batch)
+                log(f"[bench] {work.name}: packed {done}/{len(keys)} tensors "
+                    f"({time.time() - t0:.1f} s)")
+        torch.cuda.synchronize()
+
+
+class WorkSet:
+    """Activations, outputs, plans and step functions of one workload over a
+    PackedSet of its weights."""
+
+    def __init__(self, work: wl.Workload, ps: PackedSet, torch, bt,
+                 mode="grouped"):
+        self.work, self.torch, self.bt, self.mode = work, torch, bt, mode
         dev = torch.device("cuda:0")
         probs = work.problems()
         m = work.m
@@ -86,43 +127,30 @@ class WorkSet:
                    for k in ks}
         off = {k: 0 for k in ks}
         self.problems = []
-        t0 = time.time()
-        for i, p in enumerate(probs):
-            t, s_w = work.weights(p.layer, p.proj)
-            packed = bt.bt_pack_i2s(torch.from_numpy(t).to(dev))
-            del t
-            x = work.activations(p.layer, p.proj)
+        for p in probs:
+            key = (p.layer, p.proj)
             o = off[p.k]
-            self.x[p.k][o:o + m].copy_(torch.from_numpy(x))
+            self.x[p.k][o:o + m].copy_(torch.from_numpy(
+                work.activations(p.layer, p.proj)))
             off[p.k] += m
-            y = torch.empty((m, p.n), dtype=torch.float32, device=dev)
-            self.problems.append(dict(packed=packed, s_w=float(s_w), n=p.n,
-                                      k=p.k, x_q=self.xq[p.k][o:o + m],
-                                      s_a=self.sa[p.k][o:o + m], y=y))
-            if (i + 1) % 50 == 0:
-                log(f"[bench] prepared {i + 1}/{len(probs)} tensors "
-                    f"({time.time() - t0:.1f} s)")
+            self.problems.append(dict(
+                packed=ps.packed[key], s_w=ps.s_w[key], n=p.n, k=p.k,
+                x_q=self.xq[p.k][o:o + m], s_a=self.sa[p.k][o:o + m],
+                x=self.x[p.k][o:o + m],
+                y=torch.empty((m, p.n), dtype=torch.float32, device=dev)))
         torch.cuda.synchronize()
-        self.plan = bt.bt_grouped_plan(self.problems)
-        if mode == "fused":
-            # the same products, quantizing the fp32 rows in the launch
-            fprobs = []
-            off = {k: 0 for k in ks}
-            for p in self.problems:
-                o = off[p["k"]]
-                off[p["k"]] += m
-                fprobs.append(dict(packed=p["packed"], s_w=p["s_w"], n=p["n"],
-                                   k=p["k"], x=self.x[p["k"]][o:o + m],
-                                   y=p["y"]))
-            self.fplan = bt.bt_grouped_plan_f32(fprobs)
         self.ks = ks
+        if mode == "fused":
+            self.plan = bt.bt_grouped_plan_f32(self.problems)
+        else:
+            self.plan = bt.bt_grouped_plan(self.problems)
 
     # algorithmic bytes and ops -------------------------------------------
-    def product_bytes(self):
+    def product_bytes(self, mode=None):
         """Packed weights + int8 activations + scales + fp32 outputs (fused:
         packed weights + fp32 activations + fp32 outputs)."""
         m = self.m
-        if self.mode == "fused":
+        if (mode or self.mode) == "fused":
             return sum(self.bt.bt_packed_bytes(p["n"], p["k"]) + 4 * m * p["k"]
                        + 4 * m * p["n"] for p in self.problems)
         return sum(self.bt.bt_packed_bytes(p["n"], p["k"]) + m * p["k"] + 4 * m
@@ -131,8 +159,7 @@ class WorkSet:
     def quant_bytes(self):
         if self.mode == "fused":
             return 0
-        m = self.m
-        return sum(5 * m * p["k"] + 4 * m for p in self.problems)
+        return sum(5 * self.m * p["k"] + 4 * self.m for p in self.problems)
 
     def weight_bytes(self):
         return sum(self.bt.bt_packed_bytes(p["n"], p["k"])
@@ -150,155 +177,43 @@ class WorkSet:
                                   [self.sa[k] for k in self.ks])
 
     def product(self):
-        if self.mode == "fused":
-            self.bt.bt_gemm_grouped(self.fplan)
-        elif self.mode == "grouped":
-            self.bt.bt_gemm_grouped(self.plan)
-        else:
-            for p in self.problems:
-                self.bt.bt_gemm(p["packed"], p["s_w"], p["n"], p["k"],
-                                p["x_q"], p["s_a"], y=p["y"])
+        self.bt.bt_gemm_grouped(self.plan)
+
+    def product_per_launch(self):
+        for p in self.problems:
+            self.bt.bt_gemm(p["packed"], p["s_w"], p["n"], p["k"], p["x_q"],
+                            p["s_a"], y=p["y"])
 
 
-class ChainSet:
-    """One token through the layer-chained decode of a workload's weights
-    (workloads.CHAIN_PHASES): per layer, four dependent phases, each one
-    quantization launch of the phase's input and one grouped launch of the
-    products that read it (fused: one grouped launch that quantizes its fp32
-    input itself).  Nothing runs ahead of its input."""
-
-    def __init__(self, work: wl.Workload, torch, bt, layers=None,
-                 fused=False):
-        self.torch, self.bt = torch, bt
-        self.fused = fused
-        dev = torch.device("cuda:0")
-        self.layers = work.layers if layers is None else layers
-        self.x0 = torch.from_numpy(wl.chain_input(work)).to(dev)
-        self.phases = []  # (input [1, k], x_q, s_a, plan, names, layer)
-        self.y = []       # per layer: projection -> output [1, n]
-        self.bytes = 0
-        x = self.x0
-        for l in range(self.layers):
-            ys, packed = {}, {}
-            for proj in wl.PROJ_NAMES:
-                t, s_w = work.weights(l, proj)
-                packed[proj] = (bt.bt_pack_i2s(torch.from_numpy(t).to(dev)),
-                                float(s_w))
-                ys[proj] = torch.empty((1, t.shape[0]), dtype=torch.float32,
-                                       device=dev)
-                del t
-            for src, dsts in wl.CHAIN_PHASES:
-                xin = x if src == "x" else ys[src]
-                k = xin.shape[1]
-                x_q = torch.empty((1, k), dtype=torch.int8, device=dev)
-                s_a = torch.empty(1, dtype=torch.float32, device=dev)
-                probs = [dict(packed=packed[d][0], s_w=packed[d][1],
-                              n=ys[d].shape[1], k=k, x_q=x_q, s_a=s_a,
-                              x=xin, y=ys[d]) for d in dsts]
-                plan = (bt.bt_grouped_plan_f32(probs) if fused
-                        else bt.bt_grouped_plan(probs))
-                self.phases.append((xin, x_q, s_a, plan, dsts, l))
-                self.bytes += 5 * k + 4 + sum(
-                    bt.bt_packed_bytes(p["n"], k) + k + 4 + 4 * p["n"]
-                    for p in probs)
-            self.y.append(ys)
-            x = ys[wl.CHAIN_OUT]
-        self.out = x
-        torch.cuda.synchronize()
-
-    def launches(self):
-        return (1 if self.fused else 2) * len(self.phases)
-
-    def step(self):
-        for xin, x_q, s_a, plan, _, _ in self.phases:
-            if not self.fused:
-                self.bt.bt_quant_act(xin, x_q, s_a)
-            self.bt.bt_gemm_grouped(plan)
-
-    def capture(self):
-        """The token as one HIP graph (captured after a warm-up pass on a
-        side stream)."""
-        torch = self.torch
-        side = torch.cuda.Stream()
-        side.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(side):
-            self.step()
-        torch.cuda.current_stream().wait_stream(side)
-        torch.cuda.synchronize()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            self.step()
-        torch.cuda.synchronize()
-        return g
-
-
-def run_chain(cs: ChainSet, tokens: int, warmup: int, torch):
-    """Per-token wall time of the chained decode, eager and graph-replayed
-    (ms)."""
-    for _ in range(warmup):
-        cs.step()
+def capture(torch, fn):
+    """fn's launches as one HIP graph (captured after a warm-up call on a
+    side stream)."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(tokens):
-        cs.step()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
     torch.cuda.synchronize()
-    eager = (time.perf_counter() - t0) / tokens * 1e3
-    g = cs.capture()
-    for _ in range(warmup):
+    return g
+
+
+def time_graph(torch, g, reps):
+    """Average ms per replay of graph g over `reps` back-to-back replays
+    (HIP events on the current stream, after two untimed replays)."""
+    g.replay()
+    g.replay()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
         g.replay()
+    e1.record()
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(tokens):
-        g.replay()
-    torch.cuda.synchronize()
-    graph = (time.perf_counter() - t0) / tokens * 1e3
-    return eager, graph
-
-
-def lut_ablation(torch, bt, reps=30):
-    """Single-token products with dot products (bt_gemv) and with lookup
-    tables (bt_gemv_lut) on random packed weights: microseconds per call,
-    averaged over back-to-back calls replayed from a HIP graph (so that the
-    host's call rate does not set the time)."""
-    dev = torch.device("cuda:0")
-    shapes = [(2560, 2560), (6912, 2560), (2560, 6912), (131072, 4096)]
-    out = {}
-    for n, k in shapes:
-        valid = torch.tensor([b for b in range(256)
-                              if all((b >> (2 * j)) & 3 != 3 for j in range(4))],
-                             dtype=torch.uint8, device=dev)  # no code 3
-        packed = valid[torch.randint(0, valid.numel(),
-                                     (bt.bt_packed_bytes(n, k),), device=dev)]
-        x_q = torch.randint(-127, 128, (k,), dtype=torch.int8, device=dev)
-        s_a = torch.ones(1, device=dev)
-        y = torch.empty((1, n), device=dev)
-        res = {}
-        for name, fn in (("dot4_us", bt.bt_gemv), ("lut_us", bt.bt_gemv_lut)):
-            side = torch.cuda.Stream()
-            side.wait_stream(torch.cuda.current_stream())
-            with torch.cuda.stream(side):
-                for _ in range(3):
-                    fn(packed, 0.02, n, k, x_q, s_a, y=y)
-            torch.cuda.current_stream().wait_stream(side)
-            torch.cuda.synchronize()
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
-                for _ in range(reps):
-                    fn(packed, 0.02, n, k, x_q, s_a, y=y)
-            g.replay()
-            torch.cuda.synchronize()
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record()
-            g.replay()
-            e1.record()
-            torch.cuda.synchronize()
-            res[name] = round(e0.elapsed_time(e1) / reps * 1e3, 2)
-            del g
-        res["weight_bytes"] = packed.numel()
-        out[f"{n}x{k}"] = res
-        del packed
-    return out
+    return e0.elapsed_time(e1) / reps
 
 
 def run_timed(ws: WorkSet, steps: int, warmup: int, torch):
@@ -330,56 +245,310 @@ def run_timed(ws: WorkSet, steps: int, warmup: int, torch):
     return wall, e0.elapsed_time(e1) / steps
 
 
-def cpu_baseline(work: wl.Workload, seconds: float):
+def per_launch_ms(ws: WorkSet, torch, reps=10):
+    """One bt_gemm launch per product (the non-grouped mode), all of a pass
+    captured in one HIP graph: ms per pass of the products alone (the
+    activations are quantized once beforehand)."""
+    ws.quant()
+    g = capture(torch, ws.product_per_launch)
+    ms = time_graph(torch, g, reps)
+    del g
+    return ms
+
+
+def roofline(nbytes, ops, kern_ms, bound, traffic=None):
+    if bound == "mfma":
+        achieved = ops / (kern_ms * 1e-3) / 1e12
+        return dict(bound="mfma", achieved=round(achieved, 2),
+                    peak=INT8_PEAK_TOPS, unit="TFLOP/s",
+                    frac=round(achieved / INT8_PEAK_TOPS, 4), traffic=traffic)
+    achieved = nbytes / (kern_ms * 1e-3) / 1e9
+    return dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS,
+                unit="GB/s", frac=round(achieved / HBM_PEAK_GBS, 4),
+                traffic=traffic)
+
+
+def config_entry(ws: WorkSet, torch, steps, warmup, ceiling=None,
+                 with_per_launch=True, cpu_seconds=0.0, ps=None):
+    """Figures of one configuration: the step (quantize + grouped product),
+    the grouped product kernel against its roofline, one launch per product,
+    and the oracle on a sample of the same workload."""
+    wall, kern = run_timed(ws, steps, warmup, torch)
+    ms_step = wall / steps * 1e3
+    prefill = ws.m >= 128
+    nbytes = ws.product_bytes()
+    roof = roofline(nbytes, ws.ops(), kern, "mfma" if prefill else "hbm")
+    if ceiling and not prefill:
+        roof["frac_of_measured_ceiling"] = round(
+            roof["achieved"] / ceiling, 4)
+    e = {"workload": ws.work.name, "m": ws.m,
+         "ms_per_step": round(ms_step, 4),
+         "product_kernel_ms": round(kern, 5),
+         "algorithmic_bytes": nbytes,
+         "weight_gb_s": round(ws.weight_bytes() / (kern * 1e-3) / 1e9, 1),
+         "tops": round(ws.ops() / (kern * 1e-3) / 1e12, 2),
+         "tokens_per_s_equiv": round(ws.m / (ms_step * 1e-3), 1),
+         "roofline": roof}
+    if with_per_launch:
+        pl = per_launch_ms(ws, torch)
+        e["per_launch"] = {
+            "launches": len(ws.problems), "ms_per_pass": round(pl, 5),
+            "gb_s": round(nbytes / (pl * 1e-3) / 1e9, 1),
+            "tops": round(ws.ops() / (pl * 1e-3) / 1e12, 2),
+            "frac": round((ws.ops() / (pl * 1e-3) / 1e12 / INT8_PEAK_TOPS)
+                          if prefill else
+                          (nbytes / (pl * 1e-3) / 1e9 / HBM_PEAK_GBS), 4)}
+    if cpu_seconds > 0 and ps is not None:
+        e["cpu_baseline"] = cpu_baseline(ws.work, ps, cpu_seconds,
+                                         host_threads())
+    return e
+
+
+class ChainSet:
+    """One token through the layer-chained decode of a workload's weights
+    (workloads.CHAIN_PHASES): per layer, four dependent phases, each one
+    quantization launch of the phase's input and one grouped launch of the
+    products that read it (fused: one grouped launch that quantizes its fp32
+    input itself).  Nothing runs ahead of its input."""
+
+    def __init__(self, work: wl.Workload, torch, bt, layers=None,
+                 fused=False, ps: PackedSet | None = None):
+        self.torch, self.bt = torch, bt
+        self.fused = fused
+        dev = torch.device("cuda:0")
+        self.layers = work.layers if layers is None else layers
+        self.x0 = torch.from_numpy(wl.chain_input(work)).to(dev)
+        self.phases = []  # (input [1, k], x_q, s_a, plan, names, layer)
+        self.y = []       # per layer: projection -> output [1, n]
+        self.bytes = 0
+        x = self.x0
+        for l in range(self.layers):
+            ys, packed = {}, {}
+            for proj in wl.PROJ_NAMES:
+                if ps is not None:
+                    packed[proj] = (ps.packed[(l, proj)], ps.s_w[(l, proj)])
+                    n = work.shapes[proj][1]
+                else:
+                    t, s_w = work.weights(l, proj)
+                    packed[proj] = (bt.bt_pack_i2s(torch.from_numpy(t).to(dev)),
+                                    float(s_w))
+                    n = t.shape[0]
+                    del t
+                ys[proj] = torch.empty((1, n), dtype=torch.float32,
+                                       device=dev)
+            for src, dsts in wl.CHAIN_PHASES:
+                xin = x if src == "x" else ys[src]
+                k = xin.shape[1]
+                x_q = torch.empty((1, k), dtype=torch.int8, device=dev)
+                s_a = torch.empty(1, dtype=torch.float32, device=dev)
+                probs = [dict(packed=packed[d][0], s_w=packed[d][1],
+                              n=ys[d].shape[1], k=k, x_q=x_q, s_a=s_a,
+                              x=xin, y=ys[d]) for d in dsts]
+                plan = (bt.bt_grouped_plan_f32(probs) if fused
+                        else bt.bt_grouped_plan(probs))
+                self.phases.append((xin, x_q, s_a, plan, dsts, l))
+                self.bytes += 5 * k + 4 + sum(
+                    bt.bt_packed_bytes(p["n"], k) + k + 4 + 4 * p["n"]
+                    for p in probs)
+            self.y.append(ys)
+            x = ys[wl.CHAIN_OUT]
+        self.out = x
+        torch.cuda.synchronize()
+
+    def launches(self):
+        return (1 if self.fused else 2) * len(self.phases)
+
+    def step(self):
+        for xin, x_q, s_a, plan, _, _ in self.phases:
+            if not self.fused:
+                self.bt.bt_quant_act(xin, x_q, s_a)
+            self.bt.bt_gemm_grouped(plan)
+
+    def capture(self):
+        """The token as one HIP graph."""
+        return capture(self.torch, self.step)
+
+
+def run_chain(cs: ChainSet, tokens: int, warmup: int, torch):
+    """Per-token wall time of the chained decode, eager and graph-replayed
+    (ms)."""
+    for _ in range(warmup):
+        cs.step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(tokens):
+        cs.step()
+    torch.cuda.synchronize()
+    eager = (time.perf_counter() - t0) / tokens * 1e3
+    g = cs.capture()
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(tokens):
+        g.replay()
+    torch.cuda.synchronize()
+    graph = (time.perf_counter() - t0) / tokens * 1e3
+    return eager, graph
+
+
+def format_ablation(torch, bt, reps=30):
+    """Single-token products over the same random trits with the 2-bit
+    format and packed dot products (bt_gemv), with the 2-bit format and
+    lookup tables (bt_gemv_lut), and with five trits per byte (bt_gemv_b3):
+    microseconds per call, averaged over back-to-back calls replayed from a
+    HIP graph (so that the host's call rate does not set the time), and the
+    weights per second each reaches."""
+    dev = torch.device("cuda:0")
+    shapes = [(2560, 2560), (6912, 2560), (2560, 6912), (131072, 4096)]
+    out = {}
+    for n, k in shapes:
+        t = torch.randint(-1, 2, (n, k), dtype=torch.int8, device=dev)
+        p2 = bt.bt_pack_i2s(t)
+        p3 = bt.bt_pack_b3(t)
+        del t
+        x_q = torch.randint(-127, 128, (k,), dtype=torch.int8, device=dev)
+        s_a = torch.ones(1, device=dev)
+        y = torch.empty((1, n), device=dev)
+        res = {}
+        for name, fn, packed in (("dot4_us", bt.bt_gemv, p2),
+                                 ("lut_us", bt.bt_gemv_lut, p2),
+                                 ("b3_us", bt.bt_gemv_b3, p3)):
+            def calls(fn=fn, packed=packed):
+                for _ in range(reps):
+                    fn(packed, 0.02, n, k, x_q, s_a, y=y)
+            g = capture(torch, calls)
+            res[name] = round(time_graph(torch, g, 1) / reps * 1e3, 2)
+            del g
+        res["bytes_2bit"] = p2.numel()
+        res["bytes_b3"] = p3.numel()
+        for name in ("dot4", "lut", "b3"):
+            res[f"{name}_gweights_s"] = round(n * k / res[f"{name}_us"] / 1e3,
+                                              1)
+        out[f"{n}x{k}"] = res
+        del p2, p3
+    return out
+
+
+def single_gemv(torch, bt, reps=200):
+    """The small single GEMV (M=1, K=256, N=512, seed 0): latency of one
+    bt_gemv call and of bt_quant_act followed by bt_gemv, averaged over
+    back-to-back calls replayed from a HIP graph, and the host-side time of
+    an eager call pair (enqueue to completion)."""
+    dev = torch.device("cuda:0")
+    t, s_w, x = wl.single_gemv()
+    packed = bt.bt_pack_i2s(torch.from_numpy(t).to(dev))
+    xd = torch.from_numpy(x).to(dev)
+    x_q, s_a = bt.bt_quant_act(xd)
+    y = torch.empty((1, t.shape[0]), device=dev)
+
+    def gemv():
+        for _ in range(reps):
+            bt.bt_gemv(packed, s_w, t.shape[0], t.shape[1], x_q, s_a, y=y)
+
+    def both():
+        for _ in range(reps):
+            bt.bt_quant_act(xd, x_q, s_a)
+            bt.bt_gemv(packed, s_w, t.shape[0], t.shape[1], x_q, s_a, y=y)
+
+    g1 = capture(torch, gemv)
+    g2 = capture(torch, both)
+    gemv_us = time_graph(torch, g1, 1) / reps * 1e3
+    both_us = time_graph(torch, g2, 1) / reps * 1e3
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(50):
+        bt.bt_quant_act(xd, x_q, s_a)
+        bt.bt_gemv(packed, s_w, t.shape[0], t.shape[1], x_q, s_a, y=y)
+        torch.cuda.synchronize()
+    eager_us = (time.perf_counter() - t0) / 50 * 1e6
+    return {"workload": "single_gemv_m1_k256_n512",
+            "gemv_us_graph": round(gemv_us, 3),
+            "quant_plus_gemv_us_graph": round(both_us, 3),
+            "quant_plus_gemv_us_eager_sync": round(eager_us, 2),
+            "algorithmic_bytes": 32768 + 256 + 4 + 2048,
+            "note": "L2-resident: a latency, not a bandwidth figure"}
+
+
+def read_ceiling(torch, bt, nbytes=1 << 30, reps=20):
+    """The streaming-read ceiling: bt_read_probe over a buffer larger than
+    the 256 MB Infinity Cache, back-to-back launches timed with HIP events;
+    GB/s for 4 and 8 waves per compute unit with 1 to 4 groups of four
+    loads in flight per wave; the ceiling is the best of them."""
+    dev = torch.device("cuda:0")
+    buf = torch.ones(nbytes, dtype=torch.uint8, device=dev)
+    sink = torch.empty(1 << 16, dtype=torch.int32, device=dev)
+    out = {"bytes": nbytes, "sweep": {}}
+    for wpc in (4, 8):
+        for groups in (1, 2, 3, 4):
+            for _ in range(3):
+                bt.bt_read_probe(buf, sink, wpc, groups)
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                bt.bt_read_probe(buf, sink, wpc, groups)
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / reps
+            out["sweep"][f"{wpc}w_{groups}g"] = round(
+                nbytes / (ms * 1e-3) / 1e9, 1)
+    best = max(out["sweep"], key=out["sweep"].get)
+    out["gb_s"] = out["sweep"][best]
+    out["best"] = best
+    del buf, sink
+    return out
+
+
+def cpu_baseline(work: wl.Workload, ps: PackedSet, seconds: float,
+                 threads: int):
     """The oracle, as it stands, on a bounded sample of the same workload:
-    whole layers (all projections), repeated until about `seconds` of timed
-    work (packing, the offline step, is not timed)."""
+    whole layers (all projections) of the trits kept on the host, repeated
+    until about `seconds` of timed work (at least one layer pass); packing,
+    the offline step, is not timed."""
     import oracle
-    threads = int(os.environ.get("OMP_NUM_THREADS", 0) or os.cpu_count() or 1)
-    timed = 0.0
-    nbytes = 0
-    passes = 0
-    layer = 0
-    items_cache = {}
-    while timed < seconds:
-        if layer not in items_cache:
-            items = []
-            for proj in work.projs:
-                t, s_w = work.weights(layer, proj)
-                packed, _ = oracle.pack_i2s(t)
-                x = work.activations(layer, proj)
-                items.append((packed, s_w, t.shape[0], t.shape[1], x))
-                del t
-            if len(items_cache) < 8:
-                items_cache[layer] = items
-        else:
-            items = items_cache[layer]
+    layers = sorted({l for l, _ in ps.trits})
+    items = {}
+    for l in layers:
+        items[l] = []
+        for proj in work.projs:
+            t = ps.trits[(l, proj)]
+            packed, _ = oracle.pack_i2s(t)
+            items[l].append((packed, ps.s_w[(l, proj)], t.shape[0],
+                             t.shape[1], work.activations(l, proj)))
+    timed, nbytes, macs, passes = 0.0, 0, 0, 0
+    while timed < seconds or passes == 0:
+        l = layers[passes % len(layers)]
         t0 = time.perf_counter()
-        for packed, s_w, n, k, x in items:
+        for packed, s_w, n, k, x in items[l]:
             q, s_a = oracle.quant_act(x)
             oracle.gemm(packed, s_w, n, k, q, s_a, nthreads=threads)
         timed += time.perf_counter() - t0
         m = work.m
         nbytes += sum(p.size + 5 * m * k + 8 * m + 4 * m * n
-                      for p, _, n, k, _ in items)
+                      for p, _, n, k, _ in items[l])
+        macs += sum(m * n * k for _, _, n, k, _ in items[l])
         passes += 1
-        layer = (layer + 1) % min(work.layers, 8)
-    return dict(value=round(nbytes / timed / 1e9, 3), unit="GB/s",
+    return dict(value=round(nbytes / timed / 1e9, 4), unit="GB/s",
                 cores=threads, kind="oracle",
-                sample=f"{passes} layer passes (layers 0-{min(work.layers, 8) - 1} "
-                       f"of {work.layers}, all {len(work.projs)} projections, "
-                       f"M={work.m}; quantize + product; {timed:.1f} s timed)")
+                gmac_s=round(macs / timed / 1e9, 3),
+                sample=f"{passes} layer passes (layers {layers[0]}-"
+                       f"{layers[-1]} of {work.layers}, all "
+                       f"{len(work.projs)} projections, M={work.m}; quantize "
+                       f"+ product; {timed:.1f} s timed)")
 
 
-def load_traffic(workload: str, sha: str, launch_bytes: int):
-    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+def load_profile(name: str, sha: str, key: str):
+    """A figure from a counter summary in profiles/ (null once the kernel
+    sources have changed since the counters were taken)."""
+    path = os.path.join(ROOT, "profiles", name)
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
     if rec.get("kernel_sources_sha") != sha:
         return None
-    return rec.get("hbm_bytes_per_launch")
+    return rec.get(key)
 
 
 def main():
@@ -389,16 +558,15 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="decode_2b_m1",
                     choices=sorted(WORKLOADS))
-    ap.add_argument("--mode", default="grouped",
-                    choices=["grouped", "per-launch", "fused"])
+    ap.add_argument("--mode", default="grouped", choices=["grouped", "fused"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true",
-                    help="skip the M=512 prefill, chained-decode and "
-                         "lookup-table figures")
+                    help="only the selected workload (no other configuration)")
     ap.add_argument("--no-chain", action="store_true",
-                    help="skip the chained-decode and lookup-table figures "
-                         "(keeps the M=512 prefill figure)")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+                    help="skip the chained-decode and lookup-table figures")
+    ap.add_argument("--no-8b", action="store_true",
+                    help="skip the 8B-shaped set")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one plain 256 MiB device copy, so that a "
                          "counter run can scale FETCH_SIZE / WRITE_SIZE")
@@ -417,11 +585,16 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     bt.lib()  # fails loudly if the HIP library is missing
+    sha = kernel_sources_sha()
+    extra = not args.no_extra
+    cpu = not args.no_cpu_baseline
 
+    ceiling = read_ceiling(torch, bt) if extra else None
     work = WORKLOADS[args.workload]()
     log(f"[bench] workload {work.name}: {len(work.problems())} products, "
         f"{work.weight_bytes() / 1e6:.1f} MB packed weights")
-    ws = WorkSet(work, torch, bt, args.mode)
+    ps = PackedSet(work, torch, bt, keep_layers=2 if work.layers > 1 else 1)
+    ws = WorkSet(work, ps, torch, bt, args.mode)
     wall, kern_avg = run_timed(ws, args.steps, args.warmup, torch)
     ms_step = wall / args.steps * 1e3
     step_bytes = ws.product_bytes() + ws.quant_bytes()
@@ -432,20 +605,15 @@ def main():
     else:
         value = step_bytes / (ms_step * 1e-3) / 1e9
         unit = "GB/s"
-    launch_bytes = ws.product_bytes()
-    sha = kernel_sources_sha()
-    if prefill:
-        achieved = ws.ops() / (kern_avg * 1e-3) / 1e12
-        roof = dict(bound="mfma", achieved=round(achieved, 2),
-                    peak=INT8_PEAK_TOPS, unit="TFLOP/s",
-                    frac=round(achieved / INT8_PEAK_TOPS, 4),
-                    traffic=load_traffic(args.workload, sha, launch_bytes))
-    else:
-        achieved = launch_bytes / (kern_avg * 1e-3) / 1e9
-        roof = dict(bound="hbm", achieved=round(achieved, 1),
-                    peak=HBM_PEAK_GBS, unit="GB/s",
-                    frac=round(achieved / HBM_PEAK_GBS, 4),
-                    traffic=load_traffic(args.workload, sha, launch_bytes))
+    prof = "prefill_2b_m512" if prefill else work.name
+    roof = roofline(ws.product_bytes(), ws.ops(), kern_avg,
+                    "mfma" if prefill else "hbm",
+                    load_profile(f"traffic_{prof}.json", sha,
+                                 "hbm_bytes_per_launch"))
+    if ceiling and not prefill:
+        roof["measured_ceiling_gb_s"] = ceiling["gb_s"]
+        roof["frac_of_measured_ceiling"] = round(
+            roof["achieved"] / ceiling["gb_s"], 4)
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": unit,
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -458,31 +626,57 @@ def main():
                    "launch": args.mode,
                    "product_kernel_ms": round(kern_avg, 5),
                    "tokens_per_s_equiv": round(work.m / (ms_step * 1e-3), 1),
-                   "tops": round(ws.ops() / (ms_step * 1e-3) / 1e12, 3)},
+                   "tops": round(ws.ops() / (kern_avg * 1e-3) / 1e12, 3)},
         "roofline": roof,
     }
+    if extra and args.mode == "grouped":
+        pl = per_launch_ms(ws, torch)
+        out["per_launch"] = {
+            "launches": len(ws.problems), "ms_per_pass": round(pl, 5),
+            "gb_s": round(ws.product_bytes() / (pl * 1e-3) / 1e9, 1),
+            "frac": round(ws.product_bytes() / (pl * 1e-3) / 1e9
+                          / HBM_PEAK_GBS, 4)}
+    if cpu:
+        log("[bench] timing the CPU oracle on a sample")
+        cb = cpu_baseline(work, ps, args.cpu_seconds, host_threads())
+        one = cpu_baseline(work, ps, args.cpu_seconds, 1)
+        cb["value_1_thread"] = one["value"]
+        cb["gmac_s_1_thread"] = one["gmac_s"]
+        cb["sample_1_thread"] = one["sample"]
+        out["cpu_baseline"] = cb
     del ws
     torch.cuda.empty_cache()
 
-    if not args.no_extra and not prefill:
+    if extra and work.name == "decode_2b_m1":
+        out["read_ceiling"] = ceiling
+        out["single_gemv"] = single_gemv(torch, bt)
+        cpu_s = 3.0 if cpu else 0.0
+        batched = {}
+        for m in (8, 16, 32):
+            bws = WorkSet(wl.decode_2b(m), ps, torch, bt)
+            batched[f"m{m}"] = config_entry(bws, torch, 20, 3, ceiling["gb_s"],
+                                            cpu_seconds=cpu_s, ps=ps)
+            del bws
+            torch.cuda.empty_cache()
+        out["batched_decode_2b"] = batched
         pw = wl.prefill_2b(512)
-        pws = WorkSet(pw, torch, bt, "grouped")
-        pwall, pk_avg = run_timed(pws, 20, 3, torch)
-        tops_k = pws.ops() / (pk_avg * 1e-3) / 1e12
-        out["prefill_m512"] = {
-            "workload": pw.name, "ms_per_step": round(pwall / 20 * 1e3, 4),
-            "product_kernel_ms": round(pk_avg, 5),
-            "tops_step": round(pws.ops() / (pwall / 20) / 1e12, 2),
-            "tops_kernel": round(tops_k, 2),
-            "frac_int8_peak": round(tops_k / INT8_PEAK_TOPS, 4),
-            "traffic": load_traffic(pw.name, sha, pws.product_bytes())}
-        del pws
+        pps = PackedSet(pw, torch, bt)
+        pws = WorkSet(pw, pps, torch, bt)
+        pe = config_entry(pws, torch, 20, 3, cpu_seconds=cpu_s, ps=pps)
+        pe["frac_int8_peak"] = pe["roofline"]["frac"]
+        pe["traffic"] = load_profile("traffic_prefill_2b_m512.json", sha,
+                                     "hbm_bytes_per_launch")
+        pe["roofline"]["traffic"] = pe["traffic"]
+        pe["mfma_busy"] = load_profile("counters_prefill_2b_m512.json", sha,
+                                       "mfma_busy")
+        out["prefill_m512"] = pe
+        del pws, pps
         torch.cuda.empty_cache()
-        if work.name.startswith("decode_2b_m1") and not args.no_chain:
+        if not args.no_chain:
             chained = {"workload": "decode_2b chained, M=1 (one token, every "
                                    "dependency kept)"}
             for fused in (False, True):
-                cs = ChainSet(work, torch, bt, fused=fused)
+                cs = ChainSet(work, torch, bt, fused=fused, ps=ps)
                 eager, graph = run_chain(cs, 20, 3, torch)
                 chained["fused" if fused else "two_launch"] = {
                     "layers": cs.layers, "launches_per_token": cs.launches(),
@@ -492,7 +686,22 @@ def main():
                 del cs
                 torch.cuda.empty_cache()
             out["chained_decode"] = chained
-            out["lut_ablation"] = lut_ablation(torch, bt)
+            out["format_ablation"] = format_ablation(torch, bt)
+        del ps
+        torch.cuda.empty_cache()
+        if not args.no_8b:
+            w8 = wl.decode_8b(1)
+            ps8 = PackedSet(w8, torch, bt)
+            d8 = {}
+            for m in (1, 64):
+                ws8 = WorkSet(wl.decode_8b(m), ps8, torch, bt)
+                d8[f"m{m}"] = config_entry(ws8, torch, 20, 3, ceiling["gb_s"],
+                                           cpu_seconds=cpu_s, ps=ps8)
+                del ws8
+                torch.cuda.empty_cache()
+            out["decode_8b"] = d8
+            del ps8
+            torch.cuda.empty_cache()
 
     if args.calibrate_copy:
         n = 256 << 20
@@ -504,9 +713,6 @@ def main():
         out["calibration_copy_bytes"] = n
         del src, dst
 
-    if not args.no_cpu_baseline:
-        log("[bench] timing the CPU oracle on a sample")
-        out["cpu_baseline"] = cpu_baseline(work, args.cpu_seconds)
     print(json.dumps(out), flush=True)
 
 

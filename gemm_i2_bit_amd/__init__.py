@@ -5,7 +5,7 @@ library's HIP kernels.  PyTorch supplies device memory and streams.
 Functions carry the C ABI's names (see include/bt.h for the contract):
 bt_pack_i2s, bt_quant_act, bt_quant_act_many, bt_gemv, bt_gemm,
 bt_grouped_plan, bt_grouped_plan_f32, bt_gemm_grouped, bt_packed_bytes,
-bt_status_str.
+bt_status_str, and the measurement helper bt_read_probe.
 """
 from __future__ import annotations
 
@@ -91,6 +91,14 @@ def lib() -> ctypes.CDLL:
         L.bt_grouped_plan_f32.restype = i32
         L.bt_gemm_grouped.argtypes = [p, p, p]
         L.bt_gemm_grouped.restype = i32
+        L.bt_b3_packed_bytes.argtypes = [i64, i64]
+        L.bt_b3_packed_bytes.restype = i64
+        L.bt_pack_b3.argtypes = [p, i64, i64, p, p, p]
+        L.bt_pack_b3.restype = i32
+        L.bt_gemv_b3.argtypes = [p, f32, i64, i64, p, p, p, p, p]
+        L.bt_gemv_b3.restype = i32
+        L.bt_read_probe.argtypes = [p, i64, p, i64, i32, i32, p]
+        L.bt_read_probe.restype = i32
         _lib = L
     return _lib
 
@@ -264,6 +272,48 @@ def bt_gemv_lut(packed, s_w, n: int, k: int, x_q, s_a, y=None, acc=None,
     return y, acc
 
 
+def bt_b3_packed_bytes(n: int, k: int) -> int:
+    r = lib().bt_b3_packed_bytes(n, k)
+    if r < 0:
+        raise BtError(r, "bt_b3_packed_bytes")
+    return r
+
+
+def bt_pack_b3(t, packed=None, n_invalid=None, stream=None):
+    """int8 trits [n, k] (GPU) -> uint8 packed five per byte (GPU,
+    bt_b3_packed_bytes)."""
+    torch = _torch()
+    n, k = t.shape
+    if packed is None:
+        packed = torch.empty(bt_b3_packed_bytes(n, k), dtype=torch.uint8,
+                             device=t.device)
+    if packed.numel() != bt_b3_packed_bytes(n, k):
+        raise ValueError("packed has the wrong size")
+    _check(lib().bt_pack_b3(_dev(t, torch.int8, "t"), n, k,
+                            _dev(packed, torch.uint8, "packed"),
+                            _dev(n_invalid, torch.int32, "n_invalid"),
+                            _stream(stream)), "bt_pack_b3")
+    return packed
+
+
+def bt_gemv_b3(packed, s_w, n: int, k: int, x_q, s_a, y=None, acc=None,
+               want_acc: bool = False, stream=None):
+    """bt_gemv over weights packed by bt_pack_b3."""
+    torch = _torch()
+    if x_q.numel() != k or s_a.numel() != 1:
+        raise ValueError("x_q or s_a has the wrong size")
+    if packed.numel() != bt_b3_packed_bytes(n, k):
+        raise ValueError("packed has the wrong size")
+    y, acc = _outputs(1, n, x_q.device, y, acc, want_acc)
+    _check(lib().bt_gemv_b3(_dev(packed, torch.uint8, "packed"), float(s_w),
+                            n, k, _dev(x_q, torch.int8, "x_q"),
+                            _dev(s_a, torch.float32, "s_a"),
+                            _dev(y, torch.float32, "y"),
+                            _dev(acc, torch.int32, "acc"), _stream(stream)),
+           "bt_gemv_b3")
+    return y, acc
+
+
 class GroupedPlan:
     """A grouped-product plan: the host image and its device copy.  Keeps
     references to every tensor the plan points at."""
@@ -345,3 +395,15 @@ def bt_gemm_grouped(plan: GroupedPlan, stream=None):
     _check(lib().bt_gemm_grouped(_dev(plan.dev, torch.uint8, "plan"),
                                  plan.host.ctypes.data, _stream(stream)),
            "bt_gemm_grouped")
+
+
+def bt_read_probe(buf, sink, waves_per_cu: int = 8, groups: int = 2,
+                  stream=None):
+    """Stream-read a uint8 GPU buffer once (the read-ceiling probe); sink is
+    an int32 GPU tensor with at least (compute units) * waves_per_cu
+    elements."""
+    torch = _torch()
+    _check(lib().bt_read_probe(_dev(buf, torch.uint8, "buf"), buf.numel(),
+                               _dev(sink, torch.int32, "sink"), sink.numel(),
+                               int(waves_per_cu), int(groups),
+                               _stream(stream)), "bt_read_probe")

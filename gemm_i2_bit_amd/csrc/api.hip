@@ -431,7 +431,7 @@ int32_t bt_grouped_plan_f32(const bt_problem_f32* probs, int32_t count,
   return build_plan(q.data(), count, plan, plan_bytes, xf.data());
 }
 
-int32_t bt_gemm_grouped(const void* plan_dev, const void* plan_host,
+int32_t bt_gemm_grouped(void* plan_dev, const void* plan_host,
                         void* stream) {
   if (!plan_dev || !plan_host) return BT_E_NULL;
   if (!aligned(plan_dev, 256)) return BT_E_ALIGN;
@@ -450,19 +450,18 @@ int32_t bt_gemm_grouped(const void* plan_dev, const void* plan_host,
     return BT_E_ARG;
   const int32_t arch = check_arch();
   if (arch != BT_OK) return arch;
-  const unsigned char* base = static_cast<const unsigned char*>(plan_dev);
+  unsigned char* base = static_cast<unsigned char*>(plan_dev);
   const Desc* descs = reinterpret_cast<const Desc*>(base + h.desc_off);
   const hipStream_t s = static_cast<hipStream_t>(stream);
   if (h.kind != bt::kKindDot4) {
     const Unit* units = reinterpret_cast<const Unit*>(base + h.unit_off);
-    unsigned char* mut = const_cast<unsigned char*>(base);
     return hip_status(bt::launch_tiled_grouped(
-        descs, units, h.units, h.m, reinterpret_cast<int32_t*>(mut + h.sacc_off),
-        reinterpret_cast<int32_t*>(mut + h.scnt_off), s));
+        descs, units, h.units, h.m,
+        reinterpret_cast<int32_t*>(base + h.sacc_off),
+        reinterpret_cast<int32_t*>(base + h.scnt_off), s));
   }
   const int cus = cu_count();
   if (cus <= 0) return BT_E_HIP;
-  unsigned char* mut = const_cast<unsigned char*>(base);
   // at least a group of 4 chunks per wave (counted in workgroups of 4 waves;
   // the launch may regroup the same waves): a wave's set-up and hand-offs
   // cost about what streaming a few chunks does, so small plans (one phase
@@ -471,8 +470,55 @@ int32_t bt_gemm_grouped(const void* plan_dev, const void* plan_host,
                                         (h.total_chunks + 15) / 16);
   return hip_status(bt::launch_stream_grouped(
       descs, reinterpret_cast<const int64_t*>(base + h.chunk_off), h.count,
-      h.total_chunks, h.m, reinterpret_cast<int32_t*>(mut + h.sacc_off),
+      h.total_chunks, h.m, reinterpret_cast<int32_t*>(base + h.sacc_off),
       (int)wgs, h.fused == 1, wgs == (int64_t)cus * bt::kStreamWgPerCu, s));
+}
+
+int64_t bt_b3_packed_bytes(int64_t n, int64_t k) {
+  if (!n_ok(n) || !k_ok(k)) return BT_E_SHAPE;
+  return bt::b3_packed_bytes(n, k);
+}
+
+int32_t bt_pack_b3(const int8_t* t, int64_t n, int64_t k, uint8_t* packed,
+                   int32_t* n_invalid, void* stream) {
+  if (!t || !packed) return BT_E_NULL;
+  if (!n_ok(n) || !k_ok(k)) return BT_E_SHAPE;
+  if (!aligned(packed, 16) || (n_invalid && !aligned(n_invalid, 4)))
+    return BT_E_ALIGN;
+  const int32_t arch = check_arch();
+  if (arch != BT_OK) return arch;
+  return hip_status(bt::launch_pack_b3(t, n, k, packed, n_invalid,
+                                       static_cast<hipStream_t>(stream)));
+}
+
+int32_t bt_gemv_b3(const uint8_t* packed, float s_w, int64_t n, int64_t k,
+                   const int8_t* x_q, const float* s_a, float* y, int32_t* acc,
+                   void* stream) {
+  const int32_t st = check_problem(packed, s_w, n, k, 1, x_q, s_a, y, acc);
+  if (st != BT_OK) return st;
+  const int32_t arch = check_arch();
+  if (arch != BT_OK) return arch;
+  const Desc d = make_desc(packed, s_w, n, k, 1, x_q, s_a, y, acc);
+  return hip_status(bt::launch_b3(d, static_cast<hipStream_t>(stream)));
+}
+
+int32_t bt_read_probe(const void* buf, int64_t bytes, uint32_t* sink,
+                      int64_t sink_words, int32_t waves_per_cu,
+                      int32_t groups, void* stream) {
+  if (!buf || !sink) return BT_E_NULL;
+  if (bytes < 1024 || bytes % 1024 != 0) return BT_E_SHAPE;
+  if (!aligned(buf, 16) || !aligned(sink, 4)) return BT_E_ALIGN;
+  if ((waves_per_cu != 4 && waves_per_cu != 8) || groups < 1 || groups > 4)
+    return BT_E_ARG;
+  const int32_t arch = check_arch();
+  if (arch != BT_OK) return arch;
+  const int cus = cu_count();
+  if (cus <= 0) return BT_E_HIP;
+  const int64_t waves = (int64_t)cus * waves_per_cu;
+  if (sink_words < waves) return BT_E_SHAPE;
+  return hip_status(bt::launch_read_probe(buf, bytes, sink, (int)waves,
+                                          waves_per_cu, groups,
+                                          static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

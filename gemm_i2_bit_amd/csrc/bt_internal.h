@@ -171,6 +171,13 @@ __device__ __forceinline__ uint32_t quant4(const float4& v, float inv) {
   }
   return packed4;
 }
+// five-trits-per-byte comparison format (gemv_b3.hip)
+int64_t b3_packed_bytes(int64_t n, int64_t k);
+hipError_t launch_pack_b3(const int8_t* t, int64_t n, int64_t k,
+                          uint8_t* packed, int32_t* n_invalid, hipStream_t s);
+hipError_t launch_b3(const Desc& d, hipStream_t s);  // m = 1 only
+hipError_t launch_read_probe(const void* buf, int64_t bytes, uint32_t* sink,
+                             int waves, int wpw, int groups, hipStream_t s);
 hipError_t launch_tiled(const Desc& d, hipStream_t s);
 hipError_t launch_tiled_grouped(const Desc* descs, const Unit* units,
                                 int64_t count, int m, int32_t* sacc,

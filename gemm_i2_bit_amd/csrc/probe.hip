@@ -1,0 +1,97 @@
+// Streaming-read probe: the HBM read rate that a pure sequential read of a
+// device buffer reaches on this GPU, measured with the same access pattern as
+// the decode kernel's weight stream (persistent waves, each streaming one
+// contiguous range in 1 KiB steps with non-temporal 128-bit buffer loads, in
+// groups of four loads, 1 to 4 groups in flight).  The ternary GEMV is bound by this rate
+// ("1bit-systems" page, section "性能实测：92%的内存带宽利用率": the GEMV
+// saturates memory bandwidth), so the benchmark reports its products as a
+// fraction of the nameplate peak and of this measured ceiling.  Nothing of
+// the product path uses this kernel.
+#include "bt_internal.h"
+
+namespace bt {
+namespace {
+
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
+constexpr int kRsrcFlags = 0x00020000;  // raw buffer, 32-bit words
+constexpr int D = 4;                     // 1 KiB steps per load group
+
+__device__ __forceinline__ void load_group(v4u (&buf)[D], const uint8_t* base,
+                                           int64_t chunk, int cnt) {
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(base + chunk * 1024), 0, cnt * 1024, kRsrcFlags);
+  const int lane16 = (threadIdx.x & 63) * 16;
+#pragma unroll
+  for (int j = 0; j < D; ++j)
+    buf[j] = __builtin_bit_cast(
+        v4u, __builtin_amdgcn_raw_buffer_load_b128(r, lane16 + j * 1024, 0, 2));
+}
+
+// Steps of a group starting at step `at` of a range ending at `hi` (0..D).
+__device__ __forceinline__ int group_cnt(int64_t at, int64_t hi) {
+  const int64_t left = hi - at;
+  return left <= 0 ? 0 : (left >= D ? D : (int)left);
+}
+
+__device__ __forceinline__ uint32_t fold(const v4u (&buf)[D]) {
+  uint32_t x = 0;
+#pragma unroll
+  for (int j = 0; j < D; ++j) x ^= buf[j].x ^ buf[j].y ^ buf[j].z ^ buf[j].w;
+  return x;
+}
+
+// Wave w of W reads 1 KiB steps [w T / W, (w + 1) T / W), with G groups of
+// D loads in flight, and writes the XOR of every word it read to sink[w]
+// (so that no load is dead).
+template <int WPW, int G>
+__global__ __launch_bounds__(64 * WPW) void read_probe_kernel(
+    const uint8_t* __restrict__ buf, int64_t total, uint32_t* sink) {
+  const int64_t W = (int64_t)gridDim.x * WPW;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t wv = (int64_t)blockIdx.x * WPW + wave;
+  const int64_t lo = wv * total / W, hi = (wv + 1) * total / W;
+  uint32_t x = 0;
+  v4u ring[G][D];
+#pragma unroll
+  for (int g = 0; g < G; ++g) load_group(ring[g], buf, lo + g * D,
+                                         group_cnt(lo + g * D, hi));
+  for (int64_t pos = lo; pos < hi; pos += G * D) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      // group g of this round holds steps pos + g D ..; once folded, its
+      // buffer takes the group G rounds ahead
+      x ^= fold(ring[g]);
+      const int64_t next = pos + (g + G) * D;
+      load_group(ring[g], buf, next, group_cnt(next, hi));
+    }
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) x ^= __shfl_xor(x, off, 64);
+  if ((threadIdx.x & 63) == 0) sink[wv] = x;
+}
+
+template <int WPW>
+void launch_wpw(const uint8_t* b, int64_t steps, uint32_t* sink, int waves,
+                int groups, hipStream_t s) {
+  const dim3 grid((unsigned)(waves / WPW)), block(64 * WPW);
+  switch (groups) {
+    case 1: read_probe_kernel<WPW, 1><<<grid, block, 0, s>>>(b, steps, sink); break;
+    case 2: read_probe_kernel<WPW, 2><<<grid, block, 0, s>>>(b, steps, sink); break;
+    case 3: read_probe_kernel<WPW, 3><<<grid, block, 0, s>>>(b, steps, sink); break;
+    default: read_probe_kernel<WPW, 4><<<grid, block, 0, s>>>(b, steps, sink); break;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_read_probe(const void* buf, int64_t bytes, uint32_t* sink,
+                             int waves, int wpw, int groups, hipStream_t s) {
+  const uint8_t* b = static_cast<const uint8_t*>(buf);
+  if (wpw == 8)
+    launch_wpw<8>(b, bytes / 1024, sink, waves, groups, s);
+  else
+    launch_wpw<4>(b, bytes / 1024, sink, waves, groups, s);
+  return hipGetLastError();
+}
+
+}  // namespace bt

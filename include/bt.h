@@ -156,8 +156,9 @@ typedef struct bt_problem {
  * decode step whose projections are each too small to fill the GPU.
  * Use: bytes = bt_grouped_plan_bytes(probs, count); fill a host buffer of that
  * size with bt_grouped_plan (pure host code, no HIP call); copy it to device
- * memory the caller owns (256-byte aligned); then call
- * bt_gemm_grouped(plan_dev, plan_host, s) as often as wanted.  The plan holds
+ * memory the caller owns (256-byte aligned, writable: every launch writes
+ * the plan's scratch area); then call bt_gemm_grouped(plan_dev, plan_host, s)
+ * as often as wanted.  The plan holds
  * the problem descriptors (pointers, shapes, scales), the work order and a
  * scratch area through which workgroups that share part of the work combine
  * their partial sums: with packed dot products, m * 512 bytes per 64-row
@@ -178,13 +179,13 @@ typedef struct bt_problem {
 int64_t bt_grouped_plan_bytes(const bt_problem* probs, int32_t count);
 int32_t bt_grouped_plan(const bt_problem* probs, int32_t count, void* plan,
                         int64_t plan_bytes);
-int32_t bt_gemm_grouped(const void* plan_dev, const void* plan_host,
+int32_t bt_gemm_grouped(void* plan_dev, const void* plan_host,
                         void* stream);
 
 /* Grouped decode product that quantizes its own activations (the per-token
- * int8 absmax step and the ternary product in one launch: the activation
- * quantization of "Microsoft BitNet" section "技术实现细节" fused into the
- * GEMV).  Each problem gives fp32 activations x [m, k] instead of x_q and
+ * int8 absmax step and the ternary product in one launch: the 8-bit
+ * activation quantization of "BitNet-rs：Rust实现的高效1比特大语言模型推理
+ * 引擎", section "技术实现细节", fused into the GEMV).  Each problem gives fp32 activations x [m, k] instead of x_q and
  * s_a; the launch quantizes every token row exactly as bt_quant_act would
  * (same x_q, same s_a, bit for bit) and then computes what bt_gemm would
  * with them.  Neither x_q nor s_a is written out.
@@ -207,6 +208,52 @@ typedef struct bt_problem_f32 {
 int64_t bt_grouped_plan_f32_bytes(const bt_problem_f32* probs, int32_t count);
 int32_t bt_grouped_plan_f32(const bt_problem_f32* probs, int32_t count,
                             void* plan, int64_t plan_bytes);
+
+/* Fewer-bytes format, for comparison: five trits per byte in base 3
+ * (1.6 bits per weight, a fifth fewer bytes than bt_pack_i2s when k is a
+ * multiple of 80).  The M=1 product is bound by the bytes it reads
+ * ("1bit-systems：在AMD Strix Halo上实现纯Rust本地三值权重LLM推理", section
+ * "性能实测：92%的内存带宽利用率"), and the CPU kernels of "BitNet 1 位 LLM
+ * 独立推理引擎：位串行 GEMM 内核与 LUT 优化工程实践" (body) pack three weights
+ * into one index (TL2) to read a sixth fewer bytes; this format takes the
+ * same lever further, at the cost of decoding base-3 digits.
+ * Layout: rows padded to a multiple of 64 and inputs to a multiple of 80,
+ * with trit 0.  Row block b occupies bytes [b * 64 * P * 16,
+ * (b + 1) * 64 * P * 16), P = ceil(k / 80); inside it, the 16-byte piece
+ * holding inputs [80 p, 80 p + 80) of row r sits at offset
+ * (p * 64 + r % 64) * 16; byte 4 u + i of a piece holds inputs
+ * 80 p + 20 u + 4 j + i, j = 0..4, as the base-3 number
+ * v = sum_j (trit + 1) * 3^(4 - j), stored as ceil(v * 256 / 243).
+ * bt_b3_packed_bytes: ceil(n / 64) * 64 * ceil(k / 80) * 16, or BT_E_SHAPE
+ * under the rules of bt_packed_bytes.
+ * bt_pack_b3: as bt_pack_i2s (same arguments and rules), writing this
+ * format; entries outside {-1, 0, 1} are counted in *n_invalid and stored
+ * as trit 0.
+ * bt_gemv_b3: bt_gemv (same arguments, rules and results, bit for bit) over
+ * weights packed by bt_pack_b3. */
+int64_t bt_b3_packed_bytes(int64_t n, int64_t k);
+int32_t bt_pack_b3(const int8_t* t, int64_t n, int64_t k, uint8_t* packed,
+                   int32_t* n_invalid, void* stream);
+int32_t bt_gemv_b3(const uint8_t* packed, float s_w, int64_t n, int64_t k,
+                   const int8_t* x_q, const float* s_a, float* y, int32_t* acc,
+                   void* stream);
+
+/* Measurement helper, not part of the product path: reads `bytes` of device
+ * memory at buf once, with the access pattern of the decode kernel's weight
+ * stream (persistent waves, waves_per_cu of them per compute unit, each
+ * streaming one contiguous range with non-temporal 128-bit loads, 1 KiB per
+ * wave and load, in groups of four loads of which `groups` are in flight),
+ * and writes one XOR of the words each wave read to sink[wave].  Timing it
+ * gives the streaming-read ceiling of the GPU it runs on, against which the
+ * ternary GEMV, a bandwidth-bound kernel ("1bit-systems" page, section
+ * "性能实测：92%的内存带宽利用率"), is compared.
+ *  buf         device, 16-byte aligned; bytes >= 1024 and bytes % 1024 == 0.
+ *  sink        device uint32 [sink_words], 4-byte aligned; sink_words must be
+ *              at least (compute units) * waves_per_cu, else BT_E_SHAPE.
+ *  waves_per_cu  4 or 8; groups 1 to 4; else BT_E_ARG. */
+int32_t bt_read_probe(const void* buf, int64_t bytes, uint32_t* sink,
+                      int64_t sink_words, int32_t waves_per_cu,
+                      int32_t groups, void* stream);
 
 #ifdef __cplusplus
 }

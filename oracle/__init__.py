@@ -46,6 +46,12 @@ def lib() -> ctypes.CDLL:
         L.oracle_pack_i2s.restype = i64
         L.oracle_unpack_i2s.argtypes = [p, i64, i64, p]
         L.oracle_unpack_i2s.restype = i64
+        L.oracle_b3_packed_bytes.argtypes = [i64, i64]
+        L.oracle_b3_packed_bytes.restype = i64
+        L.oracle_pack_b3.argtypes = [p, i64, i64, p]
+        L.oracle_pack_b3.restype = i64
+        L.oracle_unpack_b3.argtypes = [p, i64, i64, p]
+        L.oracle_unpack_b3.restype = i64
         L.oracle_quant_act.argtypes = [p, i64, i64, p, p]
         L.oracle_quant_act.restype = i32
         L.oracle_gemm.argtypes = [p, ctypes.c_float, i64, i64, i64, p, p, i64,
@@ -96,6 +102,33 @@ def unpack_i2s(packed, n: int, k: int):
         raise ValueError("packed size does not match n, k")
     t = np.empty((n, k), np.int8)
     bad = lib().oracle_unpack_i2s(_ptr(packed), n, k, _ptr(t))
+    return t, int(bad)
+
+
+def b3_packed_bytes(n: int, k: int) -> int:
+    """Size of the base-3 layout (five trits per byte; rows padded to 64,
+    inputs to 80)."""
+    return int(lib().oracle_b3_packed_bytes(n, k))
+
+
+def pack_b3(t):
+    """Five trits per byte: int8 trits [n, k] -> (uint8 packed, invalid
+    count)."""
+    t = _c(t, np.int8)
+    n, k = t.shape
+    out = np.empty(b3_packed_bytes(n, k), np.uint8)
+    bad = lib().oracle_pack_b3(_ptr(t), n, k, _ptr(out))
+    return out, int(bad)
+
+
+def unpack_b3(packed, n: int, k: int):
+    """Inverse of pack_b3 -> (int8 trits [n, k], count of bytes the packer
+    cannot have written)."""
+    packed = _c(packed, np.uint8).ravel()
+    if packed.size != b3_packed_bytes(n, k):
+        raise ValueError("packed size does not match n, k")
+    t = np.empty((n, k), np.int8)
+    bad = lib().oracle_unpack_b3(_ptr(packed), n, k, _ptr(t))
     return t, int(bad)
 
 

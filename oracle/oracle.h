@@ -51,6 +51,31 @@ int64_t oracle_pack_i2s(const int8_t* t, int64_t n, int64_t k, uint8_t* packed);
 int64_t oracle_unpack_i2s(const uint8_t* packed, int64_t n, int64_t k,
                           int8_t* t);
 
+/* Fewer-bytes packing (base 3, five trits per byte), the comparison format
+ * of the "fewer bytes" lever: "1bit-systems：在AMD Strix Halo上实现纯Rust本地
+ * 三值权重LLM推理", section "性能实测：92%的内存带宽利用率" (the GEMV is bound
+ * by the bytes it reads), and "BitNet 1 位 LLM 独立推理引擎：位串行 GEMM 内核
+ * 与 LUT 优化工程实践" (body: TL2 groups three weights into one index and
+ * needs a sixth less bandwidth than 2 bits per weight).  Five trits per byte
+ * is 1.6 bits per weight: 3^5 = 243 <= 256.
+ * Layout: rows padded to np = ceil(n / 64) * 64 (trit 0); inputs padded to
+ * kp = ceil(k / 80) * 80 (trit 0).  Row block b = r / 64 occupies bytes
+ * [b * 64 * kp / 5, (b + 1) * 64 * kp / 5); inside it the 16-byte piece
+ * holding inputs [80 p, 80 p + 80) of row r sits at offset
+ * (p * 64 + r % 64) * 16.  Inside a piece, byte 4 u + i (u < 4, i < 4) holds
+ * the five inputs 80 p + 20 u + 4 j + i, j = 0..4, as the base-3 number
+ * v = sum_j c_j * 3^(4 - j) (c = trit + 1, j = 0 most significant), stored
+ * as the byte ceil(v * 256 / 243).  Decoding a byte x: for j = 0..4,
+ * c_j = (3 x) >> 8 and x = (3 x) & 255.  Returns the number of entries
+ * outside {-1, 0, 1}; they are encoded as trit 0. */
+int64_t oracle_b3_packed_bytes(int64_t n, int64_t k);
+int64_t oracle_pack_b3(const int8_t* t, int64_t n, int64_t k, uint8_t* packed);
+/* Inverse of oracle_pack_b3 for the first n rows and k inputs.  A byte whose
+ * decoded digits do not re-encode to it (not produced by the packer) is
+ * counted; returns the count. */
+int64_t oracle_unpack_b3(const uint8_t* packed, int64_t n, int64_t k,
+                         int8_t* t);
+
 /* O3: per-row (per token) absmax quantization of fp32 x [m, k] to int8.
  * amax = max |x|, a = max(amax, 1e-5f), inv = 127.0f / a (fp32),
  * q = clamp(rne(x * inv), -127, 127) (fp32 product), s_a = a / 127.0f. */

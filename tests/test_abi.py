@@ -396,3 +396,34 @@ def test_grouped_plan_kind_by_m_and_size(L):
         k = 16384 // m // 64 * 64
         assert kind([(65536, k, m)], f32=True) == (0, 1024 * (k // 64), 1)
     assert kind([(64, 64, 5)])[0] == 1
+
+
+def test_read_probe_argument_errors(L):
+    g = L.bt_read_probe
+    assert g(None, 1024, P, 4096, 8, 2, None) == bt.BT_E_NULL
+    assert g(P, 1024, None, 4096, 8, 2, None) == bt.BT_E_NULL
+    for nbytes in (0, 512, 1000, 1024 + 16):
+        assert g(P, nbytes, P, 4096, 8, 2, None) == bt.BT_E_SHAPE, nbytes
+    assert g(P + 8, 1024, P, 4096, 8, 2, None) == bt.BT_E_ALIGN
+    assert g(P, 1024, P + 2, 4096, 8, 2, None) == bt.BT_E_ALIGN
+    for wpc in (0, 1, 2, 3, 5, 16):
+        assert g(P, 1024, P, 4096, wpc, 2, None) == bt.BT_E_ARG, wpc
+    for groups in (0, 5, -1):
+        assert g(P, 1024, P, 4096, 4, groups, None) == bt.BT_E_ARG, groups
+
+
+def test_b3_sizes_and_argument_errors(L):
+    assert L.bt_b3_packed_bytes(64, 80 * 4) == 64 * 4 * 16
+    assert L.bt_b3_packed_bytes(70, 64) == 128 * 16      # 64 inputs -> 80
+    assert L.bt_b3_packed_bytes(2560, 6912) == 2560 * 87 * 16
+    for n, k in [(0, 64), (1, 32), (1, 100), (1, 65536 + 64)]:
+        assert L.bt_b3_packed_bytes(n, k) == bt.BT_E_SHAPE
+    assert L.bt_pack_b3(None, 64, 64, P, None, None) == bt.BT_E_NULL
+    assert L.bt_pack_b3(P, 64, 100, P, None, None) == bt.BT_E_SHAPE
+    assert L.bt_pack_b3(P, 64, 64, P + 8, None, None) == bt.BT_E_ALIGN
+    g = L.bt_gemv_b3
+    assert g(None, 0.5, 64, 64, P, P, P, None, None) == bt.BT_E_NULL
+    assert g(P, 0.5, 64, 100, P, P, P, None, None) == bt.BT_E_SHAPE
+    assert g(P + 4, 0.5, 64, 64, P, P, P, None, None) == bt.BT_E_ALIGN
+    assert g(P, -1.0, 64, 64, P, P, P, None, None) == bt.BT_E_ARG
+    assert g(P, float("nan"), 64, 64, P, P, P, None, None) == bt.BT_E_ARG

@@ -58,6 +58,61 @@ def check_guards(buf, fill):
             "write outside the output"
 
 
+class Arena:
+    """The outputs of one grouped plan carved from one device buffer per
+    dtype, each output 16-byte aligned, with GAP guard elements before,
+    between and after them (NaN for fp32, a sentinel for int32).  check()
+    asserts that no guard element changed, so a store anywhere outside a
+    problem's own outputs but inside the arena is caught."""
+    GAP = 64  # elements (256 bytes)
+
+    def __init__(self, sizes, dtype, fill):
+        self.dtype, self.fill = dtype, fill
+        offs, pos = [], self.GAP
+        for s in sizes:
+            offs.append(pos)
+            pos += (s + 3) // 4 * 4 + self.GAP
+        self.buf = torch.full((pos,), fill, dtype=dtype, device="cuda:0")
+        self.views = [self.buf[o:o + s] for o, s in zip(offs, sizes)]
+        mask = np.zeros(pos, bool)
+        for o, s in zip(offs, sizes):
+            mask[o:o + s] = True
+        self.mask = mask
+
+    def reset(self):
+        for v in self.views:
+            v.fill_(self.fill)
+
+    def check(self):
+        guards = self.buf.cpu().numpy()[~self.mask]
+        if self.dtype == torch.float32:
+            assert np.isnan(guards).all(), "write outside the outputs"
+        else:
+            assert (guards == self.fill).all(), "write outside the outputs"
+
+
+class OutSet:
+    """y and acc arenas for a list of (m, n) outputs."""
+
+    def __init__(self, shapes):
+        self.y = Arena([m * n for m, n in shapes], torch.float32,
+                       float("nan"))
+        self.acc = Arena([m * n for m, n in shapes], torch.int32, 0x7EADBEEF)
+        self.shapes = shapes
+
+    def out(self, i):
+        m, n = self.shapes[i]
+        return self.y.views[i].view(m, n), self.acc.views[i].view(m, n)
+
+    def reset(self):
+        self.y.reset()
+        self.acc.reset()
+
+    def check(self):
+        self.y.check()
+        self.acc.check()
+
+
 def check_y(y_gpu, y_ref, acc_ref):
     y_gpu = np.asarray(y_gpu, np.float64)
     zero = acc_ref == 0
@@ -279,94 +334,118 @@ def test_gemv_lut_matches_oracle(n, k):
         assert acc_r[0, 2] == 0
 
 
+@pytest.mark.parametrize("n,k", [(200, 192), (64, 64), (130, 2560),
+                                 (70, 6912), (300, 4096), (66, 65536)])
+def test_gemv_b3_matches_oracle(n, k):
+    """The five-trits-per-byte format: packed bytes equal the oracle's
+    packing bit for bit (and unpack to the trits), and the product equals
+    the oracle's accumulators exactly and bt_gemv's outputs bit for bit;
+    k that is not a multiple of 80 leaves a padded last piece; at the
+    largest k, all +1, all -1 and zero rows against all-127 activations."""
+    rng = np.random.default_rng([115, n, k])
+    t = wl.trits(rng, (n, k), wl.DECODE_2B)
+    x = wl.x_normal_outliers(rng, (1, k))
+    if k == 65536:
+        t[0], t[1], t[2] = 1, -1, 0
+        x[0] = 1.0
+    s_w = wl.scale(rng, 0.01, 0.05)
+    n_bad = torch.zeros(1, dtype=torch.int32, device="cuda:0")
+    pbuf, packed = guarded(bt.bt_b3_packed_bytes(n, k), torch.uint8, 0xA5)
+    bt.bt_pack_b3(dev(t), packed=packed, n_invalid=n_bad)
+    p_ref, bad = oracle.pack_b3(t)
+    assert bad == 0 and int(n_bad.item()) == 0
+    np.testing.assert_array_equal(packed.cpu().numpy(), p_ref)
+    check_guards(pbuf, 0xA5)
+    back, bad = oracle.unpack_b3(packed.cpu().numpy(), n, k)
+    assert bad == 0
+    np.testing.assert_array_equal(back, t)
+    x_q, s_a = bt.bt_quant_act(dev(x))
+    ybuf, y = guarded(n, torch.float32, float("nan"))
+    abuf, acc = guarded(n, torch.int32, 0x7EADBEEF)
+    bt.bt_gemv_b3(packed, s_w, n, k, x_q[0], s_a, y=y.view(1, n),
+                  acc=acc.view(1, n))
+    y2, a2 = bt.bt_gemv(bt.bt_pack_i2s(dev(t)), s_w, n, k, x_q[0], s_a,
+                        want_acc=True)
+    torch.cuda.synchronize()
+    check_guards(ybuf, None)
+    check_guards(abuf, 0x7EADBEEF)
+    _, _, _, acc_r, y_r = oracle_product(t, x, s_w)
+    np.testing.assert_array_equal(acc.view(1, n).cpu().numpy(), acc_r)
+    check_y(y.view(1, n).cpu().numpy(), y_r, acc_r)
+    assert torch.equal(acc.view(1, n), a2) and torch.equal(y.view(1, n), y2)
+    if k == 65536:
+        assert acc_r[0, 0] == 127 * k and acc_r[0, 1] == -127 * k
+        assert acc_r[0, 2] == 0
+
+
+def test_pack_b3_counts_invalid():
+    t = np.zeros((70, 128), np.int8)
+    t[3, 5], t[69, 127], t[10, 64] = 2, -2, 100
+    n_bad = torch.zeros(1, dtype=torch.int32, device="cuda:0")
+    packed = bt.bt_pack_b3(dev(t), n_invalid=n_bad)
+    assert int(n_bad.item()) == 3
+    back, _ = oracle.unpack_b3(packed.cpu().numpy(), 70, 128)
+    assert back[3, 5] == 0 and back[69, 127] == 0 and back[10, 64] == 0
+
+
 # ------------------------------------------------------------ grouped calls
-def grouped_case(work, layers):
-    """Upload, pack and quantize `layers` layers of a workload; return the
-    problem dicts and the host inputs per problem."""
-    probs, host = [], []
-    for p in work.problems():
-        if p.layer >= layers:
-            continue
-        t, s_w = work.weights(p.layer, p.proj)
-        x = work.activations(p.layer, p.proj)
-        packed = bt.bt_pack_i2s(dev(t))
-        x_q, s_a = bt.bt_quant_act(dev(x))
-        y = torch.full((p.m, p.n), float("nan"), device="cuda:0")
-        acc = torch.full((p.m, p.n), 0x7EADBEEF, dtype=torch.int32,
-                         device="cuda:0")
-        probs.append(dict(packed=packed, s_w=s_w, n=p.n, k=p.k, x_q=x_q,
-                          s_a=s_a, y=y, acc=acc))
-        host.append((t, x, s_w))
-    return probs, host
+def launch_and_check(plan, probs, outs, refs, launches=2, label=""):
+    """Launch `plan` `launches` times; before each launch every output is
+    reset to its guard fill; after it every output must match its reference
+    (acc_r, y_r) and every guard element of the arenas must be untouched.
+    refs[i] is a list of (r0, r1, acc_r, y_r) row spans of problem i."""
+    for launch in range(launches):
+        outs.reset()
+        bt.bt_gemm_grouped(plan)
+        torch.cuda.synchronize()
+        for i, (prob, spans) in enumerate(zip(probs, refs)):
+            acc = prob["acc"].cpu().numpy()
+            y = prob["y"].cpu().numpy()
+            for r0, r1, acc_r, y_r in spans:
+                assert np.array_equal(acc[:, r0:r1], acc_r), \
+                    f"{label} launch {launch} problem {i} rows {r0}..{r1}"
+                check_y(y[:, r0:r1], y_r, acc_r)
+        outs.check()
+
+
+def grouped_problems(cases, m, fused=False):
+    """cases: list of (t, x, s_w) host inputs.  Packs, quantizes (unless
+    fused) and returns (problem dicts, OutSet, whole-output references)."""
+    outs = OutSet([(m, t.shape[0]) for t, _, _ in cases])
+    probs, refs = [], []
+    for i, (t, x, s_w) in enumerate(cases):
+        y, acc = outs.out(i)
+        prob = dict(packed=bt.bt_pack_i2s(dev(t)), s_w=s_w, n=t.shape[0],
+                    k=t.shape[1], y=y, acc=acc)
+        if fused:
+            prob["x"] = dev(x)
+        else:
+            prob["x_q"], prob["s_a"] = bt.bt_quant_act(dev(x))
+        probs.append(prob)
+        _, _, _, acc_r, y_r = oracle_product(t, x, s_w)
+        refs.append([(0, t.shape[0], acc_r, y_r)])
+    return probs, outs, refs
+
+
+def grouped_plan(probs, fused=False):
+    return (bt.bt_grouped_plan_f32(probs) if fused
+            else bt.bt_grouped_plan(probs))
 
 
 @pytest.mark.parametrize("m,layers", [(1, 2), (3, 2), (8, 2), (16, 2),
                                       (32, 2), (40, 1), (64, 1), (130, 1)])
 def test_grouped_layers_match_oracle(m, layers):
     work = wl.decode_2b(m=m, layers=layers)
-    probs, host = grouped_case(work, layers)
-    plan = bt.bt_grouped_plan(probs)
-    refs = [oracle_product(t, x, s_w) for t, x, s_w in host]
-    for _ in range(2):  # the plan is reusable; each launch writes everything
-        for p in probs:
-            p["y"].fill_(float("nan"))
-            p["acc"].fill_(0x7EADBEEF)
-        bt.bt_gemm_grouped(plan)
-        torch.cuda.synchronize()
-        for prob, (_, q_r, s_r, acc_r, y_r) in zip(probs, refs):
-            np.testing.assert_array_equal(prob["x_q"].cpu().numpy(), q_r)
-            np.testing.assert_array_equal(prob["acc"].cpu().numpy(), acc_r)
-            check_y(prob["y"].cpu().numpy(), y_r, acc_r)
-
-
-@pytest.mark.parametrize("m,fused", [(1, False), (2, False), (4, False),
-                                     (8, False), (32, False), (1, True)])
-def test_decode_set_grouped_full_size(m, fused):
-    """The whole 2B-shaped decode set (30 layers x 7 projections, 521 MB of
-    packed weights) in one grouped launch, as the benchmark runs it, three
-    times in a row; every output of every launch against the oracle.  M=1
-    streams with dot products; M=2 and 4 (sets this large) and the batched
-    decode sizes M=8 and 32 run on the matrix cores.  To
-    keep the host side short, the 30 layers share layer 0's seven weight
-    tensors (the launch still streams 521 MB); every (layer, projection) has
-    its own activations.  fused: the launch quantizes the fp32 activations
-    itself."""
-    work = wl.decode_2b(m=m)
-    shared = {}
+    cases = []
     for p in work.problems():
-        if p.layer == 0:
-            t, s_w = work.weights(0, p.proj)
-            shared[p.proj] = (t, s_w, bt.bt_pack_i2s(dev(t)),
-                              oracle.pack_i2s(t)[0])
-    probs, refs = [], []
-    for p in work.problems():
-        t, s_w, packed, packed_ref = shared[p.proj]
-        x = work.activations(p.layer, p.proj)
-        prob = dict(packed=packed, s_w=s_w, n=p.n, k=p.k,
-                    y=torch.empty((m, p.n), device="cuda:0"),
-                    acc=torch.empty((m, p.n), dtype=torch.int32,
-                                    device="cuda:0"))
-        if fused:
-            prob["x"] = dev(x)
-        else:
-            prob["x_q"], prob["s_a"] = bt.bt_quant_act(dev(x))
-        probs.append(prob)
-        q_r, sa_r = oracle.quant_act(x)
-        acc_r, y_r = oracle.gemm(packed_ref, s_w, p.n, p.k, q_r, sa_r,
-                                 nthreads=NTHREADS)
-        refs.append((acc_r, y_r))
-    plan = (bt.bt_grouped_plan_f32(probs) if fused
-            else bt.bt_grouped_plan(probs))
-    for launch in range(3):
-        for p in probs:
-            p["y"].fill_(float("nan"))
-            p["acc"].fill_(0x7EADBEEF)
-        bt.bt_gemm_grouped(plan)
-        torch.cuda.synchronize()
-        for i, (prob, (acc_r, y_r)) in enumerate(zip(probs, refs)):
-            acc = prob["acc"].cpu().numpy()
-            assert np.array_equal(acc, acc_r), f"launch {launch} problem {i}"
-            check_y(prob["y"].cpu().numpy(), y_r, acc_r)
+        t, s_w = work.weights(p.layer, p.proj)
+        cases.append((t, work.activations(p.layer, p.proj), s_w))
+    probs, outs, refs = grouped_problems(cases, m)
+    for prob, (t, x, _) in zip(probs, cases):
+        q_r, _ = oracle.quant_act(x)
+        np.testing.assert_array_equal(prob["x_q"].cpu().numpy(), q_r)
+    # the plan is reusable; each launch writes everything
+    launch_and_check(bt.bt_grouped_plan(probs), probs, outs, refs)
 
 
 @pytest.mark.parametrize("m", [1, 2, 3, 4, 5, 8, 32, 33, 64])
@@ -375,30 +454,16 @@ def test_grouped_small_problems(m):
     rows, k of one chunk): row blocks shared by many waves; each plan is
     launched twice to check that the scratch area is left clean."""
     specs = [(512, 256), (64, 64), (70, 192), (1, 64), (130, 320)]
-    probs, host = [], []
+    cases = []
     for i, (n, k) in enumerate(specs):
         rng = np.random.default_rng([107, m, i])
-        t = wl.trits(rng, (n, k), wl.DECODE_2B)
-        x = wl.x_normal_outliers(rng, (m, k))
-        s_w = wl.scale(rng, 0.01, 0.05)
-        x_q, s_a = bt.bt_quant_act(dev(x))
-        probs.append(dict(packed=bt.bt_pack_i2s(dev(t)), s_w=s_w, n=n, k=k,
-                          x_q=x_q, s_a=s_a,
-                          y=torch.full((m, n), float("nan"), device="cuda:0"),
-                          acc=torch.full((m, n), 0x7EADBEEF, dtype=torch.int32,
-                                         device="cuda:0")))
-        host.append((t, x, s_w))
-    for sub in (probs[:1], probs):
-        plan = bt.bt_grouped_plan(sub)
-        for _ in range(2):
-            for p in sub:
-                p["y"].fill_(float("nan"))
-            bt.bt_gemm_grouped(plan)
-            torch.cuda.synchronize()
-            for prob, (t, x, s_w) in zip(sub, host):
-                _, q_r, s_r, acc_r, y_r = oracle_product(t, x, s_w)
-                np.testing.assert_array_equal(prob["acc"].cpu().numpy(), acc_r)
-                check_y(prob["y"].cpu().numpy(), y_r, acc_r)
+        cases.append((wl.trits(rng, (n, k), wl.DECODE_2B),
+                      wl.x_normal_outliers(rng, (m, k)),
+                      wl.scale(rng, 0.01, 0.05)))
+    probs, outs, refs = grouped_problems(cases, m)
+    for cnt in (1, len(probs)):
+        launch_and_check(bt.bt_grouped_plan(probs[:cnt]), probs[:cnt], outs,
+                         refs[:cnt])
 
 
 @pytest.mark.parametrize("m", [1, 4, 8, 130])
@@ -420,34 +485,16 @@ def test_grouped_extremes(m):
         x[1] = -1.0
     if m > 2:
         x[2] = 0.0
-    t2 = wl.trits(rng, (64, 64))
-    x2 = wl.x_normal(rng, (m, 64))
-    cases = [(t, x, np.float32(1.0)), (t2, x2, np.float32(0.02))]
-    probs = []
-    for tt, xx, s_w in cases:
-        x_q, s_a = bt.bt_quant_act(dev(xx))
-        probs.append(dict(packed=bt.bt_pack_i2s(dev(tt)), s_w=s_w,
-                          n=tt.shape[0], k=tt.shape[1], x_q=x_q, s_a=s_a,
-                          y=torch.full((m, tt.shape[0]), float("nan"),
-                                       device="cuda:0"),
-                          acc=torch.full((m, tt.shape[0]), 0x7EADBEEF,
-                                         dtype=torch.int32, device="cuda:0")))
-    plan = bt.bt_grouped_plan(probs)
-    for _ in range(2):
-        for p in probs:
-            p["y"].fill_(float("nan"))
-        bt.bt_gemm_grouped(plan)
-        torch.cuda.synchronize()
-        for prob, (tt, xx, s_w) in zip(probs, cases):
-            _, _, _, acc_r, y_r = oracle_product(tt, xx, s_w)
-            acc = prob["acc"].cpu().numpy()
-            np.testing.assert_array_equal(acc, acc_r)
-            check_y(prob["y"].cpu().numpy(), y_r, acc_r)
-        acc = probs[0]["acc"].cpu().numpy()
-        assert acc[0, 0] == 127 * k and acc[0, 1] == -127 * k
-        assert (acc[:, 2] == 0).all()
-        if m > 2:
-            assert (acc[2] == 0).all()
+    cases = [(t, x, np.float32(1.0)),
+             (wl.trits(rng, (64, 64)), wl.x_normal(rng, (m, 64)),
+              np.float32(0.02))]
+    probs, outs, refs = grouped_problems(cases, m)
+    launch_and_check(bt.bt_grouped_plan(probs), probs, outs, refs)
+    acc = probs[0]["acc"].cpu().numpy()
+    assert acc[0, 0] == 127 * k and acc[0, 1] == -127 * k
+    assert (acc[:, 2] == 0).all()
+    if m > 2:
+        assert (acc[2] == 0).all()
 
 
 @pytest.mark.parametrize("m", [1, 3])
@@ -459,31 +506,36 @@ def test_grouped_full_grid_cuts(m):
     neighbouring waves (combined inside the workgroup); three launches in a
     row, every output against the oracle."""
     rng = np.random.default_rng([112, m])
+    cases = [(wl.trits(rng, (n, k), wl.DECODE_2B), wl.x_normal(rng, (m, k)),
+              np.float32(rng.uniform(0.01, 0.05)))
+             for n, k in ((640, 65536), (4096, 256))]
+    probs, outs, refs = grouped_problems(cases, m)
+    launch_and_check(bt.bt_grouped_plan(probs), probs, outs, refs,
+                     launches=3)
+
+
+@pytest.mark.parametrize("m,fused", [(1, False), (2, False), (1, True),
+                                     (3, True)])
+def test_grouped_many_problems(m, fused):
+    """Plans of 300 small problems, each with its own weights and
+    activations (ragged rows, k from one to twelve chunks), large enough to
+    fill every CU: waves whose range starts past problem 255 look their
+    problem up beyond the first 256 descriptors.  Three launches in a row,
+    every output and every guard element checked."""
+    rng = np.random.default_rng([113, m, int(fused)])
     cases = []
-    for n, k in ((640, 65536), (4096, 256)):
+    for i in range(300):
+        n = int(rng.integers(1, 7)) * 64 + int(rng.integers(0, 64))
+        k = 64 * int(rng.integers(1, 15))
         cases.append((wl.trits(rng, (n, k), wl.DECODE_2B),
-                      wl.x_normal(rng, (m, k)),
+                      wl.x_normal_outliers(rng, (m, k)),
                       np.float32(rng.uniform(0.01, 0.05))))
-    probs = []
-    for tt, xx, s_w in cases:
-        x_q, s_a = bt.bt_quant_act(dev(xx))
-        probs.append(dict(packed=bt.bt_pack_i2s(dev(tt)), s_w=s_w,
-                          n=tt.shape[0], k=tt.shape[1], x_q=x_q, s_a=s_a,
-                          y=torch.empty((m, tt.shape[0]), device="cuda:0"),
-                          acc=torch.empty((m, tt.shape[0]), dtype=torch.int32,
-                                          device="cuda:0")))
-    refs = [oracle_product(tt, xx, s_w)[3:] for tt, xx, s_w in cases]
-    plan = bt.bt_grouped_plan(probs)
-    for launch in range(3):
-        for p in probs:
-            p["y"].fill_(float("nan"))
-            p["acc"].fill_(0x7EADBEEF)
-        bt.bt_gemm_grouped(plan)
-        torch.cuda.synchronize()
-        for i, (prob, (acc_r, y_r)) in enumerate(zip(probs, refs)):
-            acc = prob["acc"].cpu().numpy()
-            assert np.array_equal(acc, acc_r), f"launch {launch} problem {i}"
-            check_y(prob["y"].cpu().numpy(), y_r, acc_r)
+    probs, outs, refs = grouped_problems(cases, m, fused)
+    chunks = sum((t.shape[0] + 63) // 64 * t.shape[1] // 64
+                 for t, _, _ in cases)
+    assert chunks >= 512 * 16, "the plan must fill every CU"
+    launch_and_check(grouped_plan(probs, fused), probs, outs, refs,
+                     launches=3)
 
 
 @pytest.mark.parametrize("m", [1, 2, 3, 4])
@@ -496,39 +548,22 @@ def test_grouped_fused_quant(m):
     kmax = bt.BT_FUSED_MAX_MK // m // 64 * 64
     specs = [(512, 256), (64, 64), (70, 192), (1, 64), (130, 320),
              (300, 2560), (200, kmax)]
-    probs, steps, refs = [], [], []
+    cases = []
     for i, (n, k) in enumerate(specs):
         rng = np.random.default_rng([109, m, i])
         t = wl.trits(rng, (n, k), wl.DECODE_2B)
         x = wl.x_normal_outliers(rng, (m, k))
         if i == 1:
             x[0] = 0  # an all-zero row: amax floor, q = 0
-        s_w = wl.scale(rng, 0.01, 0.05)
-        packed = bt.bt_pack_i2s(dev(t))
-        probs.append(dict(packed=packed, s_w=s_w, n=n, k=k, x=dev(x),
-                          y=torch.empty((m, n), device="cuda:0"),
-                          acc=torch.empty((m, n), dtype=torch.int32,
-                                          device="cuda:0")))
-        x_q, s_a = bt.bt_quant_act(dev(x))
-        steps.append(dict(packed=packed, s_w=s_w, n=n, k=k, x_q=x_q, s_a=s_a,
-                          y=torch.empty((m, n), device="cuda:0"),
-                          acc=torch.empty((m, n), dtype=torch.int32,
-                                          device="cuda:0")))
-        refs.append(oracle_product(t, x, s_w))
-    plan = bt.bt_grouped_plan_f32(probs)
-    plan2 = bt.bt_grouped_plan(steps)
-    bt.bt_gemm_grouped(plan2)
-    for _ in range(2):
-        for p in probs:
-            p["y"].fill_(float("nan"))
-            p["acc"].fill_(0x7EADBEEF)
-        bt.bt_gemm_grouped(plan)
-        torch.cuda.synchronize()
-        for prob, two, (_, _, _, acc_r, y_r) in zip(probs, steps, refs):
-            np.testing.assert_array_equal(prob["acc"].cpu().numpy(), acc_r)
-            check_y(prob["y"].cpu().numpy(), y_r, acc_r)
-            assert torch.equal(prob["y"], two["y"])
-            assert torch.equal(prob["acc"], two["acc"])
+        cases.append((t, x, wl.scale(rng, 0.01, 0.05)))
+    probs, outs, refs = grouped_problems(cases, m, fused=True)
+    steps, souts, _ = grouped_problems(cases, m, fused=False)
+    bt.bt_gemm_grouped(bt.bt_grouped_plan(steps))
+    launch_and_check(bt.bt_grouped_plan_f32(probs), probs, outs, refs)
+    for prob, two in zip(probs, steps):
+        assert torch.equal(prob["y"], two["y"])
+        assert torch.equal(prob["acc"], two["acc"])
+    souts.check()
 
 
 @pytest.mark.parametrize("m", [70, 130])
@@ -541,115 +576,185 @@ def test_grouped_split_ranges(m, specs):
     combined through the plan's scratch slots (odd chunk counts, partial row
     and token tiles); each plan is launched twice to check that the slots and
     counters are left clean."""
-    probs, host = [], []
+    cases = []
     for i, (n, k) in enumerate(specs):
         rng = np.random.default_rng([108, m, i, len(specs)])
-        t = wl.trits(rng, (n, k))
-        x = wl.x_normal(rng, (m, k))
-        s_w = wl.scale(rng, 0.01, 0.05)
-        x_q, s_a = bt.bt_quant_act(dev(x))
-        probs.append(dict(packed=bt.bt_pack_i2s(dev(t)), s_w=s_w, n=n, k=k,
-                          x_q=x_q, s_a=s_a,
-                          y=torch.full((m, n), float("nan"), device="cuda:0"),
-                          acc=torch.full((m, n), 0x7EADBEEF, dtype=torch.int32,
-                                         device="cuda:0")))
-        host.append((t, x, s_w))
-    plan = bt.bt_grouped_plan(probs)
-    for _ in range(2):
-        for p in probs:
-            p["y"].fill_(float("nan"))
-            p["acc"].fill_(0x7EADBEEF)
-        bt.bt_gemm_grouped(plan)
-        torch.cuda.synchronize()
-        for prob, (t, x, s_w) in zip(probs, host):
-            _, q_r, s_r, acc_r, y_r = oracle_product(t, x, s_w)
-            np.testing.assert_array_equal(prob["acc"].cpu().numpy(), acc_r)
-            check_y(prob["y"].cpu().numpy(), y_r, acc_r)
+        cases.append((wl.trits(rng, (n, k)), wl.x_normal(rng, (m, k)),
+                      wl.scale(rng, 0.01, 0.05)))
+    probs, outs, refs = grouped_problems(cases, m)
+    launch_and_check(bt.bt_grouped_plan(probs), probs, outs, refs)
 
 
-def test_prefill_layer_sampled():
-    """One 2B-shaped layer at M=512 (7 products): 24 sampled output rows per
-    projection against the oracle, all 512 tokens."""
-    work = wl.prefill_2b()
-    for p in work.problems():
-        t, s_w = work.weights(p.layer, p.proj)
-        x = work.activations(p.layer, p.proj)
-        _, q, s_a, acc, y = gpu_product(t, x, s_w)
-        rng = np.random.default_rng([106, wl.PROJ_NAMES.index(p.proj)])
-        starts = sorted(set(rng.integers(0, p.n - 8, size=3).tolist()))
-        for r0 in starts:
-            rows = (r0, r0 + 8)
-            q_r, s_r = oracle.quant_act(x)
-            pk, _ = oracle.pack_i2s(t[r0:r0 + 8])
-            acc_r, y_r = oracle.gemm(pk, s_w, 8, p.k, q_r, s_r,
-                                     nthreads=NTHREADS)
-            np.testing.assert_array_equal(acc[:, r0:r0 + 8], acc_r)
-            check_y(y[:, r0:r0 + 8], y_r, acc_r)
+# ------------------------------------------------- full-size weight sets
+class WeightSet:
+    """Every (layer, projection) tensor of a workload packed on the GPU and
+    by the oracle, each from its own seeded generator (distinct weights per
+    layer, as the benchmark uploads them), or, with shared=True, every layer
+    reusing layer 0's seven tensors (the launch still streams the whole
+    set)."""
+
+    def __init__(self, work, shared=False):
+        from concurrent.futures import ThreadPoolExecutor
+        self.work = work
+        self.gpu, self.ref, self.s_w = {}, {}, {}
+        keys = sorted({(0 if shared else p.layer, p.proj)
+                       for p in work.problems()})
+
+        def make(key):  # host side: trits and the oracle's packing
+            t, s_w = work.weights(*key)
+            return t, s_w, oracle.pack_i2s(t)[0]
+
+        with ThreadPoolExecutor(NTHREADS) as ex:
+            for i in range(0, len(keys), 32):
+                batch = keys[i:i + 32]
+                for key, (t, s_w, ref) in zip(batch, ex.map(make, batch)):
+                    self.gpu[key] = bt.bt_pack_i2s(dev(t))
+                    self.ref[key] = ref
+                    self.s_w[key] = s_w
+                    del t
+        self.shared = shared
+
+    def key(self, p):
+        return (0 if self.shared else p.layer, p.proj)
 
 
-def shared_weight_set(work, sample=None, launches=2, seed=110):
-    """The products of `work` in one grouped plan, the way the benchmark
-    launches them, with every layer reusing layer 0's weight tensors (the
-    launch still streams the whole set); each (layer, projection) has its
-    own activations.  Every launch is checked against the oracle: every
-    output, or, with sample = r, r sampled row groups of 8 per product (all
-    tokens)."""
+def run_weight_set(ws, work, fused=False, full_layers=None, sample=3,
+                   launches=3, seed=110):
+    """All products of `work` (the workload of ws's weights at some M, with
+    its own activations) in one grouped launch, as the benchmark launches
+    them.  Products of the layers in full_layers (None: every layer) are
+    checked on every output; the others on `sample` random groups of 8 rows
+    (all tokens)."""
+    assert work.seed == ws.work.seed and work.shapes == ws.work.shapes
     m = work.m
-    shared = {}
-    for p in work.problems():
-        if p.layer == 0:
-            t, s_w = work.weights(0, p.proj)
-            shared[p.proj] = (t, s_w, bt.bt_pack_i2s(dev(t)))
-    probs, checks = [], []
-    for i, p in enumerate(work.problems()):
-        t, s_w, packed = shared[p.proj]
+    plist = work.problems()
+    outs = OutSet([(m, p.n) for p in plist])
+    probs, refs = [], []
+    for i, p in enumerate(plist):
+        key = ws.key(p)
         x = work.activations(p.layer, p.proj)
-        x_q, s_a = bt.bt_quant_act(dev(x))
-        probs.append(dict(packed=packed, s_w=s_w, n=p.n, k=p.k, x_q=x_q,
-                          s_a=s_a, y=torch.empty((m, p.n), device="cuda:0"),
-                          acc=torch.empty((m, p.n), dtype=torch.int32,
-                                          device="cuda:0")))
-        q_r, sa_r = oracle.quant_act(x)
-        if sample is None:
-            spans = [(0, p.n)]
+        y, acc = outs.out(i)
+        prob = dict(packed=ws.gpu[key], s_w=ws.s_w[key], n=p.n, k=p.k, y=y,
+                    acc=acc)
+        if fused:
+            prob["x"] = dev(x)
         else:
-            rng = np.random.default_rng([seed, i])
-            spans = [(r0, r0 + 8) for r0 in sorted(set(
-                rng.integers(0, p.n - 8, size=sample).tolist()))]
-        refs = []
-        for r0, r1 in spans:
-            pk = oracle.pack_i2s(t[r0:r1])[0]
-            refs.append((r0, r1) + tuple(oracle.gemm(
-                pk, s_w, r1 - r0, p.k, q_r, sa_r, nthreads=NTHREADS)))
-        checks.append(refs)
-    plan = bt.bt_grouped_plan(probs)
-    for launch in range(launches):
-        for p in probs:
-            p["y"].fill_(float("nan"))
-            p["acc"].fill_(0x7EADBEEF)
-        bt.bt_gemm_grouped(plan)
-        torch.cuda.synchronize()
-        for i, (prob, refs) in enumerate(zip(probs, checks)):
-            acc = prob["acc"].cpu().numpy()
-            y = prob["y"].cpu().numpy()
-            for r0, r1, acc_r, y_r in refs:
-                assert np.array_equal(acc[:, r0:r1], acc_r), \
-                    f"launch {launch} product {i} rows {r0}..{r1}"
-                check_y(y[:, r0:r1], y_r, acc_r)
+            prob["x_q"], prob["s_a"] = bt.bt_quant_act(dev(x))
+        probs.append(prob)
+        q_r, sa_r = oracle.quant_act(x)
+        if full_layers is None or p.layer in full_layers:
+            acc_r, y_r = oracle.gemm(ws.ref[key], ws.s_w[key], p.n, p.k, q_r,
+                                     sa_r, nthreads=NTHREADS)
+            refs.append([(0, p.n, acc_r, y_r)])
+            continue
+        rng = np.random.default_rng([seed, i])
+        spans = []
+        for r0 in sorted(set(rng.integers(0, p.n - 8, size=sample).tolist())):
+            # rows r0..r0+7 of the packed tensor: the oracle reads whole row
+            # blocks, so multiply the enclosing block and cut the rows out
+            b0 = r0 // 64 * 64
+            b1 = min(p.n, (r0 + 8 + 63) // 64 * 64)
+            blk = ws.ref[key][b0 * p.k // 4:(b1 + 63) // 64 * 64 * p.k // 4]
+            acc_r, y_r = oracle.gemm(blk, ws.s_w[key], b1 - b0, p.k, q_r,
+                                     sa_r, nthreads=NTHREADS)
+            spans.append((r0, r0 + 8, acc_r[:, r0 - b0:r0 - b0 + 8],
+                          y_r[:, r0 - b0:r0 - b0 + 8]))
+        refs.append(spans)
+    plan = grouped_plan(probs, fused)
+    launch_and_check(plan, probs, outs, refs, launches=launches,
+                     label=f"{work.name}")
+
+
+@pytest.fixture(scope="module")
+def decode_2b_distinct():
+    """The 2B-shaped decode set (30 layers x 7 projections, 521 MB packed),
+    every tensor distinct."""
+    return WeightSet(wl.decode_2b(1))
+
+
+@pytest.mark.parametrize("m,fused", [(1, False), (1, True), (2, False),
+                                     (4, False), (8, False), (16, False),
+                                     (32, False)])
+def test_decode_set_distinct_full_size(decode_2b_distinct, m, fused):
+    """The whole 2B-shaped decode set with distinct weights per layer in one
+    grouped launch, as the benchmark runs it, three times in a row; every
+    output of every launch against the oracle.  M=1 streams with dot
+    products (fused: the launch quantizes the fp32 activations itself); M=2
+    and 4 (sets this large) and the batched decode sizes M=8, 16 and 32 run
+    on the matrix cores."""
+    run_weight_set(decode_2b_distinct, wl.decode_2b(m), fused)
 
 
 @pytest.mark.parametrize("m", [1, 64])
 def test_decode_8b_set_grouped_full_size(m):
     """The 8B-shaped set (32 layers x 7 projections, 1.74 GB of packed
-    weights) in one grouped launch: every output at M=1, sampled rows at
-    M=64."""
-    shared_weight_set(wl.decode_8b(m), sample=None if m == 1 else 3)
+    weights, every layer reusing layer 0's tensors) in one grouped launch:
+    every output at M=1; at M=64 every output of layer 0 and sampled rows of
+    the other layers."""
+    ws = WeightSet(wl.decode_8b(m), shared=True)
+    run_weight_set(ws, wl.decode_8b(m), full_layers=None if m == 1 else {0},
+                   launches=2)
 
 
-def test_prefill_layer_grouped_sampled():
-    """The M=512 layer's seven products in one grouped launch (split
-    reductions for the long down projection), as the benchmark runs it."""
-    shared_weight_set(wl.prefill_2b(512), sample=4)
+@pytest.fixture(scope="module")
+def prefill_layer():
+    """The M=512 prefill layer: host inputs and the oracle's outputs of all
+    seven products (every output)."""
+    work = wl.prefill_2b(512)
+    out = []
+    for p in work.problems():
+        t, s_w = work.weights(p.layer, p.proj)
+        x = work.activations(p.layer, p.proj)
+        out.append((t, x, s_w) + oracle_product(t, x, s_w))
+    return out
+
+
+def test_prefill_layer_single(prefill_layer):
+    """One 2B-shaped layer at M=512, each product through bt_gemm: every
+    output of all seven products against the oracle."""
+    for t, x, s_w, p_r, q_r, s_r, acc_r, y_r in prefill_layer:
+        p, q, s_a, acc, y = gpu_product(t, x, s_w)
+        np.testing.assert_array_equal(p, p_r)
+        np.testing.assert_array_equal(q, q_r)
+        np.testing.assert_array_equal(s_a, s_r)
+        np.testing.assert_array_equal(acc, acc_r)
+        check_y(y, y_r, acc_r)
+
+
+def test_prefill_layer_grouped(prefill_layer):
+    """The M=512 layer's seven products in one grouped launch, as the
+    benchmark runs it (split reductions for the long down projection):
+    every output of three launches in a row, guards around every output."""
+    cases = [(t, x, s_w) for t, x, s_w, *_ in prefill_layer]
+    outs = OutSet([(512, t.shape[0]) for t, _, _ in cases])
+    probs, refs = [], []
+    for i, (t, x, s_w, p_r, q_r, s_r, acc_r, y_r) in enumerate(prefill_layer):
+        y, acc = outs.out(i)
+        x_q, s_a = bt.bt_quant_act(dev(x))
+        probs.append(dict(packed=bt.bt_pack_i2s(dev(t)), s_w=s_w,
+                          n=t.shape[0], k=t.shape[1], x_q=x_q, s_a=s_a, y=y,
+                          acc=acc))
+        refs.append([(0, t.shape[0], acc_r, y_r)])
+    launch_and_check(bt.bt_grouped_plan(probs), probs, outs, refs,
+                     launches=3)
+
+
+# ------------------------------------------------------ read-ceiling probe
+def test_read_probe_reads_every_word_once():
+    """The read-ceiling probe: the XOR of the per-wave results equals the XOR
+    of every 32-bit word of the buffer (each word read exactly once), for a
+    buffer whose length does not divide evenly among the waves."""
+    rng = np.random.default_rng(114)
+    words = rng.integers(0, 1 << 32, size=(3 * 1024 * 1024 + 37 * 256),
+                         dtype=np.uint32)
+    buf = dev(words.view(np.uint8))
+    for wpc in (4, 8):
+        for groups in (1, 2, 3, 4):
+            sink = torch.zeros(1 << 16, dtype=torch.int32, device="cuda:0")
+            bt.bt_read_probe(buf, sink, wpc, groups)
+            torch.cuda.synchronize()
+            got = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32))
+            assert got == np.bitwise_xor.reduce(words), (wpc, groups)
 
 
 # ------------------------------------------------------- layer-chained decode

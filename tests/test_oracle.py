@@ -191,6 +191,88 @@ def test_pack_size_matches_two_bits_per_weight(orc):
     assert orc.packed_bytes(10 ** 6, 1024) == 256_000_000  # ~1B weights
 
 
+# ------------------------------------------- fewer-bytes (base-3) packing
+def b3_digits(byte):
+    """The five ternary digits of a stored byte, most significant first, by
+    exact rational arithmetic: the byte stands for the fraction byte / 256 of
+    243, so digit j is floor(byte * 3^(j+1) / 256) mod 3."""
+    return [(byte * 3 ** (j + 1) // 256) % 3 for j in range(5)]
+
+
+def test_b3_all_243_values(orc):
+    """Every combination of five trits in one byte (inputs 0, 4, 8, 12, 16 of
+    a row share byte 0): the stored byte decodes back to the same digits by
+    exact arithmetic, the 243 combinations give 243 distinct bytes, larger
+    base-3 numbers give larger bytes, and unpacking returns the trits."""
+    seen = {}
+    for combo in itertools.product((-1, 0, 1), repeat=5):
+        t = np.zeros((1, 80), np.int8)
+        t[0, [0, 4, 8, 12, 16]] = combo
+        p, bad = orc.pack_b3(t)
+        assert bad == 0 and p.size == 64 * 16
+        b = int(p[0])
+        assert b3_digits(b) == [c + 1 for c in combo], combo
+        v = sum((c + 1) * 3 ** (4 - j) for j, c in enumerate(combo))
+        seen[v] = b
+        back, bad2 = orc.unpack_b3(p, 1, 80)
+        assert bad2 == 0
+        np.testing.assert_array_equal(back, t)
+    assert len(set(seen.values())) == 243
+    vals = [seen[v] for v in range(243)]
+    assert vals == sorted(vals)
+    # the 13 byte values no combination produces are flagged on unpacking
+    unused = sorted(set(range(256)) - set(vals))
+    assert len(unused) == 13
+    for b in unused:
+        _, bad = orc.unpack_b3(np.full(1024, b, np.uint8), 1, 80)
+        assert bad == 1024, b
+
+
+def test_b3_closed_forms(orc):
+    # all trits 0: digits 1,1,1,1,1 (v = 121) -> byte 128; all +1 (v = 242)
+    # -> 255; all -1 (v = 0) -> 0
+    for trit, byte in [(0, 128), (1, 255), (-1, 0)]:
+        p, bad = orc.pack_b3(np.full((64, 160), trit, np.int8))
+        assert bad == 0 and p.size == 64 * 160 // 5
+        assert (p == byte).all(), trit
+
+
+def test_b3_padding_and_size(orc):
+    """n = 70, k = 100: rows pad to 128 and inputs to 160 with trit 0 (byte
+    128 where all five inputs of a byte are padding); 1.6 bits per weight,
+    a fifth fewer bytes than 2 bits per weight when k is a multiple of 80."""
+    t = np.full((70, 100), 1, np.int8)
+    p, bad = orc.pack_b3(t)
+    assert bad == 0 and p.size == 128 * 160 // 5
+    back, _ = orc.unpack_b3(p, 70, 100)
+    np.testing.assert_array_equal(back, t)
+    assert (p == 255).sum() == 70 * 100 // 5   # all five inputs real: +1
+    assert (p == 128).sum() == p.size - 70 * 100 // 5
+    assert orc.b3_packed_bytes(2560, 2560) * 5 == 2560 * 2560 * 8 // 8
+    assert orc.b3_packed_bytes(2560, 2560) * 10 == orc.packed_bytes(
+        2560, 2560) * 8
+
+
+def test_b3_round_trip_random(orc):
+    rng = np.random.default_rng(15)
+    for n, k in [(137, 320), (64, 6912), (3, 64), (200, 4096)]:
+        t = rng.integers(-1, 2, size=(n, k), dtype=np.int8)
+        p, bad = orc.pack_b3(t)
+        assert bad == 0
+        back, bad2 = orc.unpack_b3(p, n, k)
+        assert bad2 == 0
+        np.testing.assert_array_equal(back, t)
+
+
+def test_b3_invalid_counted(orc):
+    t = np.zeros((2, 64), np.int8)
+    t[0, 3], t[1, 7] = 2, -3
+    p, bad = orc.pack_b3(t)
+    assert bad == 2
+    back, _ = orc.unpack_b3(p, 2, 64)
+    assert back[0, 3] == 0 and back[1, 7] == 0
+
+
 # ------------------------------------------------------------------ O3
 def test_quant_tie_table(orc):
     g, _ = read_golden("quant_ties.txt")
