@@ -61,7 +61,13 @@ typedef const __attribute__((address_space(3))) v4u* lds_cv4u_ptr;
 constexpr int kRsrcFlags = 0x00020000;  // raw buffer, 32-bit words
 
 
-constexpr int D = 4;  // chunks per load group (two groups in flight)
+constexpr int D = 4;  // chunks per load group
+// load groups in flight per wave: with 8 waves per CU, 3 or 4 groups were no
+// faster on the 2B and 8B decode sets (and 4 waves per CU with 2 to 4 groups
+// 5-17 % slower, the dot products then lacking a second wave per SIMD to
+// overlap with), although a bare read of 1 GiB with the same loads is
+// fastest at 4 waves per CU and 3 or 4 groups
+constexpr int G = 2;
 
 __device__ __forceinline__ int sdot4(int a, int b, int c) {
   return __builtin_amdgcn_sdot4(a, b, c, false);
@@ -566,35 +572,45 @@ struct Stream {
     a.zero();
     ocnt = 0;
     orb0 = head_rb + (head_cut ? 1 : 0);  // the first block finished whole
-    v4u A[D], B[D];
+    // G groups in flight: ring slot i holds the i-th group from g on, and pg
+    // is the last group issued
+    v4u ring[G][D];
+    load_group(ring[0], g);
     if constexpr (FUSED) {
-      load_group(A, g);
-      load_group(B, pg);
+#pragma unroll
+      for (int i = 1; i < G; ++i) {
+        if (i > 1) pg = next(pg, s1);
+        load_group(ring[i], pg);
+      }
       quantize_rows();
     } else {
       ActPre pre;
       issue_act(pre);
-      load_group(A, g);
-      load_group(B, pg);
+#pragma unroll
+      for (int i = 1; i < G; ++i) {
+        if (i > 1) pg = next(pg, s1);
+        load_group(ring[i], pg);
+      }
       finish_act(pre);
 #pragma unroll
       for (int t = 0; t < TOK; ++t) sav[t] = sa[t];
     }
-    while (true) {
-      g.uniform();
-      pg.uniform();
-      consume(A, g, a);
-      group_end(g, head_rb, head_cut, head_sum, a);
-      pg = next(pg, s1);
-      load_group(A, pg);
-      g = next(g, s1);
-      if (g.cnt == 0) break;
-      consume(B, g, a);
-      group_end(g, head_rb, head_cut, head_sum, a);
-      pg = next(pg, s1);
-      load_group(B, pg);
-      g = next(g, s1);
-      if (g.cnt == 0) break;
+    bool more = true;
+    while (more) {
+#pragma unroll
+      for (int i = 0; i < G; ++i) {
+        g.uniform();
+        pg.uniform();
+        consume(ring[i], g, a);
+        group_end(g, head_rb, head_cut, head_sum, a);
+        pg = next(pg, s1);
+        load_group(ring[i], pg);
+        g = next(g, s1);
+        if (g.cnt == 0) {
+          more = false;
+          break;
+        }
+      }
     }
     // The staged blocks go first; then both hand-offs are issued, and only
     // then are the atomics' results looked at.  The cut head block's sums
@@ -800,8 +816,9 @@ hipError_t launch_stream_grouped(const Desc* descs, const int64_t* chunk0,
   if (fused)
     return launch_stream<true, 4>(descs, chunk0, count, total_chunks, m, sacc,
                                   workgroups, s);
-  return full ? launch_stream<false, 8>(descs, chunk0, count, total_chunks, m,
-                                        sacc, workgroups, s)
+  // a full grid runs one workgroup per CU (all of the CU's waves)
+  return full ? launch_stream<false, 4 * kStreamWgPerCu>(
+                    descs, chunk0, count, total_chunks, m, sacc, workgroups, s)
               : launch_stream<false, 4>(descs, chunk0, count, total_chunks, m,
                                         sacc, workgroups, s);
 }
