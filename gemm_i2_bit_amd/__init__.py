@@ -23,6 +23,7 @@ BT_OK, BT_E_NULL, BT_E_SHAPE, BT_E_ALIGN, BT_E_ARG, BT_E_HIP, BT_E_ARCH = (
 BT_MAX_M = 1 << 24
 BT_MAX_QUANT_JOBS = 16
 BT_FUSED_MAX_MK = 16384
+BT_STATIC_SCRATCH_BYTES = 32 << 20
 
 _lib = None
 
@@ -97,6 +98,8 @@ def lib() -> ctypes.CDLL:
         L.bt_pack_b3.restype = i32
         L.bt_gemv_b3.argtypes = [p, f32, i64, i64, p, p, p, p, p]
         L.bt_gemv_b3.restype = i32
+        L.bt_gemm_grouped_static.argtypes = [p, p, p]
+        L.bt_gemm_grouped_static.restype = i32
         L.bt_read_probe.argtypes = [p, i64, p, i64, i32, i32, p]
         L.bt_read_probe.restype = i32
         _lib = L
@@ -395,6 +398,16 @@ def bt_gemm_grouped(plan: GroupedPlan, stream=None):
     _check(lib().bt_gemm_grouped(_dev(plan.dev, torch.uint8, "plan"),
                                  plan.host.ctypes.data, _stream(stream)),
            "bt_gemm_grouped")
+
+
+def bt_gemm_grouped_static(plan: GroupedPlan, stream=None):
+    """bt_gemm_grouped with the kernels' scratch in the library's static
+    device array (no allocation; calls on one GPU must not overlap)."""
+    torch = _torch()
+    _check(lib().bt_gemm_grouped_static(_dev(plan.dev, torch.uint8, "plan"),
+                                        plan.host.ctypes.data,
+                                        _stream(stream)),
+           "bt_gemm_grouped_static")
 
 
 def bt_read_probe(buf, sink, waves_per_cu: int = 8, groups: int = 2,

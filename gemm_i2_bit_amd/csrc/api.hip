@@ -226,6 +226,85 @@ int32_t check_group(const bt_problem* probs, int32_t count, bool fused) {
   return BT_OK;
 }
 
+// Header of a grouped plan, checked for consistency.
+int32_t read_plan_header(const void* plan_host, PlanHeader* out) {
+  PlanHeader h;
+  memcpy(&h, plan_host, sizeof(h));
+  if (h.magic != bt::kPlanMagic || h.count < 1 || h.blocks < 1 ||
+      h.total_chunks < 1 ||
+      h.m < 1 || h.m > BT_MAX_M || h.fused < 0 || h.fused > 1 ||
+      h.kind != bt::group_kind(h.m, h.total_chunks, h.fused == 1) ||
+      h.desc_off != 256 ||
+      h.bytes < h.scnt_off || h.scnt_off < h.sacc_off ||
+      h.sacc_off < h.unit_off || h.unit_off < h.chunk_off ||
+      h.chunk_off < h.desc_off + (int64_t)h.count * (int64_t)sizeof(Desc) ||
+      (h.kind != bt::kKindDot4 && h.units < 1) ||
+      (h.fused == 1 && h.kind != bt::kKindDot4) || h.sacc_off % 256 != 0 ||
+      h.scnt_off % 256 != 0 || h.bytes % 256 != 0)
+    return BT_E_ARG;
+  *out = h;
+  return BT_OK;
+}
+
+// Launches a checked plan whose descriptors are at plan_dev, with its
+// scratch area (partial sums and counters) at sacc and scnt.
+int32_t launch_plan(void* plan_dev, const PlanHeader& h, unsigned char* sacc,
+                    unsigned char* scnt, hipStream_t s) {
+  unsigned char* base = static_cast<unsigned char*>(plan_dev);
+  const Desc* descs = reinterpret_cast<const Desc*>(base + h.desc_off);
+  if (h.kind != bt::kKindDot4) {
+    const Unit* units = reinterpret_cast<const Unit*>(base + h.unit_off);
+    return hip_status(bt::launch_tiled_grouped(
+        descs, units, h.units, h.m, reinterpret_cast<int32_t*>(sacc),
+        reinterpret_cast<int32_t*>(scnt), s));
+  }
+  const int cus = cu_count();
+  if (cus <= 0) return BT_E_HIP;
+  // at least a group of 4 chunks per wave (counted in workgroups of 4 waves;
+  // the launch may regroup the same waves): a wave's set-up and hand-offs
+  // cost about what streaming a few chunks does, so small plans (one phase
+  // of a chained decode) run on fewer, fuller waves
+  const int64_t wgs = std::min<int64_t>((int64_t)cus * bt::kStreamWgPerCu,
+                                        (h.total_chunks + 15) / 16);
+  return hip_status(bt::launch_stream_grouped(
+      descs, reinterpret_cast<const int64_t*>(base + h.chunk_off), h.count,
+      h.total_chunks, h.m, reinterpret_cast<int32_t*>(sacc), (int)wgs,
+      h.fused == 1, wgs == (int64_t)cus * bt::kStreamWgPerCu, s));
+}
+
+// Scratch memory of bt_gemm_grouped_static: one array per GPU the library
+// runs on, alive until the process ends.  In host code `scratch` is only a
+// stand-in for the symbol: its device address comes from
+// hipGetSymbolAddress, taken once per device (with that device current) and
+// kept in g_scratch; kernels and the zero fill receive that address.
+__device__ __align__(256) unsigned char scratch[BT_STATIC_SCRATCH_BYTES];
+std::atomic<unsigned char*> g_scratch[kMaxDevices];
+
+int32_t static_scratch(unsigned char** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return BT_E_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return BT_E_ARCH;
+  unsigned char* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    void* addr = nullptr;
+    if (hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch)) != hipSuccess ||
+        addr == nullptr)
+      return BT_E_HIP;
+    p = static_cast<unsigned char*>(addr);
+    g_scratch[dev].store(p, std::memory_order_release);
+  }
+  *out = p;
+  return BT_OK;
+}
+
+// Zeroes words 16-byte words at p (vector stores; usable under graph
+// capture, unlike a memset node).
+__global__ __launch_bounds__(256) void zero_kernel(uint4* p, int64_t words) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < words;
+       i += (int64_t)gridDim.x * 256)
+    p[i] = make_uint4(0u, 0u, 0u, 0u);
+}
+
 }  // namespace
 
 extern "C" {
@@ -436,42 +515,42 @@ int32_t bt_gemm_grouped(void* plan_dev, const void* plan_host,
   if (!plan_dev || !plan_host) return BT_E_NULL;
   if (!aligned(plan_dev, 256)) return BT_E_ALIGN;
   PlanHeader h;
-  memcpy(&h, plan_host, sizeof(h));
-  if (h.magic != bt::kPlanMagic || h.count < 1 || h.blocks < 1 ||
-      h.total_chunks < 1 ||
-      h.m < 1 || h.m > BT_MAX_M || h.fused < 0 || h.fused > 1 ||
-      h.kind != bt::group_kind(h.m, h.total_chunks, h.fused == 1) ||
-      h.desc_off != 256 ||
-      h.bytes < h.scnt_off || h.scnt_off < h.sacc_off ||
-      h.sacc_off < h.unit_off || h.unit_off < h.chunk_off ||
-      h.chunk_off < h.desc_off + (int64_t)h.count * (int64_t)sizeof(Desc) ||
-      (h.kind != bt::kKindDot4 && h.units < 1) || h.fused < 0 ||
-      h.fused > 1 || (h.fused == 1 && h.kind != bt::kKindDot4))
-    return BT_E_ARG;
+  const int32_t st = read_plan_header(plan_host, &h);
+  if (st != BT_OK) return st;
   const int32_t arch = check_arch();
   if (arch != BT_OK) return arch;
   unsigned char* base = static_cast<unsigned char*>(plan_dev);
-  const Desc* descs = reinterpret_cast<const Desc*>(base + h.desc_off);
+  return launch_plan(plan_dev, h, base + h.sacc_off, base + h.scnt_off,
+                     static_cast<hipStream_t>(stream));
+}
+
+int32_t bt_gemm_grouped_static(const void* plan_dev, const void* plan_host,
+                               void* stream) {
+  if (!plan_dev || !plan_host) return BT_E_NULL;
+  if (!aligned(plan_dev, 256)) return BT_E_ALIGN;
+  PlanHeader h;
+  const int32_t st = read_plan_header(plan_host, &h);
+  if (st != BT_OK) return st;
+  // the plan's scratch area (partial sums, then counters) mapped onto the
+  // static array; it must fit
+  const int64_t need = h.bytes - h.sacc_off;
+  if (need > BT_STATIC_SCRATCH_BYTES) return BT_E_SHAPE;
+  const int32_t arch = check_arch();
+  if (arch != BT_OK) return arch;
+  unsigned char* scr = nullptr;
+  const int32_t sst = static_scratch(&scr);
+  if (sst != BT_OK) return sst;
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  if (h.kind != bt::kKindDot4) {
-    const Unit* units = reinterpret_cast<const Unit*>(base + h.unit_off);
-    return hip_status(bt::launch_tiled_grouped(
-        descs, units, h.units, h.m,
-        reinterpret_cast<int32_t*>(base + h.sacc_off),
-        reinterpret_cast<int32_t*>(base + h.scnt_off), s));
+  // every launch starts from zeroed slots and counters: the array keeps
+  // whatever the last call on this device left in it
+  if (need > 0) {
+    const int64_t words = need / 16;
+    zero_kernel<<<dim3((unsigned)std::min<int64_t>((words + 255) / 256, 4096)),
+                  dim3(256), 0, s>>>(reinterpret_cast<uint4*>(scr), words);
+    if (hipGetLastError() != hipSuccess) return BT_E_HIP;
   }
-  const int cus = cu_count();
-  if (cus <= 0) return BT_E_HIP;
-  // at least a group of 4 chunks per wave (counted in workgroups of 4 waves;
-  // the launch may regroup the same waves): a wave's set-up and hand-offs
-  // cost about what streaming a few chunks does, so small plans (one phase
-  // of a chained decode) run on fewer, fuller waves
-  const int64_t wgs = std::min<int64_t>((int64_t)cus * bt::kStreamWgPerCu,
-                                        (h.total_chunks + 15) / 16);
-  return hip_status(bt::launch_stream_grouped(
-      descs, reinterpret_cast<const int64_t*>(base + h.chunk_off), h.count,
-      h.total_chunks, h.m, reinterpret_cast<int32_t*>(base + h.sacc_off),
-      (int)wgs, h.fused == 1, wgs == (int64_t)cus * bt::kStreamWgPerCu, s));
+  return launch_plan(const_cast<void*>(plan_dev), h, scr,
+                     scr + (h.scnt_off - h.sacc_off), s);
 }
 
 int64_t bt_b3_packed_bytes(int64_t n, int64_t k) {

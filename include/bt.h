@@ -182,6 +182,25 @@ int32_t bt_grouped_plan(const bt_problem* probs, int32_t count, void* plan,
 int32_t bt_gemm_grouped(void* plan_dev, const void* plan_host,
                         void* stream);
 
+/* bt_gemm_grouped for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same launch over the same plan, with the same results bit
+ * for bit, except that the scratch memory its kernels use (the partial sums
+ * and arrival counters that bt_gemm_grouped keeps in the plan's scratch
+ * area) lives in a static array of the library, BT_STATIC_SCRATCH_BYTES per
+ * GPU, held from the first call on that GPU until the process ends.  The
+ * plan's own scratch area is not touched, so plan_dev may be read-only.
+ * Every call zeroes the part of the array its plan uses (one fill kernel on
+ * `stream`, before the product) and calls no allocating routine.  All calls
+ * on one GPU share its array: calls that overlap in time on one GPU (other
+ * streams, other threads) race and give wrong results.
+ * Returns BT_E_SHAPE when the plan's scratch area (its image size minus the
+ * scratch offset in the header) is larger than BT_STATIC_SCRATCH_BYTES;
+ * otherwise the checks and results of bt_gemm_grouped. */
+#define BT_STATIC_SCRATCH_BYTES (32 << 20)
+int32_t bt_gemm_grouped_static(const void* plan_dev, const void* plan_host,
+                               void* stream);
+
 /* Grouped decode product that quantizes its own activations (the per-token
  * int8 absmax step and the ternary product in one launch: the 8-bit
  * activation quantization of "BitNet-rs：Rust实现的高效1比特大语言模型推理

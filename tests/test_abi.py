@@ -427,3 +427,20 @@ def test_b3_sizes_and_argument_errors(L):
     assert g(P + 4, 0.5, 64, 64, P, P, P, None, None) == bt.BT_E_ALIGN
     assert g(P, -1.0, 64, 64, P, P, P, None, None) == bt.BT_E_ARG
     assert g(P, float("nan"), 64, 64, P, P, P, None, None) == bt.BT_E_ARG
+
+
+def test_grouped_static_rejects_large_scratch(L):
+    """A plan whose scratch area exceeds the static array is refused before
+    any HIP call (fake device pointers, never dereferenced)."""
+    assert L.bt_gemm_grouped_static(None, P, None) == bt.BT_E_NULL
+    n = (bt.BT_STATIC_SCRATCH_BYTES // 512 + 1) * 64   # m = 1: 512 B/block
+    probs = (bt.bt_problem * 1)()
+    probs[0] = bt.bt_problem(P, P, P, P, None, 0.5, n, 64, 1)
+    nbytes = L.bt_grouped_plan_bytes(probs, 1)
+    assert nbytes > bt.BT_STATIC_SCRATCH_BYTES
+    host = np.zeros(nbytes, np.uint8)
+    assert L.bt_grouped_plan(probs, 1, host.ctypes.data, nbytes) == bt.BT_OK
+    assert L.bt_gemm_grouped_static(P, host.ctypes.data, None) == \
+        bt.BT_E_SHAPE
+    assert L.bt_gemm_grouped_static(P + 16, host.ctypes.data, None) == \
+        bt.BT_E_ALIGN
