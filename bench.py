@@ -312,9 +312,10 @@ class ChainSet:
     input itself).  Nothing runs ahead of its input."""
 
     def __init__(self, work: wl.Workload, torch, bt, layers=None,
-                 fused=False, ps: PackedSet | None = None):
+                 fused=False, ps: PackedSet | None = None, norm=False):
         self.torch, self.bt = torch, bt
         self.fused = fused
+        self.norm = norm
         dev = torch.device("cuda:0")
         self.layers = work.layers if layers is None else layers
         self.x0 = torch.from_numpy(wl.chain_input(work)).to(dev)
@@ -336,17 +337,23 @@ class ChainSet:
                     del t
                 ys[proj] = torch.empty((1, n), dtype=torch.float32,
                                        device=dev)
-            for src, dsts in wl.CHAIN_PHASES:
+            for ph, (src, dsts) in enumerate(wl.CHAIN_PHASES):
                 xin = x if src == "x" else ys[src]
                 k = xin.shape[1]
                 x_q = torch.empty((1, k), dtype=torch.int8, device=dev)
                 s_a = torch.empty(1, dtype=torch.float32, device=dev)
+                gain = (torch.from_numpy(wl.norm_gain(work, l, ph)).to(dev)
+                        if norm else None)
                 probs = [dict(packed=packed[d][0], s_w=packed[d][1],
                               n=ys[d].shape[1], k=k, x_q=x_q, s_a=s_a,
-                              x=xin, y=ys[d]) for d in dsts]
-                plan = (bt.bt_grouped_plan_f32(probs) if fused
-                        else bt.bt_grouped_plan(probs))
-                self.phases.append((xin, x_q, s_a, plan, dsts, l))
+                              x=xin, g=gain, eps=wl.NORM_EPS, y=ys[d])
+                         for d in dsts]
+                if fused:
+                    plan = (bt.bt_grouped_plan_norm(probs) if norm
+                            else bt.bt_grouped_plan_f32(probs))
+                else:
+                    plan = bt.bt_grouped_plan(probs)
+                self.phases.append((xin, x_q, s_a, plan, dsts, l, gain))
                 self.bytes += 5 * k + 4 + sum(
                     bt.bt_packed_bytes(p["n"], k) + k + 4 + 4 * p["n"]
                     for p in probs)
@@ -359,9 +366,12 @@ class ChainSet:
         return (1 if self.fused else 2) * len(self.phases)
 
     def step(self):
-        for xin, x_q, s_a, plan, _, _ in self.phases:
+        for xin, x_q, s_a, plan, _, _, gain in self.phases:
             if not self.fused:
-                self.bt.bt_quant_act(xin, x_q, s_a)
+                if self.norm:
+                    self.bt.bt_rmsnorm_quant(xin, gain, wl.NORM_EPS, x_q, s_a)
+                else:
+                    self.bt.bt_quant_act(xin, x_q, s_a)
             self.bt.bt_gemm_grouped(plan)
 
     def capture(self):
@@ -675,16 +685,21 @@ def main():
         if not args.no_chain:
             chained = {"workload": "decode_2b chained, M=1 (one token, every "
                                    "dependency kept)"}
-            for fused in (False, True):
-                cs = ChainSet(work, torch, bt, fused=fused, ps=ps)
-                eager, graph = run_chain(cs, 20, 3, torch)
-                chained["fused" if fused else "two_launch"] = {
-                    "layers": cs.layers, "launches_per_token": cs.launches(),
-                    "ms_per_token_eager": round(eager, 4),
-                    "ms_per_token_graph": round(graph, 4),
-                    "tokens_per_s_graph": round(1e3 / graph, 1)}
-                del cs
-                torch.cuda.empty_cache()
+            for norm in (False, True):
+                for fused in (False, True):
+                    cs = ChainSet(work, torch, bt, fused=fused, ps=ps,
+                                  norm=norm)
+                    eager, graph = run_chain(cs, 20, 3, torch)
+                    key = (("norm_" if norm else "") +
+                           ("fused" if fused else "two_launch"))
+                    chained[key] = {
+                        "layers": cs.layers,
+                        "launches_per_token": cs.launches(),
+                        "ms_per_token_eager": round(eager, 4),
+                        "ms_per_token_graph": round(graph, 4),
+                        "tokens_per_s_graph": round(1e3 / graph, 1)}
+                    del cs
+                    torch.cuda.empty_cache()
             out["chained_decode"] = chained
             out["format_ablation"] = format_ablation(torch, bt)
         del ps

@@ -49,6 +49,14 @@ class bt_problem_f32(ctypes.Structure):
                 ("k", ctypes.c_int32), ("m", ctypes.c_int32)]
 
 
+class bt_problem_norm(ctypes.Structure):
+    _fields_ = [("packed", ctypes.c_void_p), ("x", ctypes.c_void_p),
+                ("g", ctypes.c_void_p), ("y", ctypes.c_void_p),
+                ("acc", ctypes.c_void_p), ("s_w", ctypes.c_float),
+                ("eps", ctypes.c_float), ("n", ctypes.c_int32),
+                ("k", ctypes.c_int32), ("m", ctypes.c_int32)]
+
+
 class bt_quant_job(ctypes.Structure):
     _fields_ = [("x", ctypes.c_void_p), ("x_q", ctypes.c_void_p),
                 ("s_a", ctypes.c_void_p), ("m", ctypes.c_int64),
@@ -98,6 +106,12 @@ def lib() -> ctypes.CDLL:
         L.bt_pack_b3.restype = i32
         L.bt_gemv_b3.argtypes = [p, f32, i64, i64, p, p, p, p, p]
         L.bt_gemv_b3.restype = i32
+        L.bt_rmsnorm_quant.argtypes = [p, p, i64, i64, f32, p, p, p, p]
+        L.bt_rmsnorm_quant.restype = i32
+        L.bt_grouped_plan_norm_bytes.argtypes = [p, i32]
+        L.bt_grouped_plan_norm_bytes.restype = i64
+        L.bt_grouped_plan_norm.argtypes = [p, i32, p, i64]
+        L.bt_grouped_plan_norm.restype = i32
         L.bt_gemm_grouped_static.argtypes = [p, p, p]
         L.bt_gemm_grouped_static.restype = i32
         L.bt_read_probe.argtypes = [p, i64, p, i64, i32, i32, p]
@@ -181,6 +195,32 @@ def bt_quant_act(x, x_q=None, s_a=None, stream=None):
                               _dev(s_a, torch.float32, "s_a"),
                               _stream(stream)), "bt_quant_act")
     return x_q, s_a
+
+
+def bt_rmsnorm_quant(x, g, eps: float, x_q=None, s_a=None, h=None,
+                     want_h: bool = False, stream=None):
+    """RMSNorm (gain g [k], eps) then absmax quantization of fp32 [m, k]
+    (GPU) -> (int8 x_q, fp32 s_a, fp32 h or None)."""
+    torch = _torch()
+    if x.dim() == 1:
+        x = x.unsqueeze(0)
+    m, k = x.shape
+    if x_q is None:
+        x_q = torch.empty((m, k), dtype=torch.int8, device=x.device)
+    if s_a is None:
+        s_a = torch.empty(m, dtype=torch.float32, device=x.device)
+    if h is None and want_h:
+        h = torch.empty((m, k), dtype=torch.float32, device=x.device)
+    if (x_q.numel() != m * k or s_a.numel() != m or g.numel() != k
+            or (h is not None and h.numel() != m * k)):
+        raise ValueError("x_q, s_a, g or h has the wrong size")
+    _check(lib().bt_rmsnorm_quant(_dev(x, torch.float32, "x"),
+                                  _dev(g, torch.float32, "g"), m, k,
+                                  float(eps), _dev(x_q, torch.int8, "x_q"),
+                                  _dev(s_a, torch.float32, "s_a"),
+                                  _dev(h, torch.float32, "h"),
+                                  _stream(stream)), "bt_rmsnorm_quant")
+    return x_q, s_a, h
 
 
 def bt_quant_act_many(xs, x_qs=None, s_as=None, stream=None):
@@ -387,6 +427,43 @@ def bt_grouped_plan_f32(problems, device=None) -> GroupedPlan:
     host = np.zeros(nbytes, np.uint8)
     _check(lib().bt_grouped_plan_f32(arr, len(problems), host.ctypes.data,
                                      nbytes), "bt_grouped_plan_f32")
+    if device is None:
+        device = problems[0]["x"].device
+    dev = torch.from_numpy(host).to(device)
+    return GroupedPlan(host, dev, keep)
+
+
+def bt_grouped_plan_norm(problems, device=None) -> GroupedPlan:
+    """problems: list of dicts with packed, s_w, n, k, x (fp32 [m, k]), g
+    (fp32 gain [k]), eps, y and optionally acc (GPU tensors; one m <= 4 for
+    all).  The launch normalizes and quantizes x itself, as
+    bt_rmsnorm_quant would."""
+    torch = _torch()
+    arr = (bt_problem_norm * len(problems))()
+    keep = []
+    for i, p in enumerate(problems):
+        x = p["x"]
+        m = x.shape[0] if x.dim() == 2 else 1
+        if (x.numel() != m * p["k"] or p["y"].numel() != m * p["n"]
+                or p["g"].numel() != p["k"]
+                or p["packed"].numel() != bt_packed_bytes(p["n"], p["k"])
+                or (p.get("acc") is not None
+                    and p["acc"].numel() != m * p["n"])):
+            raise ValueError(f"problem {i} has inconsistent sizes")
+        arr[i] = bt_problem_norm(_dev(p["packed"], torch.uint8, "packed"),
+                                 _dev(x, torch.float32, "x"),
+                                 _dev(p["g"], torch.float32, "g"),
+                                 _dev(p["y"], torch.float32, "y"),
+                                 _dev(p.get("acc"), torch.int32, "acc"),
+                                 float(p["s_w"]), float(p["eps"]), p["n"],
+                                 p["k"], m)
+        keep.append(p)
+    nbytes = lib().bt_grouped_plan_norm_bytes(arr, len(problems))
+    if nbytes < 0:
+        raise BtError(nbytes, "bt_grouped_plan_norm_bytes")
+    host = np.zeros(nbytes, np.uint8)
+    _check(lib().bt_grouped_plan_norm(arr, len(problems), host.ctypes.data,
+                                      nbytes), "bt_grouped_plan_norm")
     if device is None:
         device = problems[0]["x"].device
     dev = torch.from_numpy(host).to(device)

@@ -417,9 +417,12 @@ int64_t bt_grouped_plan_bytes(const bt_problem* probs, int32_t count) {
 }
 
 // Builds a grouped plan image; with xf, the problems give fp32 activations
-// (xf[i]) that the launch quantizes itself.
+// (xf[i]) that the launch quantizes itself, after an RMSNorm with gain g[i]
+// and eps[i] when g is given.
 static int32_t build_plan(const bt_problem* probs, int32_t count, void* plan,
-                          int64_t plan_bytes, const float* const* xf) {
+                          int64_t plan_bytes, const float* const* xf,
+                          const float* const* g = nullptr,
+                          const float* eps = nullptr) {
   if (!plan) return BT_E_NULL;
   const bool fused = xf != nullptr;
   const int32_t st = check_group(probs, count, fused);
@@ -445,6 +448,10 @@ static int32_t build_plan(const bt_problem* probs, int32_t count, void* plan,
       d.xf = xf[i];
       d.xq = nullptr;
       d.sa = nullptr;
+      if (g) {
+        d.g = g[i];
+        d.eps = eps[i];
+      }
     }
     if (h.kind != bt::kKindDot4) {
       d.nsplit = split[i].nsplit;
@@ -508,6 +515,65 @@ int32_t bt_grouped_plan_f32(const bt_problem_f32* probs, int32_t count,
   std::vector<const float*> xf(count);
   for (int32_t i = 0; i < count; ++i) xf[i] = probs[i].x;
   return build_plan(q.data(), count, plan, plan_bytes, xf.data());
+}
+
+// The RMSNorm problems as bt_problem_f32, after checks of their own: a
+// non-null, 16-byte aligned gain and a finite, non-negative eps.
+static int32_t as_problems_norm(const bt_problem_norm* probs, int32_t count,
+                                std::vector<bt_problem_f32>& out) {
+  if (!probs) return BT_E_NULL;
+  if (count < 1 || count > (1 << 20)) return BT_E_ARG;
+  out.resize(count);
+  for (int32_t i = 0; i < count; ++i) {
+    const bt_problem_norm& p = probs[i];
+    if (!p.g) return BT_E_NULL;
+    if (!aligned(p.g, 16)) return BT_E_ALIGN;
+    if (!std::isfinite(p.eps) || p.eps < 0.0f) return BT_E_ARG;
+    out[i] = bt_problem_f32{p.packed, p.x, p.y, p.acc, p.s_w, p.n, p.k, p.m};
+  }
+  return BT_OK;
+}
+
+int64_t bt_grouped_plan_norm_bytes(const bt_problem_norm* probs,
+                                   int32_t count) {
+  std::vector<bt_problem_f32> f;
+  int32_t st = as_problems_norm(probs, count, f);
+  if (st != BT_OK) return st;
+  return bt_grouped_plan_f32_bytes(f.data(), count);
+}
+
+int32_t bt_grouped_plan_norm(const bt_problem_norm* probs, int32_t count,
+                             void* plan, int64_t plan_bytes) {
+  std::vector<bt_problem_f32> f;
+  int32_t st = as_problems_norm(probs, count, f);
+  if (st != BT_OK) return st;
+  std::vector<bt_problem> q;
+  st = as_problems(f.data(), count, q);
+  if (st != BT_OK) return st;
+  std::vector<const float*> xf(count), g(count);
+  std::vector<float> eps(count);
+  for (int32_t i = 0; i < count; ++i) {
+    xf[i] = probs[i].x;
+    g[i] = probs[i].g;
+    eps[i] = probs[i].eps;
+  }
+  return build_plan(q.data(), count, plan, plan_bytes, xf.data(), g.data(),
+                    eps.data());
+}
+
+int32_t bt_rmsnorm_quant(const float* x, const float* g, int64_t m, int64_t k,
+                         float eps, int8_t* x_q, float* s_a, float* h,
+                         void* stream) {
+  if (!x || !g || !x_q || !s_a) return BT_E_NULL;
+  if (!m_ok(m) || !k_ok(k)) return BT_E_SHAPE;
+  if (!aligned(x, 16) || !aligned(g, 16) || !aligned(x_q, 16) ||
+      !aligned(s_a, 4) || (h && !aligned(h, 16)))
+    return BT_E_ALIGN;
+  if (!std::isfinite(eps) || eps < 0.0f) return BT_E_ARG;
+  const int32_t arch = check_arch();
+  if (arch != BT_OK) return arch;
+  return hip_status(bt::launch_norm_quant(x, g, m, k, eps, x_q, s_a, h,
+                                          static_cast<hipStream_t>(stream)));
 }
 
 int32_t bt_gemm_grouped(void* plan_dev, const void* plan_host,

@@ -37,8 +37,12 @@ struct alignas(16) Desc {
   int32_t region0;
   // fused-quantization plans: fp32 activations [m, k] (xq and sa are null)
   const float* xf;
+  // fused plans with RMSNorm: per-feature gain [k] (null: no norm) and eps
+  const float* g;
+  float eps;
+  int32_t pad_;
 };
-static_assert(sizeof(Desc) == 112, "Desc is 112 bytes");
+static_assert(sizeof(Desc) == 128, "Desc is 128 bytes");
 
 // One work unit of a grouped launch: problem index and a sub-index whose
 // meaning depends on the kernel: for the matrix-core kinds,
@@ -178,6 +182,43 @@ hipError_t launch_pack_b3(const int8_t* t, int64_t n, int64_t k,
 hipError_t launch_b3(const Desc& d, hipStream_t s);  // m = 1 only
 hipError_t launch_read_probe(const void* buf, int64_t bytes, uint32_t* sink,
                              int waves, int wpw, int groups, hipStream_t s);
+// RMSNorm before the quantization.  A row's sum of squares is taken by one
+// wave, in one fixed order, by every kernel that normalizes: lane l adds the
+// squares of float4 i = l, l + 64, l + 128, ... in increasing i (x, y, z, w
+// within each), in double (each square is exact), and the lanes combine by
+// an xor butterfly over offsets 32, 16, ..., 1 (every lane ends with the
+// same sum).  So the standalone and the fused kernels give identical bits.
+__device__ __forceinline__ double sumsq4(double s, const float4& v) {
+  s += (double)v.x * (double)v.x;
+  s += (double)v.y * (double)v.y;
+  s += (double)v.z * (double)v.z;
+  s += (double)v.w * (double)v.w;
+  return s;
+}
+__device__ __forceinline__ double wave_sum_f64(double s) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off, 64);
+  return s;
+}
+// r = 1 / sqrt(ss / k + eps) in double, rounded once to fp32
+__device__ __forceinline__ float rms_scale(double ss, int64_t k, float eps) {
+  return (float)(1.0 / sqrt(ss / (double)k + (double)eps));
+}
+// h = (x * r) * g, two fp32 products
+__device__ __forceinline__ float4 rms_apply(const float4& x, float r,
+                                            const float4& g) {
+  return make_float4(__fmul_rn(__fmul_rn(x.x, r), g.x),
+                     __fmul_rn(__fmul_rn(x.y, r), g.y),
+                     __fmul_rn(__fmul_rn(x.z, r), g.z),
+                     __fmul_rn(__fmul_rn(x.w, r), g.w));
+}
+__device__ __forceinline__ float absmax4(const float4& v) {
+  return fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+}
+hipError_t launch_norm_quant(const float* x, const float* g, int64_t m,
+                             int64_t k, float eps, int8_t* xq, float* sa,
+                             float* h, hipStream_t s);
+
 hipError_t launch_tiled(const Desc& d, hipStream_t s);
 hipError_t launch_tiled_grouped(const Desc* descs, const Unit* units,
                                 int64_t count, int m, int32_t* sacc,

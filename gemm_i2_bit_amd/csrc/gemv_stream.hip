@@ -216,6 +216,8 @@ struct Stream {
   const uint8_t* w;  // the problem's packed weights
   const int8_t* xq;
   gcfloat_ptr xf;    // FUSED: fp32 activations [TOK, k]
+  gcfloat_ptr gain;  // FUSED with RMSNorm: per-feature gain [k], else null
+  float eps;
   lds_i8_ptr xl;     // FUSED: this wave's LDS copy of the quantized rows
   const_fptr sa;     // scalar loads: a vector load would wait behind the
                      // weight loads in flight
@@ -492,9 +494,6 @@ struct Stream {
       v[u] = make_float4(f.x, f.y, f.z, f.w);
     }
   }
-  __device__ __forceinline__ static float absmax4(const float4& v) {
-    return fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
-  }
   __device__ __forceinline__ void quant_batch(const float4 (&v)[kBatch],
                                               lds_u32_ptr dst, int b0, int n4,
                                               float inv, int& s) const {
@@ -509,7 +508,96 @@ struct Stream {
       }
     }
   }
+  // FUSED with RMSNorm: the same three passes as the standalone kernel
+  // (sum of squares in the fixed order of sumsq4, normalized absmax,
+  // rounding), so both give the same bytes.
+  __device__ __forceinline__ void norm_rows() {
+    const int lane = threadIdx.x & 63;
+    const int n4 = k >> 2;
+    const gcfloat4_ptr gr = (gcfloat4_ptr)gain;
+#pragma unroll
+    for (int t = 0; t < TOK; ++t) {
+      const gcfloat4_ptr xr = (gcfloat4_ptr)(xf + (size_t)t * k);
+      const lds_u32_ptr dst = (lds_u32_ptr)(xl + t * k);
+      float4 v[kBatch];
+      double ss = 0.0;
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const int i = u * 64 + lane;
+        const v4f f = i < n4 ? xr[i] : v4f{0.0f, 0.0f, 0.0f, 0.0f};
+        v[u] = make_float4(f.x, f.y, f.z, f.w);
+        if (i < n4) ss = sumsq4(ss, v[u]);
+      }
+      for (int b0 = 64 * kBatch; b0 < n4; b0 += 64 * kBatch)
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+          const int i = b0 + u * 64 + lane;
+          if (i < n4) {
+            const v4f f = xr[i];
+            ss = sumsq4(ss, make_float4(f.x, f.y, f.z, f.w));
+          }
+        }
+      const float r = rms_scale(wave_sum_f64(ss), k, eps);
+      float amax = 0.0f;
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const int i = u * 64 + lane;
+        if (i < n4) {
+          const v4f gv = gr[i];
+          v[u] = rms_apply(v[u], r, make_float4(gv.x, gv.y, gv.z, gv.w));
+          amax = fmaxf(amax, absmax4(v[u]));
+        }
+      }
+      for (int b0 = 64 * kBatch; b0 < n4; b0 += 64 * kBatch)
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+          const int i = b0 + u * 64 + lane;
+          if (i < n4) {
+            const v4f f = xr[i], gv = gr[i];
+            amax = fmaxf(amax, absmax4(rms_apply(
+                make_float4(f.x, f.y, f.z, f.w), r,
+                make_float4(gv.x, gv.y, gv.z, gv.w))));
+          }
+        }
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1)
+        amax = fmaxf(amax, __shfl_xor(amax, off, 64));
+      const QScale qs = quant_scale(amax);
+      int s = 0;
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const int i = u * 64 + lane;
+        if (i < n4) {
+          const uint32_t q = quant4(v[u], qs.inv);
+          dst[i] = q;
+          s = sdot4((int)q, 0x01010101, s);
+        }
+      }
+      for (int b0 = 64 * kBatch; b0 < n4; b0 += 64 * kBatch)
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+          const int i = b0 + u * 64 + lane;
+          if (i < n4) {
+            const v4f f = xr[i], gv = gr[i];
+            const uint32_t q = quant4(
+                rms_apply(make_float4(f.x, f.y, f.z, f.w), r,
+                          make_float4(gv.x, gv.y, gv.z, gv.w)),
+                qs.inv);
+            dst[i] = q;
+            s = sdot4((int)q, 0x01010101, s);
+          }
+        }
+      qsum[t] = wave_sum(s);
+      sav[t] = qs.sa;
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  }
+
   __device__ __forceinline__ void quantize_rows() {
+    if (gain != nullptr) {
+      norm_rows();
+      return;
+    }
     const int n4 = k >> 2;
 #pragma unroll
     for (int t = 0; t < TOK; ++t) {
@@ -714,6 +802,10 @@ __device__ __forceinline__ void stream_range(Stream<TOK, FUSED>& st,
       st.k = d.k;
       st.chunk0 = d.chunk0;
       chunks = (int64_t)d.nblk * d.kc;
+    }
+    if constexpr (FUSED) {
+      st.gain = (gcfloat_ptr)d.g;
+      st.eps = d.eps;
     }
     st.sa = (const_fptr)d.sa;
     st.y = (gfloat_ptr)d.y;

@@ -163,7 +163,85 @@ __global__ __launch_bounds__(256) void quant_many_kernel(QuantJobs jobs) {
             part);
 }
 
+// RMSNorm then absmax quantization of one token row per wave (4 rows per
+// workgroup).  The row's first 8 float4 per lane stay in registers across the
+// three passes (sum of squares, normalized absmax, rounding); the rest of a
+// longer row is read again for each pass.  The sum of squares follows the
+// fixed order stated with sumsq4 in bt_internal.h.
+constexpr int kNormHeld = 8;  // float4 per lane held in registers
+
+__global__ __launch_bounds__(256) void norm_quant_kernel(
+    const float* __restrict__ x, const float* __restrict__ g, int64_t m,
+    int64_t k, float eps, int8_t* __restrict__ xq, float* __restrict__ sa,
+    float* __restrict__ hout) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= m) return;  // wave-uniform; no workgroup barrier follows
+  const float4* xr = reinterpret_cast<const float4*>(x + row * k);
+  const float4* gr = reinterpret_cast<const float4*>(g);
+  float4* hr = hout ? reinterpret_cast<float4*>(hout + row * k) : nullptr;
+  int32_t* qr = reinterpret_cast<int32_t*>(xq + row * k);
+  const int64_t n4 = k >> 2;
+  constexpr int64_t kStep = 64 * kNormHeld;
+  float4 v[kNormHeld];
+  double ss = 0.0;
+#pragma unroll
+  for (int u = 0; u < kNormHeld; ++u) {
+    const int64_t i = u * 64 + lane;
+    v[u] = i < n4 ? xr[i] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    if (i < n4) ss = sumsq4(ss, v[u]);
+  }
+  for (int64_t b0 = kStep; b0 < n4; b0 += kStep)
+#pragma unroll
+    for (int u = 0; u < kNormHeld; ++u) {
+      const int64_t i = b0 + u * 64 + lane;
+      if (i < n4) ss = sumsq4(ss, xr[i]);
+    }
+  const float r = rms_scale(wave_sum_f64(ss), k, eps);
+  float amax = 0.0f;
+#pragma unroll
+  for (int u = 0; u < kNormHeld; ++u) {
+    const int64_t i = u * 64 + lane;
+    if (i < n4) {
+      v[u] = rms_apply(v[u], r, gr[i]);
+      amax = fmaxf(amax, absmax4(v[u]));
+      if (hr) hr[i] = v[u];
+    }
+  }
+  for (int64_t b0 = kStep; b0 < n4; b0 += kStep)
+#pragma unroll
+    for (int u = 0; u < kNormHeld; ++u) {
+      const int64_t i = b0 + u * 64 + lane;
+      if (i < n4) {
+        const float4 hv = rms_apply(xr[i], r, gr[i]);
+        amax = fmaxf(amax, absmax4(hv));
+        if (hr) hr[i] = hv;
+      }
+    }
+  const QScale qs = quant_scale(wave_max(amax));
+#pragma unroll
+  for (int u = 0; u < kNormHeld; ++u) {
+    const int64_t i = u * 64 + lane;
+    if (i < n4) qr[i] = (int32_t)quant4(v[u], qs.inv);
+  }
+  for (int64_t b0 = kStep; b0 < n4; b0 += kStep)
+#pragma unroll
+    for (int u = 0; u < kNormHeld; ++u) {
+      const int64_t i = b0 + u * 64 + lane;
+      if (i < n4) qr[i] = (int32_t)quant4(rms_apply(xr[i], r, gr[i]), qs.inv);
+    }
+  if (lane == 0) sa[row] = qs.sa;
+}
+
 }  // namespace
+
+hipError_t launch_norm_quant(const float* x, const float* g, int64_t m,
+                             int64_t k, float eps, int8_t* xq, float* sa,
+                             float* h, hipStream_t s) {
+  norm_quant_kernel<<<dim3((unsigned)((m + 3) / 4)), dim3(256), 0, s>>>(
+      x, g, m, k, eps, xq, sa, h);
+  return hipGetLastError();
+}
 
 hipError_t launch_pack(const int8_t* t, int64_t n, int64_t k, uint8_t* packed,
                        int32_t* n_invalid, hipStream_t s) {

@@ -274,6 +274,47 @@ int32_t bt_read_probe(const void* buf, int64_t bytes, uint32_t* sink,
                       int64_t sink_words, int32_t waves_per_cu,
                       int32_t groups, void* stream);
 
+/* RMSNorm in front of the activation quantization: RMS normalization is one
+ * of the GPU kernels of a ternary model's decode step ("1bit-systems：在AMD
+ * Strix Halo上实现纯Rust本地三值权重LLM推理", section "技术架构：Rust在上，HIP
+ * 在下").  Per token row x [k] with per-feature gain g [k]:
+ * ss = sum x^2 (double accumulation, each square exact), r = (float)(1 /
+ * sqrt(ss / k + eps)) (double arithmetic, one rounding), h = (x * r) * g
+ * (two fp32 products); then x_q and s_a of h exactly as bt_quant_act gives
+ * them.  The sum of squares is taken in one fixed order (lane l of a wave
+ * adds float4 l, l + 64, ... in increasing order, lanes combine by an xor
+ * butterfly), shared by bt_rmsnorm_quant and the fused plans below, which
+ * therefore give the same bits.
+ *  x, g   fp32 [m, k] and [k], device, 16-byte aligned.
+ *  eps    finite, >= 0, else BT_E_ARG.
+ *  x_q, s_a  as in bt_quant_act.
+ *  h      nullable fp32 [m, k], device, 16-byte aligned: the normalized
+ *         rows, written when given. */
+int32_t bt_rmsnorm_quant(const float* x, const float* g, int64_t m, int64_t k,
+                         float eps, int8_t* x_q, float* s_a, float* h,
+                         void* stream);
+
+/* Grouped decode product with RMSNorm, quantization and product in one
+ * launch: as bt_grouped_plan_f32 (same rules, kernel and results), with each
+ * problem's fp32 rows first normalized as bt_rmsnorm_quant does (same x_q
+ * and s_a, bit for bit).  g must be non-null and 16-byte aligned. */
+typedef struct bt_problem_norm {
+  const uint8_t* packed;
+  const float* x;   /* fp32 [m, k], device, 16-byte aligned */
+  const float* g;   /* fp32 [k] gain, device, 16-byte aligned */
+  float* y;
+  int32_t* acc;     /* nullable */
+  float s_w;
+  float eps;
+  int32_t n;
+  int32_t k;
+  int32_t m;
+} bt_problem_norm;
+int64_t bt_grouped_plan_norm_bytes(const bt_problem_norm* probs,
+                                   int32_t count);
+int32_t bt_grouped_plan_norm(const bt_problem_norm* probs, int32_t count,
+                             void* plan, int64_t plan_bytes);
+
 #ifdef __cplusplus
 }
 #endif

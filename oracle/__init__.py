@@ -52,6 +52,8 @@ def lib() -> ctypes.CDLL:
         L.oracle_pack_b3.restype = i64
         L.oracle_unpack_b3.argtypes = [p, i64, i64, p]
         L.oracle_unpack_b3.restype = i64
+        L.oracle_rmsnorm.argtypes = [p, p, i64, i64, ctypes.c_float, p, p]
+        L.oracle_rmsnorm.restype = i32
         L.oracle_quant_act.argtypes = [p, i64, i64, p, p]
         L.oracle_quant_act.restype = i32
         L.oracle_gemm.argtypes = [p, ctypes.c_float, i64, i64, i64, p, p, i64,
@@ -142,6 +144,30 @@ def quant_act(x):
     s = np.empty(m, np.float32)
     lib().oracle_quant_act(_ptr(x), m, k, _ptr(q), _ptr(s))
     return q, s
+
+
+def rmsnorm(x, g, eps: float):
+    """RMSNorm of fp32 rows x [m, k] with gain g [k] -> (fp32 h [m, k],
+    float64 r64 [m], the scale before its rounding to fp32)."""
+    x = _c(x, np.float32)
+    if x.ndim == 1:
+        x = x[None, :]
+    g = _c(g, np.float32).ravel()
+    m, k = x.shape
+    if g.size != k:
+        raise ValueError("g must have k elements")
+    h = np.empty((m, k), np.float32)
+    r64 = np.empty(m, np.float64)
+    lib().oracle_rmsnorm(_ptr(x), _ptr(g), m, k, float(np.float32(eps)),
+                         _ptr(h), _ptr(r64))
+    return h, r64
+
+
+def rmsnorm_quant(x, g, eps: float):
+    """RMSNorm then O3: fp32 [m, k] -> (int8 q, fp32 s_a, fp32 h, r64)."""
+    h, r64 = rmsnorm(x, g, eps)
+    q, s_a = quant_act(h)
+    return q, s_a, h, r64
 
 
 def gemm(packed, s_w, n: int, k: int, q, s_a, nthreads: int = 1, rows=None):

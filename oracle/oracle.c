@@ -184,6 +184,29 @@ int oracle_quant_act(const float* x, int64_t m, int64_t k, int8_t* q,
   return 0;
 }
 
+/* --- RMSNorm before the quantization -------------------------------------
+ * "1bit-systems" page, section "技术架构：Rust在上，HIP在下": RMS
+ * normalization is one of the GPU kernels of the decode step.  Each row is
+ * divided by the root of its mean square (plus eps) and scaled by the
+ * per-feature gain; the precision of each step is the reading stated in the
+ * header. */
+int oracle_rmsnorm(const float* x, const float* g, int64_t m, int64_t k,
+                   float eps, float* h, double* r64) {
+  for (int64_t i = 0; i < m; ++i) {
+    const float* row = x + i * k;
+    double ss = 0.0;
+    for (int64_t c = 0; c < k; ++c) ss += (double)row[c] * (double)row[c];
+    const double rr = 1.0 / sqrt(ss / (double)k + (double)eps);
+    const float r = (float)rr;
+    if (r64) r64[i] = rr;
+    for (int64_t c = 0; c < k; ++c) {
+      const float xr = row[c] * r;  /* fp32 product */
+      h[i * k + c] = xr * g[c];     /* fp32 product */
+    }
+  }
+  return 0;
+}
+
 /* --- O4 + O5: exact integer contraction, then the rescale ----------------
  * bitnet.cpp CPU tutorial, §1.1: with weights in {-1, 0, +1} every product
  * is the activation, its negation or nothing, so the matrix product is a

@@ -82,6 +82,17 @@ int64_t oracle_unpack_b3(const uint8_t* packed, int64_t n, int64_t k,
 int oracle_quant_act(const float* x, int64_t m, int64_t k, int8_t* q,
                      float* s_a);
 
+/* RMSNorm in front of the activation quantization (the fused prologue; RMS
+ * normalization is one of the hand-written GPU kernels of "1bit-systems：在
+ * AMD Strix Halo上实现纯Rust本地三值权重LLM推理", section "技术架构：Rust在
+ * 上，HIP在下").  Per row of x [m, k] with per-feature gain g [k]:
+ * ss = sum x^2 accumulated in double (each square exact), taken in index
+ * order; r64 = 1 / sqrt(ss / k + eps) in double; r = (float)r64;
+ * h = (x * r) * g with two fp32 products.  r64[i] receives r64 (nullable).
+ * Returns 0. */
+int oracle_rmsnorm(const float* x, const float* g, int64_t m, int64_t k,
+                   float eps, float* h, double* r64);
+
 /* O4 + O5: acc[i, r] = sum_k trit(r, k) * q[i, k], exact (int64 sum, checked
  * to fit int32); y[i, r] = acc * s_w * s_a[i] evaluated in double.
  * packed holds n rows in the O2 layout, q is [m, k].  Only output rows

@@ -156,7 +156,7 @@ def problems(specs):
 
 HDR_FIELDS = ["units", "desc_off", "chunk_off", "unit_off", "sacc_off",
               "scnt_off", "bytes", "total_chunks", "blocks", "fused"]
-DESC_BYTES = 112
+DESC_BYTES = 128
 
 
 def parse_plan(img):
@@ -444,3 +444,36 @@ def test_grouped_static_rejects_large_scratch(L):
         bt.BT_E_SHAPE
     assert L.bt_gemm_grouped_static(P + 16, host.ctypes.data, None) == \
         bt.BT_E_ALIGN
+
+
+def test_rmsnorm_quant_and_norm_plan_errors(L):
+    g = L.bt_rmsnorm_quant
+    assert g(None, P, 1, 64, 1e-5, P, P, None, None) == bt.BT_E_NULL
+    assert g(P, None, 1, 64, 1e-5, P, P, None, None) == bt.BT_E_NULL
+    assert g(P, P, 1, 100, 1e-5, P, P, None, None) == bt.BT_E_SHAPE
+    assert g(P, P, 0, 64, 1e-5, P, P, None, None) == bt.BT_E_SHAPE
+    assert g(P, P + 4, 1, 64, 1e-5, P, P, None, None) == bt.BT_E_ALIGN
+    assert g(P, P, 1, 64, 1e-5, P, P, P + 4, None) == bt.BT_E_ALIGN
+    for eps in (-1.0, float("nan"), float("inf")):
+        assert g(P, P, 1, 64, eps, P, P, None, None) == bt.BT_E_ARG
+    probs = (bt.bt_problem_norm * 1)()
+    probs[0] = bt.bt_problem_norm(P, P, P, P, None, 0.5, 1e-5, 64, 64, 1)
+    n = L.bt_grouped_plan_norm_bytes(probs, 1)
+    assert n > 0
+    img = np.zeros(n, np.uint8)
+    assert L.bt_grouped_plan_norm(probs, 1, img.ctypes.data, n) == bt.BT_OK
+    p = parse_plan(img)
+    assert p["fused"] == 1
+    d = img[p["desc_off"]:p["desc_off"] + DESC_BYTES]
+    assert np.frombuffer(d[104:112].tobytes(), np.uint64)[0] == P   # gain
+    assert np.frombuffer(d[112:116].tobytes(), np.float32)[0] == \
+        np.float32(1e-5)
+    for bad, code in [((P, P, None, P, None, 0.5, 1e-5, 64, 64, 1),
+                       bt.BT_E_NULL),
+                      ((P, P, P + 4, P, None, 0.5, 1e-5, 64, 64, 1),
+                       bt.BT_E_ALIGN),
+                      ((P, P, P, P, None, 0.5, -1.0, 64, 64, 1), bt.BT_E_ARG),
+                      ((P, P, P, P, None, 0.5, 1e-5, 64, 64, 5),
+                       bt.BT_E_SHAPE)]:
+        probs[0] = bt.bt_problem_norm(*bad)
+        assert L.bt_grouped_plan_norm_bytes(probs, 1) == code, bad

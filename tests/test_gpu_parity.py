@@ -230,6 +230,113 @@ def test_quant_many_limits():
                       for m in range(1, bt.BT_MAX_QUANT_JOBS + 1)])
 
 
+# ------------------------------------------------------ RMSNorm + quantize
+def near_scale_boundary(r64, k):
+    """Rows whose RMSNorm scale (the oracle's double value) lies so close to
+    a rounding boundary of fp32 that a double sum of squares taken in another
+    order (within (k + 4) roundings of 2^-53) could round it to the other
+    side.  Such a row may legitimately differ; every other row must match
+    bit for bit."""
+    r64 = np.asarray(r64, np.float64)
+    r32 = r64.astype(np.float32)
+    lo = np.nextafter(r32, np.float32(0)).astype(np.float64)
+    hi = np.nextafter(r32, np.float32(np.inf)).astype(np.float64)
+    mid_lo = (r32.astype(np.float64) + lo) / 2
+    mid_hi = (r32.astype(np.float64) + hi) / 2
+    d = np.minimum(np.abs(r64 - mid_lo), np.abs(r64 - mid_hi)) / r64
+    return d < (k + 4) * 2.0 ** -53
+
+
+def norm_cases():
+    rng = np.random.default_rng(130)
+    zero = np.zeros((2, 128), np.float32)
+    zero[1, 5] = 3.0
+    return [
+        ("decode", wl.x_normal_outliers(rng, (3, 2560)), 1e-5),
+        ("student_t", wl.x_student_t(rng, (5, 6912)), 1e-6),
+        ("held", wl.x_normal(rng, (2, 2048)) * np.float32(40), 1e-5),
+        ("held_plus_one", wl.x_normal(rng, (2, 2112)), 0.0),
+        ("long_8b", wl.x_student_t(rng, (2, 14336)), 1e-5),
+        ("longest", wl.x_normal_outliers(rng, (1, 65536)), 1e-5),
+        ("one_chunk", wl.x_normal(rng, (7, 64)), 1e-5),
+        ("zero_rows", zero, 1e-5),
+    ]
+
+
+@pytest.mark.parametrize("name,x,eps", norm_cases(),
+                         ids=lambda v: v if isinstance(v, str) else "")
+def test_rmsnorm_quant_matches_oracle(name, x, eps):
+    """RMSNorm then quantization: the normalized rows, x_q and s_a equal the
+    oracle's bit for bit (rows of every length class: held in registers,
+    one float4 past them, re-read, the longest), except on rows whose scale
+    sits on an fp32 rounding boundary (none expected)."""
+    m, k = x.shape
+    g = np.random.default_rng([131, k]).uniform(-1.5, 1.5, k).astype(
+        np.float32)
+    q_r, s_r, h_r, r64 = oracle.rmsnorm_quant(x, g, eps)
+    qbuf, q = guarded(m * k, torch.int8, 0x5A)
+    sbuf, s = guarded(m, torch.float32, float("nan"))
+    hbuf, h = guarded(m * k, torch.float32, float("nan"))
+    bt.bt_rmsnorm_quant(dev(x), dev(g), eps, x_q=q.view(m, k), s_a=s,
+                        h=h.view(m, k))
+    torch.cuda.synchronize()
+    check_guards(qbuf, 0x5A)
+    check_guards(sbuf, None)
+    check_guards(hbuf, None)
+    ok = ~near_scale_boundary(r64, k)
+    assert ok.sum() >= m - 1
+    np.testing.assert_array_equal(h.view(m, k).cpu().numpy()[ok], h_r[ok])
+    np.testing.assert_array_equal(q.view(m, k).cpu().numpy()[ok], q_r[ok])
+    np.testing.assert_array_equal(s.cpu().numpy()[ok].view(np.uint32),
+                                  s_r[ok].view(np.uint32))
+
+
+@pytest.mark.parametrize("m", [1, 2, 4])
+def test_grouped_norm_plan(m):
+    """Grouped plans that normalize, quantize and multiply in one launch:
+    outputs equal to bt_rmsnorm_quant followed by the grouped product, bit
+    for bit, and to the oracle (RMSNorm, quantization and product) on rows
+    away from a scale rounding boundary; ragged shapes, the longest rows
+    that fit; launched twice."""
+    kmax = bt.BT_FUSED_MAX_MK // m // 64 * 64
+    specs = [(512, 256), (64, 64), (70, 192), (300, 2560), (200, kmax)]
+    outs = OutSet([(m, n) for n, _ in specs])
+    outs2 = OutSet([(m, n) for n, _ in specs])
+    probs, steps, refs, host = [], [], [], []
+    for i, (n, k) in enumerate(specs):
+        rng = np.random.default_rng([132, m, i])
+        t = wl.trits(rng, (n, k), wl.DECODE_2B)
+        x = wl.x_normal_outliers(rng, (m, k))
+        g = rng.uniform(0.5, 1.5, k).astype(np.float32)
+        s_w = wl.scale(rng, 0.01, 0.05)
+        packed = bt.bt_pack_i2s(dev(t))
+        y, acc = outs.out(i)
+        probs.append(dict(packed=packed, s_w=s_w, n=n, k=k, x=dev(x),
+                          g=dev(g), eps=1e-5, y=y, acc=acc))
+        x_q, s_a, _ = bt.bt_rmsnorm_quant(dev(x), dev(g), 1e-5)
+        y2, acc2 = outs2.out(i)
+        steps.append(dict(packed=packed, s_w=s_w, n=n, k=k, x_q=x_q, s_a=s_a,
+                          y=y2, acc=acc2))
+        q_r, s_r, _, r64 = oracle.rmsnorm_quant(x, g, 1e-5)
+        p_r, _ = oracle.pack_i2s(t)
+        acc_r, y_r = oracle.gemm(p_r, s_w, n, k, q_r, s_r, nthreads=NTHREADS)
+        ok = ~near_scale_boundary(r64, k)
+        refs.append((acc_r, y_r, ok))
+    bt.bt_gemm_grouped(bt.bt_grouped_plan(steps))
+    plan = bt.bt_grouped_plan_norm(probs)
+    for _ in range(2):
+        outs.reset()
+        bt.bt_gemm_grouped(plan)
+        torch.cuda.synchronize()
+        outs.check()
+        for prob, two, (acc_r, y_r, ok) in zip(probs, steps, refs):
+            assert torch.equal(prob["y"], two["y"])
+            assert torch.equal(prob["acc"], two["acc"])
+            acc = prob["acc"].cpu().numpy()
+            np.testing.assert_array_equal(acc[ok], acc_r[ok])
+            check_y(prob["y"].cpu().numpy()[ok], y_r[ok], acc_r[ok])
+
+
 # ------------------------------------------------------------- the product
 def test_pipeline_worked_example():
     t = np.zeros((2, 64), np.int8)
@@ -758,17 +865,25 @@ def test_read_probe_reads_every_word_once():
 
 
 # ------------------------------------------------------- layer-chained decode
-def oracle_chain(work, layers):
-    """The chained decode on the CPU: every phase quantizes its input (O3),
-    multiplies (O4) and rescales in fp32 (O5), and the fp32 outputs feed the
-    next phase as they would on the GPU."""
+def oracle_chain(work, layers, norm=False):
+    """The chained decode on the CPU: every phase quantizes its input (O3;
+    with norm, after the RMSNorm), multiplies (O4) and rescales in fp32
+    (O5), and the fp32 outputs feed the next phase as they would on the
+    GPU.  Returns the outputs and whether any phase's RMSNorm scale sat on
+    an fp32 rounding boundary (then the chain may legitimately differ)."""
     x = wl.chain_input(work)
     outs = []
+    boundary = False
     for l in range(layers):
         ys = {}
-        for src, dsts in wl.CHAIN_PHASES:
+        for ph, (src, dsts) in enumerate(wl.CHAIN_PHASES):
             xin = x if src == "x" else ys[src]
-            q, s_a = oracle.quant_act(xin)
+            if norm:
+                q, s_a, _, r64 = oracle.rmsnorm_quant(
+                    xin, wl.norm_gain(work, l, ph), wl.NORM_EPS)
+                boundary |= bool(near_scale_boundary(r64, xin.shape[1]).any())
+            else:
+                q, s_a = oracle.quant_act(xin)
             for d in dsts:
                 t, s_w = work.weights(l, d)
                 p, bad = oracle.pack_i2s(t)
@@ -778,22 +893,25 @@ def oracle_chain(work, layers):
                 ys[d] = oracle.rescale_f32(acc, s_w, s_a)
         outs.append(ys)
         x = ys[wl.CHAIN_OUT]
-    return outs
+    return outs, boundary
 
 
-@pytest.mark.parametrize("fused", [False, True])
-def test_chained_decode_matches_oracle(fused):
+@pytest.mark.parametrize("fused,norm", [(False, False), (True, False),
+                                        (False, True), (True, True)])
+def test_chained_decode_matches_oracle(fused, norm):
     """Two 2B-shaped layers chained phase by phase (two launches per phase,
-    or one launch that quantizes its fp32 input): every output of every
-    projection equals the oracle's bit for bit (each phase's fp32 output is
-    the next phase's input), eagerly and on each replay of the token captured
-    as a HIP graph, with eager launches between the replays."""
+    or one launch that quantizes its fp32 input; with norm, RMSNorm before
+    every quantization): every output of every projection equals the
+    oracle's bit for bit (each phase's fp32 output is the next phase's
+    input), eagerly and on each replay of the token captured as a HIP graph,
+    with eager launches between the replays."""
     import bench
     work = wl.decode_2b(1)
-    cs = bench.ChainSet(work, torch, bt, layers=2, fused=fused)
+    cs = bench.ChainSet(work, torch, bt, layers=2, fused=fused, norm=norm)
     cs.step()
     torch.cuda.synchronize()
-    ref = oracle_chain(work, 2)
+    ref, boundary = oracle_chain(work, 2, norm)
+    assert not boundary, "an RMSNorm scale sits on a rounding boundary"
 
     def check(label):
         for l in range(2):

@@ -273,6 +273,83 @@ def test_b3_invalid_counted(orc):
     assert back[0, 3] == 0 and back[1, 7] == 0
 
 
+# ------------------------------------------------------------- RMSNorm
+def test_rmsnorm_closed_forms(orc):
+    # a constant row of 2 with eps = 0 has mean square 4: the scale is 1/2
+    # exactly and every output is the gain exactly
+    x = np.full((1, 64), 2.0, np.float32)
+    for g in (np.ones(64, np.float32),
+              np.float32(2.0) ** np.arange(-8, 56, dtype=np.float32)):
+        h, r64 = orc.rmsnorm(x, g, 0.0)
+        assert r64[0] == 0.5
+        np.testing.assert_array_equal(h[0], g)
+    # an all-zero row stays zero (eps keeps the scale finite) and quantizes
+    # to zeros
+    q, s_a, h, r64 = orc.rmsnorm_quant(np.zeros((1, 64), np.float32),
+                                       np.ones(64, np.float32), 1e-5)
+    assert np.isfinite(r64).all() and not h.any() and not q.any()
+
+
+def test_rmsnorm_worked_example(orc):
+    # x = [3, 4], eps = 0: mean square 25 / 2, scale sqrt(2) / 5 (exactly
+    # 0.28284271247461900976...), the double nearest to it
+    h, r64 = orc.rmsnorm(np.array([[3.0, 4.0]], np.float32),
+                         np.ones(2, np.float32), 0.0)
+    exact = Fraction(28284271247461900976033774484194, 10 ** 32)
+    assert abs(Fraction(r64[0]) - exact) <= Fraction(2 ** -54)
+    r = np.float32(r64[0])
+    assert h[0].tolist() == [float(np.float32(3 * r)), float(np.float32(4 * r))]
+
+
+def test_rmsnorm_against_exact_rationals(orc):
+    """Random rows: the double scale is within the rounding bound of a
+    k-term double sum of the exact 1 / sqrt(sum x^2 / k + eps) (computed with
+    rationals and a 60-digit square root), and each output is within two
+    fp32 roundings of x * g * r."""
+    import decimal
+    decimal.getcontext().prec = 60
+    rng = np.random.default_rng(16)
+    for k, eps in [(64, 1e-5), (256, 1e-6), (1000, 0.0)]:
+        x = (rng.standard_normal((3, k)) * 3).astype(np.float32)
+        g = rng.uniform(0.5, 1.5, k).astype(np.float32)
+        h, r64 = orc.rmsnorm(x, g, eps)
+        for i in range(3):
+            ss = sum(Fraction(float(v)) ** 2 for v in x[i])
+            ms = ss / k + Fraction(float(np.float32(eps)))
+            exact = 1 / decimal.Decimal(ms.numerator).__truediv__(
+                decimal.Decimal(ms.denominator)).sqrt()
+            # a sum of k doubles carries at most (k - 1) roundings of 2^-53
+            # relative, the divide, add, root and reciprocal four more
+            rel = abs(decimal.Decimal(float(r64[i])) - exact) / exact
+            assert rel < (k + 4) * decimal.Decimal(2) ** -53, (k, i)
+            r = np.float64(np.float32(r64[i]))
+            ref = x[i].astype(np.float64) * g.astype(np.float64) * r
+            err = np.abs(h[i].astype(np.float64) - ref)
+            assert (err <= 2 * np.abs(ref) * 2.0 ** -24 + 1e-45).all()
+
+
+def test_rmsnorm_invariants(orc):
+    rng = np.random.default_rng(17)
+    x = rng.standard_normal((4, 512)).astype(np.float32)
+    g = rng.uniform(0.5, 1.5, 512).astype(np.float32)
+    h, _ = orc.rmsnorm(x, g, 0.0)
+    # scaling a row by a power of two (eps = 0) changes nothing
+    for j in (-6, 3, 20):
+        h2, _ = orc.rmsnorm(x * np.float32(2.0 ** j), g, 0.0)
+        np.testing.assert_array_equal(h2, h)
+    # negation negates
+    h3, _ = orc.rmsnorm(-x, g, 0.0)
+    np.testing.assert_array_equal(h3, -h)
+    # with unit gains the output has mean square 1 (eps = 0)
+    h4, _ = orc.rmsnorm(x, np.ones(512, np.float32), 0.0)
+    ms = (h4.astype(np.float64) ** 2).mean(axis=1)
+    assert np.abs(ms - 1).max() < 1e-6
+    # eps only ever shrinks the scale
+    _, r0 = orc.rmsnorm(x, g, 0.0)
+    _, r1 = orc.rmsnorm(x, g, 1e-2)
+    assert (r1 < r0).all()
+
+
 # ------------------------------------------------------------------ O3
 def test_quant_tie_table(orc):
     g, _ = read_golden("quant_ties.txt")

@@ -174,6 +174,18 @@ def chain_input(work: Workload, m: int = 1):
     return x_normal(rng, shape)
 
 
+NORM_EPS = 1e-5  # RMSNorm eps of the chained decode with normalization
+
+
+def norm_gain(work: Workload, layer: int, phase: int):
+    """Per-feature RMSNorm gain of one phase input of the layer-chained
+    decode (no trained gains exist here): U(0.5, 1.5), fp32, [k]."""
+    src = CHAIN_PHASES[phase][0]
+    k = work.shapes["q"][0] if src == "x" else work.shapes[src][1]
+    rng = np.random.default_rng([work.seed, layer, 16 + phase, 2])
+    return rng.uniform(0.5, 1.5, k).astype(np.float32)
+
+
 def single_gemv():
     """The small single-GEMV case: M=1, K=256, N=512, seed 0, uniform trits
     drawn first, then x ~ N(0, 1); s_w = 0.02."""
