@@ -312,10 +312,13 @@ class ChainSet:
     input itself).  Nothing runs ahead of its input."""
 
     def __init__(self, work: wl.Workload, torch, bt, layers=None,
-                 fused=False, ps: PackedSet | None = None, norm=False):
+                 fused=False, ps: PackedSet | None = None, norm=False,
+                 persistent=False):
         self.torch, self.bt = torch, bt
-        self.fused = fused
+        self.fused = fused or persistent
+        fused = self.fused
         self.norm = norm
+        self.persistent = persistent
         dev = torch.device("cuda:0")
         self.layers = work.layers if layers is None else layers
         self.x0 = torch.from_numpy(wl.chain_input(work)).to(dev)
@@ -360,12 +363,19 @@ class ChainSet:
             self.y.append(ys)
             x = ys[wl.CHAIN_OUT]
         self.out = x
+        self.chain = (bt.bt_chain_plan([ph[3] for ph in self.phases])
+                      if persistent else None)
         torch.cuda.synchronize()
 
     def launches(self):
+        if self.persistent:
+            return 2  # the sync-word reset and the persistent launch
         return (1 if self.fused else 2) * len(self.phases)
 
     def step(self):
+        if self.persistent:
+            self.bt.bt_gemm_chain(self.chain)
+            return
         for xin, x_q, s_a, plan, _, _, gain in self.phases:
             if not self.fused:
                 if self.norm:
@@ -390,6 +400,8 @@ def run_chain(cs: ChainSet, tokens: int, warmup: int, torch):
         cs.step()
     torch.cuda.synchronize()
     eager = (time.perf_counter() - t0) / tokens * 1e3
+    if cs.persistent:  # one cooperative launch per token: no graph
+        return eager, eager
     g = cs.capture()
     for _ in range(warmup):
         g.replay()
@@ -686,12 +698,14 @@ def main():
             chained = {"workload": "decode_2b chained, M=1 (one token, every "
                                    "dependency kept)"}
             for norm in (False, True):
-                for fused in (False, True):
-                    cs = ChainSet(work, torch, bt, fused=fused, ps=ps,
-                                  norm=norm)
+                for mode in ("two_launch", "fused", "persistent"):
+                    cs = ChainSet(work, torch, bt, fused=mode == "fused",
+                                  ps=ps, norm=norm,
+                                  persistent=mode == "persistent")
                     eager, graph = run_chain(cs, 20, 3, torch)
-                    key = (("norm_" if norm else "") +
-                           ("fused" if fused else "two_launch"))
+                    if cs.persistent and bt.bt_chain_status(cs.chain) != 0:
+                        raise RuntimeError("chained launch gave up waiting")
+                    key = ("norm_" if norm else "") + mode
                     chained[key] = {
                         "layers": cs.layers,
                         "launches_per_token": cs.launches(),

@@ -24,6 +24,7 @@ BT_MAX_M = 1 << 24
 BT_MAX_QUANT_JOBS = 16
 BT_FUSED_MAX_MK = 16384
 BT_STATIC_SCRATCH_BYTES = 32 << 20
+BT_CHAIN_STATUS_OFFSET = 4356
 
 _lib = None
 
@@ -55,6 +56,10 @@ class bt_problem_norm(ctypes.Structure):
                 ("acc", ctypes.c_void_p), ("s_w", ctypes.c_float),
                 ("eps", ctypes.c_float), ("n", ctypes.c_int32),
                 ("k", ctypes.c_int32), ("m", ctypes.c_int32)]
+
+
+class bt_chain_phase(ctypes.Structure):
+    _fields_ = [("plan_dev", ctypes.c_void_p), ("plan_host", ctypes.c_void_p)]
 
 
 class bt_quant_job(ctypes.Structure):
@@ -112,6 +117,12 @@ def lib() -> ctypes.CDLL:
         L.bt_grouped_plan_norm_bytes.restype = i64
         L.bt_grouped_plan_norm.argtypes = [p, i32, p, i64]
         L.bt_grouped_plan_norm.restype = i32
+        L.bt_chain_plan_bytes.argtypes = [i32]
+        L.bt_chain_plan_bytes.restype = i64
+        L.bt_chain_plan.argtypes = [p, i32, p, i64]
+        L.bt_chain_plan.restype = i32
+        L.bt_gemm_chain.argtypes = [p, p, p]
+        L.bt_gemm_chain.restype = i32
         L.bt_gemm_grouped_static.argtypes = [p, p, p]
         L.bt_gemm_grouped_static.restype = i32
         L.bt_read_probe.argtypes = [p, i64, p, i64, i32, i32, p]
@@ -497,3 +508,47 @@ def bt_read_probe(buf, sink, waves_per_cu: int = 8, groups: int = 2,
                                _dev(sink, torch.int32, "sink"), sink.numel(),
                                int(waves_per_cu), int(groups),
                                _stream(stream)), "bt_read_probe")
+
+
+class ChainPlan:
+    """A chained launch's image (host and device copy); keeps its phase
+    plans alive."""
+
+    def __init__(self, host: np.ndarray, dev, plans):
+        self.host = host
+        self.dev = dev
+        self._plans = plans
+
+
+def bt_chain_plan(plans, device=None) -> ChainPlan:
+    """plans: fused GroupedPlans (bt_grouped_plan_f32 / _norm), in the order
+    their phases run."""
+    torch = _torch()
+    arr = (bt_chain_phase * len(plans))()
+    for i, pl in enumerate(plans):
+        arr[i] = bt_chain_phase(_dev(pl.dev, torch.uint8, "plan"),
+                                pl.host.ctypes.data)
+    nbytes = lib().bt_chain_plan_bytes(len(plans))
+    if nbytes < 0:
+        raise BtError(nbytes, "bt_chain_plan_bytes")
+    host = np.zeros(nbytes, np.uint8)
+    _check(lib().bt_chain_plan(arr, len(plans), host.ctypes.data, nbytes),
+           "bt_chain_plan")
+    if device is None:
+        device = plans[0].dev.device
+    return ChainPlan(host, torch.from_numpy(host).to(device), list(plans))
+
+
+def bt_gemm_chain(chain: ChainPlan, stream=None):
+    """All phases of the chain in one persistent launch."""
+    torch = _torch()
+    _check(lib().bt_gemm_chain(_dev(chain.dev, torch.uint8, "chain"),
+                               chain.host.ctypes.data, _stream(stream)),
+           "bt_gemm_chain")
+
+
+def bt_chain_status(chain: ChainPlan) -> int:
+    """The chain's status word (synchronizes): 0 after a complete launch,
+    nonzero if a barrier wait gave up (outputs invalid)."""
+    o = BT_CHAIN_STATUS_OFFSET
+    return int(chain.dev[o:o + 4].cpu().numpy().view(np.int32)[0])

@@ -297,6 +297,32 @@ int32_t static_scratch(unsigned char** out) {
   return BT_OK;
 }
 
+// Host image of a chained launch: header, sync words (zeroed by every
+// launch), phase table.
+struct ChainHeader {
+  uint32_t magic;
+  int32_t count;
+  int32_t m;
+  int32_t pad0;
+  int64_t sync_off;
+  int64_t table_off;
+  int64_t bytes;
+  int64_t pad1[27];
+};
+static_assert(sizeof(ChainHeader) == 256, "ChainHeader is 256 bytes");
+constexpr uint32_t kChainMagic = 0x31485442u;  // "BTH1"
+constexpr int64_t kChainSyncOff = 256;
+constexpr int64_t kChainTableOff =
+    kChainSyncOff + (int64_t)bt::kChainSyncWords * 4;
+static_assert(BT_CHAIN_STATUS_OFFSET ==
+                  kChainSyncOff + 4 * (bt::kChainMaxWg + 1),
+              "status word offset");
+
+int64_t chain_bytes(int32_t count) {
+  return (kChainTableOff + (int64_t)count * (int64_t)sizeof(bt::ChainPhase) +
+          255) / 256 * 256;
+}
+
 // Zeroes words 16-byte words at p (vector stores; usable under graph
 // capture, unlike a memset node).
 __global__ __launch_bounds__(256) void zero_kernel(uint4* p, int64_t words) {
@@ -617,6 +643,78 @@ int32_t bt_gemm_grouped_static(const void* plan_dev, const void* plan_host,
   }
   return launch_plan(const_cast<void*>(plan_dev), h, scr,
                      scr + (h.scnt_off - h.sacc_off), s);
+}
+
+int64_t bt_chain_plan_bytes(int32_t count) {
+  if (count < 1 || count > BT_MAX_CHAIN_PHASES) return BT_E_ARG;
+  return chain_bytes(count);
+}
+
+int32_t bt_chain_plan(const bt_chain_phase* phases, int32_t count,
+                      void* chain_host, int64_t chain_bytes_given) {
+  if (!phases || !chain_host) return BT_E_NULL;
+  if (count < 1 || count > BT_MAX_CHAIN_PHASES) return BT_E_ARG;
+  if (chain_bytes_given < chain_bytes(count)) return BT_E_ARG;
+  unsigned char* out = static_cast<unsigned char*>(chain_host);
+  memset(out, 0, (size_t)chain_bytes(count));
+  ChainHeader ch;
+  memset(&ch, 0, sizeof(ch));
+  ch.magic = kChainMagic;
+  ch.count = count;
+  ch.sync_off = kChainSyncOff;
+  ch.table_off = kChainTableOff;
+  ch.bytes = chain_bytes(count);
+  for (int32_t i = 0; i < count; ++i) {
+    if (!phases[i].plan_dev || !phases[i].plan_host) return BT_E_NULL;
+    if (!aligned(phases[i].plan_dev, 256)) return BT_E_ALIGN;
+    PlanHeader h;
+    const int32_t st = read_plan_header(phases[i].plan_host, &h);
+    if (st != BT_OK) return st;
+    // fused plans (fp32 inputs quantized in the launch), one m for all
+    if (h.fused != 1 || h.kind != bt::kKindDot4) return BT_E_ARG;
+    if (i == 0) ch.m = h.m;
+    if (h.m != ch.m) return BT_E_SHAPE;
+    unsigned char* base = static_cast<unsigned char*>(phases[i].plan_dev);
+    bt::ChainPhase p;
+    memset(&p, 0, sizeof(p));
+    p.descs = reinterpret_cast<const Desc*>(base + h.desc_off);
+    p.chunk0 = reinterpret_cast<const int64_t*>(base + h.chunk_off);
+    p.sacc = reinterpret_cast<int32_t*>(base + h.sacc_off);
+    p.total = h.total_chunks;
+    p.count = h.count;
+    memcpy(out + kChainTableOff + (int64_t)i * sizeof(p), &p, sizeof(p));
+  }
+  memcpy(out, &ch, sizeof(ch));
+  return BT_OK;
+}
+
+int32_t bt_gemm_chain(void* chain_dev, const void* chain_host, void* stream) {
+  if (!chain_dev || !chain_host) return BT_E_NULL;
+  if (!aligned(chain_dev, 256)) return BT_E_ALIGN;
+  ChainHeader ch;
+  memcpy(&ch, chain_host, sizeof(ch));
+  if (ch.magic != kChainMagic || ch.count < 1 ||
+      ch.count > BT_MAX_CHAIN_PHASES || ch.m < 1 || ch.m > 4 ||
+      ch.sync_off != kChainSyncOff || ch.table_off != kChainTableOff ||
+      ch.bytes != chain_bytes(ch.count))
+    return BT_E_ARG;
+  const int32_t arch = check_arch();
+  if (arch != BT_OK) return arch;
+  const int cus = cu_count();
+  if (cus <= 0) return BT_E_HIP;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  unsigned char* base = static_cast<unsigned char*>(chain_dev);
+  // arrival, release and error words start at zero in every launch
+  zero_kernel<<<dim3(2), dim3(256), 0, s>>>(
+      reinterpret_cast<uint4*>(base + kChainSyncOff),
+      (int64_t)bt::kChainSyncWords * 4 / 16);
+  if (hipGetLastError() != hipSuccess) return BT_E_HIP;
+  // one workgroup of 4 waves per CU, all resident (cooperative launch)
+  const int wgs = std::min(cus, bt::kChainMaxWg);
+  return hip_status(bt::launch_chain(
+      reinterpret_cast<const bt::ChainPhase*>(base + kChainTableOff),
+      ch.count, ch.m, reinterpret_cast<uint32_t*>(base + kChainSyncOff), wgs,
+      s));
 }
 
 int64_t bt_b3_packed_bytes(int64_t n, int64_t k) {

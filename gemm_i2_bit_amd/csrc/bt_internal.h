@@ -150,6 +150,24 @@ hipError_t launch_stream_grouped(const Desc* descs, const int64_t* chunk0,
                                  int32_t* sacc, int workgroups, bool fused,
                                  bool full, hipStream_t s);
 
+// One phase of a persistent chained launch: a fused plan's descriptors,
+// chunk offsets and scratch slots in device memory.
+struct ChainPhase {
+  const Desc* descs;
+  const int64_t* chunk0;
+  int32_t* sacc;
+  int64_t total;  // chunks of the phase
+  int32_t count;  // problems of the phase
+  int32_t pad_;
+};
+static_assert(sizeof(ChainPhase) == 40, "ChainPhase is 40 bytes");
+// Sync words of a chained launch: an arrival word per workgroup (at most
+// kChainMaxWg), the release word, the error word.
+constexpr int kChainMaxWg = 1024;
+constexpr int kChainSyncWords = kChainMaxWg + 64;
+hipError_t launch_chain(const ChainPhase* phases, int nphase, int m,
+                        uint32_t* sync, int workgroups, hipStream_t s);
+
 // A token row's scales from its absmax: a = max(amax, 1e-5), one correctly
 // rounded 127 / a for the products and s_a = a / 127 for the rescale.
 struct QScale {

@@ -210,7 +210,11 @@ struct Group {
 // FUSED: the problem gives fp32 activations; each wave quantizes the rows it
 // needs into LDS (exactly as the quantization kernel does) and reads the
 // int8 values from there instead of through scalar loads.
-template <int TOK, bool FUSED>
+// CHAIN (persistent chained launch, FUSED only): the outputs are read later
+// in the same launch by waves on other XCDs, so they are stored at agent
+// scope (written through to the device's coherence point); the inputs are
+// read after an agent-scope acquire that drops stale cached copies.
+template <int TOK, bool FUSED, bool CHAIN = false>
 struct Stream {
   // problem
   const uint8_t* w;  // the problem's packed weights
@@ -369,8 +373,17 @@ struct Stream {
     if (row >= n) return;
     const int acc = sum - qsum[t];
     const size_t o = (size_t)t * n + row;
-    if (accout != nullptr) accout[o] = acc;
-    y[o] = __fmul_rn(__fmul_rn((float)acc, sw), sav[t]);
+    const float yv = __fmul_rn(__fmul_rn((float)acc, sw), sav[t]);
+    if constexpr (CHAIN) {
+      if (accout != nullptr)
+        __hip_atomic_store((int32_t*)accout + o, acc, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store((float*)y + o, yv, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+      if (accout != nullptr) accout[o] = acc;
+      y[o] = yv;
+    }
   }
 
   // This wave holds only part of row block rb (partial sums in sum[]).  Each
@@ -484,13 +497,18 @@ struct Stream {
   // stays in registers between the absmax and the quantization, longer rows
   // are read a second time (from cache).
   static constexpr int kBatch = 8;
+  // float4 i of an activation row (in a chained launch, read after the
+  // barrier's acquire, which dropped stale cached copies)
+  __device__ __forceinline__ v4f ldx(gcfloat4_ptr xr, int i) const {
+    return xr[i];
+  }
   __device__ __forceinline__ void load_batch(float4 (&v)[kBatch],
                                              gcfloat4_ptr xr, int b0,
                                              int n4) const {
     const int lane = threadIdx.x & 63;
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {  // clamped: repeats change no maximum
-      const v4f f = xr[min(b0 + u * 64 + lane, n4 - 1)];
+      const v4f f = ldx(xr, min(b0 + u * 64 + lane, n4 - 1));
       v[u] = make_float4(f.x, f.y, f.z, f.w);
     }
   }
@@ -524,7 +542,7 @@ struct Stream {
 #pragma unroll
       for (int u = 0; u < kBatch; ++u) {
         const int i = u * 64 + lane;
-        const v4f f = i < n4 ? xr[i] : v4f{0.0f, 0.0f, 0.0f, 0.0f};
+        const v4f f = i < n4 ? ldx(xr, i) : v4f{0.0f, 0.0f, 0.0f, 0.0f};
         v[u] = make_float4(f.x, f.y, f.z, f.w);
         if (i < n4) ss = sumsq4(ss, v[u]);
       }
@@ -533,7 +551,7 @@ struct Stream {
         for (int u = 0; u < kBatch; ++u) {
           const int i = b0 + u * 64 + lane;
           if (i < n4) {
-            const v4f f = xr[i];
+            const v4f f = ldx(xr, i);
             ss = sumsq4(ss, make_float4(f.x, f.y, f.z, f.w));
           }
         }
@@ -553,7 +571,7 @@ struct Stream {
         for (int u = 0; u < kBatch; ++u) {
           const int i = b0 + u * 64 + lane;
           if (i < n4) {
-            const v4f f = xr[i], gv = gr[i];
+            const v4f f = ldx(xr, i), gv = gr[i];
             amax = fmaxf(amax, absmax4(rms_apply(
                 make_float4(f.x, f.y, f.z, f.w), r,
                 make_float4(gv.x, gv.y, gv.z, gv.w))));
@@ -578,7 +596,7 @@ struct Stream {
         for (int u = 0; u < kBatch; ++u) {
           const int i = b0 + u * 64 + lane;
           if (i < n4) {
-            const v4f f = xr[i], gv = gr[i];
+            const v4f f = ldx(xr, i), gv = gr[i];
             const uint32_t q = quant4(
                 rms_apply(make_float4(f.x, f.y, f.z, f.w), r,
                           make_float4(gv.x, gv.y, gv.z, gv.w)),
@@ -634,15 +652,67 @@ struct Stream {
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   }
 
+  // State of a segment between the issue of its first weight groups and the
+  // rest of its work (a persistent launch issues them before it waits for
+  // the segment's inputs).
+  struct Seg {
+    int s0, s1, head_rb;
+    bool head_cut;
+    Group g, pg;  // the group consumed next and the last group issued
+    v4u ring[G][D];
+  };
+
+  // First groups of chunks [s0, s1) of the current problem in flight.
+  __device__ __forceinline__ void seg_issue(Seg& sg, int s0, int s1) const {
+    s0 = __builtin_amdgcn_readfirstlane(s0);
+    s1 = __builtin_amdgcn_readfirstlane(s1);
+    sg.s0 = s0;
+    sg.s1 = s1;
+    sg.head_rb = s0 / kc;
+    sg.head_cut = s0 != sg.head_rb * kc;  // first block starts early
+    sg.g.rb = sg.head_rb;
+    sg.g.c = s0 - sg.head_rb * kc;
+    sg.g.cnt = min(min(D, kc - sg.g.c), s1 - s0);
+    sg.g.uniform();
+    sg.pg = next(sg.g, s1);
+    load_group(sg.ring[0], sg.g);
+#pragma unroll
+    for (int i = 1; i < G; ++i) {
+      if (i > 1) sg.pg = next(sg.pg, s1);
+      load_group(sg.ring[i], sg.pg);
+    }
+  }
+
+  // FUSED: the rest of a segment whose first groups are in flight: quantize
+  // the rows, then stream and hand off.
+  __device__ __forceinline__ void seg_run(Seg& sg) {
+    int head_sum[TOK];
+#pragma unroll
+    for (int t = 0; t < TOK; ++t) head_sum[t] = 0;
+    Acc<TOK> a;
+    a.zero();
+    ocnt = 0;
+    orb0 = sg.head_rb + (sg.head_cut ? 1 : 0);  // first block finished whole
+    quantize_rows();
+    stream_rest(sg.ring, sg.g, sg.pg, sg.s0, sg.s1, sg.head_rb, sg.head_cut,
+                head_sum, a);
+  }
+
   // Stream chunks [s0, s1) of the current problem (problem-local indices) in
-  // groups of up to D chunks, double buffered: while group i is consumed,
-  // group i + 1 is in flight.  Every load is unconditional (range-checked),
-  // so the wait before each group is a fixed count (the other buffer's D
-  // loads); the loop's only other memory operations are LDS writes and the
-  // occasional burst of a full staging area.  A row block cut by the range
-  // (at most the first and the last) keeps its partial sums in registers;
-  // their hand-off happens after the loop.
+  // groups of up to D chunks, G groups in flight: while one group is
+  // consumed, the next G - 1 are in flight.  Every load is unconditional
+  // (range-checked), so the wait before each group is a fixed count (the
+  // other groups' loads); the loop's only other memory operations are LDS
+  // writes and the occasional burst of a full staging area.  A row block cut
+  // by the range (at most the first and the last) keeps its partial sums in
+  // registers; their hand-off happens after the loop.
   __device__ __forceinline__ void segment(int s0, int s1) {
+    if constexpr (FUSED) {
+      Seg sg;
+      seg_issue(sg, s0, s1);
+      seg_run(sg);
+      return;
+    }
     s0 = __builtin_amdgcn_readfirstlane(s0);
     s1 = __builtin_amdgcn_readfirstlane(s1);
     const int head_rb = s0 / kc;
@@ -664,25 +734,25 @@ struct Stream {
     // is the last group issued
     v4u ring[G][D];
     load_group(ring[0], g);
-    if constexpr (FUSED) {
+    ActPre pre;
+    issue_act(pre);
 #pragma unroll
-      for (int i = 1; i < G; ++i) {
-        if (i > 1) pg = next(pg, s1);
-        load_group(ring[i], pg);
-      }
-      quantize_rows();
-    } else {
-      ActPre pre;
-      issue_act(pre);
-#pragma unroll
-      for (int i = 1; i < G; ++i) {
-        if (i > 1) pg = next(pg, s1);
-        load_group(ring[i], pg);
-      }
-      finish_act(pre);
-#pragma unroll
-      for (int t = 0; t < TOK; ++t) sav[t] = sa[t];
+    for (int i = 1; i < G; ++i) {
+      if (i > 1) pg = next(pg, s1);
+      load_group(ring[i], pg);
     }
+    finish_act(pre);
+#pragma unroll
+    for (int t = 0; t < TOK; ++t) sav[t] = sa[t];
+    stream_rest(ring, g, pg, s0, s1, head_rb, head_cut, head_sum, a);
+  }
+
+  // The loop of a segment and its hand-offs.
+  __device__ __forceinline__ void stream_rest(v4u (&ring)[G][D], Group g,
+                                              Group pg, int s0, int s1,
+                                              int head_rb, bool head_cut,
+                                              int (&head_sum)[TOK],
+                                              Acc<TOK>& a) {
     bool more = true;
     while (more) {
 #pragma unroll
@@ -882,7 +952,242 @@ __global__ __launch_bounds__(64 * WPW) void stream_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Persistent chained decode: the phases of one token (each a fused plan whose
+// fp32 input is an output of an earlier phase) in one cooperative launch,
+// with a grid-wide barrier between phases.  A wave's range of a phase is
+// split in two: range_begin finds the first problem and issues the first
+// groups of its weights (which depend on nothing computed in the launch), so
+// it runs before the barrier that precedes the phase; range_run quantizes
+// the input and does the rest after it.
+
+struct RangeCursor {
+  int p;         // problem after the first segment
+  int64_t pos;   // first chunk after the first segment
+  bool active;   // the range is not empty
+};
+
+template <int TOK, bool CHAIN>
+__device__ __forceinline__ void take_problem(Stream<TOK, true, CHAIN>& st,
+                                             const Desc& d) {
+  st.gain = (gcfloat_ptr)d.g;
+  st.eps = d.eps;
+  st.sa = (const_fptr)d.sa;
+  st.y = (gfloat_ptr)d.y;
+  st.accout = (gint_ptr)d.acc;
+  st.sw = d.sw;
+  st.n = d.n;
+  st.blk0 = d.blk0;
+}
+
+template <int TOK, bool CHAIN>
+__device__ __forceinline__ void range_begin(
+    Stream<TOK, true, CHAIN>& st, typename Stream<TOK, true, CHAIN>::Seg& sg,
+    RangeCursor& rc, const Desc* __restrict__ descs,
+    const int64_t* __restrict__ chunk0s, int count, int64_t lo, int64_t hi) {
+  rc.active = lo < hi;
+  if (!rc.active) return;
+  st.lo = lo;
+  st.hi = hi;
+  const ProbStart ps = find_problem<true>(descs, chunk0s, count, lo);
+  const Desc& d = descs[ps.p];
+  int64_t chunks;
+  if (ps.have) {
+    st.w = ps.w;
+    st.xf = (gcfloat_ptr)ps.x;
+    st.kc = ps.kc;
+    st.k = ps.kc * 64;
+    st.chunk0 = ps.chunk0;
+    chunks = (int64_t)ps.nblk * ps.kc;
+  } else {
+    st.w = d.w;
+    st.xf = (gcfloat_ptr)d.xf;
+    st.kc = d.kc;
+    st.k = d.k;
+    st.chunk0 = d.chunk0;
+    chunks = (int64_t)d.nblk * d.kc;
+  }
+  take_problem(st, d);
+  const int64_t s0 = lo - st.chunk0;
+  const int64_t s1 = min(chunks, hi - st.chunk0);
+  st.seg_issue(sg, (int)s0, (int)s1);
+  rc.p = ps.p + 1;
+  rc.pos = st.chunk0 + s1;
+}
+
+template <int TOK, bool CHAIN>
+__device__ __forceinline__ void range_run(
+    Stream<TOK, true, CHAIN>& st, typename Stream<TOK, true, CHAIN>::Seg& sg,
+    const RangeCursor& rc, const Desc* __restrict__ descs, int count) {
+  if (!rc.active) return;
+  st.seg_run(sg);
+  int p = rc.p;
+  int64_t pos = rc.pos;
+  while (pos < st.hi && p < count) {
+    const Desc& d = descs[p];
+    st.w = d.w;
+    st.xf = (gcfloat_ptr)d.xf;
+    st.kc = d.kc;
+    st.k = d.k;
+    st.chunk0 = d.chunk0;
+    take_problem(st, d);
+    const int64_t chunks = (int64_t)d.nblk * d.kc;
+    const int64_t s0 = pos - st.chunk0;
+    const int64_t s1 = min(chunks, st.hi - st.chunk0);
+    st.segment((int)s0, (int)s1);
+    pos = st.chunk0 + s1;
+    ++p;
+  }
+}
+
+// Grid-wide barrier between phases (all workgroups resident: cooperative
+// launch).  Every wave first waits for its own memory operations (its
+// outputs are agent-scope stores, so they are then at the coherence point);
+// after a workgroup barrier its first thread stores the phase number into
+// the workgroup's arrival word.  Workgroup 0 watches every arrival word and
+// then stores the phase number into the release word, which the first
+// thread of every workgroup watches.  (Every workgroup watching every
+// arrival word instead, without the release word, was slower: 1.62 against
+// 1.38 ms per token of the 2B chained decode.)  All words are read and
+// written at agent scope.  Every wait is bounded by the real-time clock: a
+// workgroup that gives up sets the error word, every waiter also stops when
+// it sees it, and the launch then ends with its outputs invalid.
+constexpr uint64_t kChainTimeoutTicks = 50000000;  // 0.5 s at 100 MHz
+
+__device__ __forceinline__ bool grid_barrier(uint32_t* sync, uint32_t target,
+                                             int* ok_flag) {
+  uint32_t* arrive = sync;
+  uint32_t* gen = sync + kChainMaxWg;
+  uint32_t* err = sync + kChainMaxWg + 1;
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    if (lane == 0)
+      __hip_atomic_store(arrive + blockIdx.x, target, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+    if (blockIdx.x == 0) {
+      while (true) {
+        bool ok = true;
+        for (int i = lane; i < (int)gridDim.x; i += 64)
+          ok = ok && __hip_atomic_load(arrive + i, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT) >= target;
+        if (__all(ok)) break;
+        if (__hip_atomic_load(err, __ATOMIC_RELAXED,
+                              __HIP_MEMORY_SCOPE_AGENT) != 0)
+          break;
+        if (__builtin_amdgcn_s_memrealtime() - t0 > kChainTimeoutTicks) {
+          if (lane == 0)
+            __hip_atomic_store(err, 1u, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+      }
+      if (lane == 0)
+        __hip_atomic_store(gen, target, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    } else if (lane == 0) {
+      while (__hip_atomic_load(gen, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT) < target &&
+             __hip_atomic_load(err, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT) == 0) {
+        if (__builtin_amdgcn_s_memrealtime() - t0 > kChainTimeoutTicks) {
+          __hip_atomic_store(err, 1u, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+      }
+    }
+    if (lane == 0)
+      *ok_flag = __hip_atomic_load(err, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT) == 0;
+    // acquire: drop the XCD's L2 and this CU's L1 copies of lines that
+    // other XCDs wrote in the phase just ended (the next phase's input),
+    // so that the loads after the barrier fetch them afresh
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    __builtin_amdgcn_s_waitcnt(0);
+  }
+  __syncthreads();
+  return *ok_flag != 0;  // one value for the whole workgroup
+}
+
+// One token's phases.  A phase of T chunks is streamed by
+// W = min(waves, max(1, T / 4)) waves (at least four chunks each, as the
+// launched plans have), in equal ranges, exactly as stream_kernel does.
+template <int TOK>
+__global__ __launch_bounds__(256) void chain_kernel(
+    const ChainPhase* __restrict__ phases, int nphase, uint32_t* sync) {
+  constexpr int WPW = 4;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int64_t wv = (int64_t)blockIdx.x * WPW + wave;
+  Stream<TOK, true, true> st;
+  __shared__ int obuf_all[WPW][16 * 64];
+  __shared__ v4u xl_all[WPW][BT_FUSED_MAX_MK / 16];
+  __shared__ int ok_flag;
+  st.obuf = obuf_all[wave];
+  st.xl = (lds_i8_ptr)xl_all[wave];
+  typename Stream<TOK, true, true>::Seg sg;
+  RangeCursor rc;
+  auto begin = [&](int ph) {
+    const ChainPhase P = phases[ph];
+    const int64_t total = P.total;
+    const int64_t W = min((int64_t)gridDim.x * WPW, max((int64_t)1, total / 4));
+    st.sacc = P.sacc;
+    st.head_local = false;
+    st.tail_local = false;
+    rc.active = false;
+    if (wv < W) {
+      st.prev_lo = wv > 0 ? (wv - 1) * total / W : 0;
+      st.next_hi = wv + 1 < W ? (wv + 2) * total / W : total;
+      st.prev_in_wg = wave > 0;
+      st.next_in_wg = wave < WPW - 1 && wv + 1 < W;
+      range_begin(st, sg, rc, P.descs, P.chunk0, P.count, wv * total / W,
+                  (wv + 1) * total / W);
+    }
+  };
+  begin(0);
+  for (int ph = 0; ph < nphase; ++ph) {
+    range_run(st, sg, rc, phases[ph].descs, phases[ph].count);
+    // cut blocks shared by two waves of this workgroup only (as in
+    // stream_kernel)
+    if (st.head_local) {
+#pragma unroll
+      for (int t = 0; t < TOK; ++t) st.obuf[t * 64 + lane] = st.head_keep[t];
+    }
+    __syncthreads();
+    if (st.tail_local) {
+      const int* other = obuf_all[wave + 1];
+#pragma unroll
+      for (int t = 0; t < TOK; ++t)
+        st.write_one(st.tail_rb_local, t,
+                     st.tail_keep[t] + other[t * 64 + lane]);
+    }
+    if (ph + 1 == nphase) break;
+    begin(ph + 1);
+    if (!grid_barrier(sync, (uint32_t)(ph + 1), &ok_flag)) return;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_chain(const ChainPhase* phases, int nphase, int m,
+                        uint32_t* sync, int workgroups, hipStream_t s) {
+  void* args[] = {(void*)&phases, (void*)&nphase, (void*)&sync};
+  const void* f;
+  switch (m) {
+    case 1: f = (const void*)chain_kernel<1>; break;
+    case 2: f = (const void*)chain_kernel<2>; break;
+    case 3: f = (const void*)chain_kernel<3>; break;
+    case 4: f = (const void*)chain_kernel<4>; break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipLaunchCooperativeKernel(f, dim3((unsigned)workgroups), dim3(256),
+                                    args, 0, s);
+}
 
 // `workgroups` counts 4-wave workgroups; with WPW = 8 the same waves are
 // regrouped in half as many.

@@ -315,6 +315,38 @@ int64_t bt_grouped_plan_norm_bytes(const bt_problem_norm* probs,
 int32_t bt_grouped_plan_norm(const bt_problem_norm* probs, int32_t count,
                              void* plan, int64_t plan_bytes);
 
+/* Layer-chained decode in one persistent launch: the phases of one token,
+ * each a fused plan (bt_grouped_plan_f32 or bt_grouped_plan_norm, one m for
+ * all) whose fp32 input may be an output of an earlier phase, run in order
+ * in one cooperative launch with a grid-wide barrier between phases.  The
+ * results are bit for bit those of launching the plans one after another
+ * with bt_gemm_grouped.  (The decode step of a ternary model runs its
+ * projections in dependent order: "1bit-systems：在AMD Strix Halo上实现纯
+ * Rust本地三值权重LLM推理", section "技术架构：Rust在上，HIP在下", puts the
+ * GEMV, RMSNorm and attention kernels of one step behind one native call.)
+ * Use: bytes = bt_chain_plan_bytes(count); fill a host buffer with
+ * bt_chain_plan from the phases' device plans and host images; copy it to
+ * device memory the caller owns (256-byte aligned, writable: every launch
+ * zeroes and uses its sync words); launch with bt_gemm_chain.  The plans
+ * must stay alive and unchanged; launches of one chain image (or sharing a
+ * phase plan) must not overlap.
+ * Every wait of the barrier is bounded (0.5 s): if one gives up, the int32
+ * at byte BT_CHAIN_STATUS_OFFSET of the device image is nonzero after the
+ * launch and the outputs are invalid; it is 0 after a complete launch.
+ * Errors: BT_E_ARG for a plan that is not fused or a bad count, BT_E_SHAPE
+ * for plans of different m; the launch fails with BT_E_HIP if the GPU cannot
+ * hold every workgroup at once. */
+#define BT_MAX_CHAIN_PHASES 4096
+#define BT_CHAIN_STATUS_OFFSET 4356
+typedef struct bt_chain_phase {
+  void* plan_dev;         /* device copy of the phase's plan */
+  const void* plan_host;  /* its host image */
+} bt_chain_phase;
+int64_t bt_chain_plan_bytes(int32_t count);
+int32_t bt_chain_plan(const bt_chain_phase* phases, int32_t count,
+                      void* chain_host, int64_t chain_bytes);
+int32_t bt_gemm_chain(void* chain_dev, const void* chain_host, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

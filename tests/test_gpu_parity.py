@@ -896,20 +896,26 @@ def oracle_chain(work, layers, norm=False):
     return outs, boundary
 
 
-@pytest.mark.parametrize("fused,norm", [(False, False), (True, False),
-                                        (False, True), (True, True)])
-def test_chained_decode_matches_oracle(fused, norm):
+@pytest.mark.parametrize("fused,norm,persistent", [
+    (False, False, False), (True, False, False), (False, True, False),
+    (True, True, False), (True, False, True), (True, True, True)])
+def test_chained_decode_matches_oracle(fused, norm, persistent):
     """Two 2B-shaped layers chained phase by phase (two launches per phase,
     or one launch that quantizes its fp32 input; with norm, RMSNorm before
     every quantization): every output of every projection equals the
     oracle's bit for bit (each phase's fp32 output is the next phase's
     input), eagerly and on each replay of the token captured as a HIP graph,
-    with eager launches between the replays."""
+    with eager launches between the replays.  persistent: every phase of
+    the token in one cooperative launch with grid barriers between phases;
+    its status word must report a complete launch each time."""
     import bench
     work = wl.decode_2b(1)
-    cs = bench.ChainSet(work, torch, bt, layers=2, fused=fused, norm=norm)
+    cs = bench.ChainSet(work, torch, bt, layers=2, fused=fused, norm=norm,
+                        persistent=persistent)
     cs.step()
     torch.cuda.synchronize()
+    if persistent:
+        assert bt.bt_chain_status(cs.chain) == 0
     ref, boundary = oracle_chain(work, 2, norm)
     assert not boundary, "an RMSNorm scale sits on a rounding boundary"
 
@@ -920,14 +926,21 @@ def test_chained_decode_matches_oracle(fused, norm):
                 assert np.array_equal(got, ref[l][proj]), (label, l, proj)
 
     check("eager")
-    graph = cs.capture()
+    # the persistent launch is one cooperative launch per token: it is
+    # repeated eagerly instead of from a graph
+    graph = None if persistent else cs.capture()
     for rep in range(3):
         for ys in cs.y:
             for t in ys.values():
                 t.fill_(float("nan"))
-        graph.replay()
+        if graph is None:
+            cs.step()
+        else:
+            graph.replay()
         torch.cuda.synchronize()
         check(f"replay {rep}")
+        if persistent:
+            assert bt.bt_chain_status(cs.chain) == 0
         cs.step()
         torch.cuda.synchronize()
         check(f"eager after replay {rep}")
