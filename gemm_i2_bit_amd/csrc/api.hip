@@ -634,11 +634,16 @@ int32_t bt_gemm_grouped_static(const void* plan_dev, const void* plan_host,
   if (sst != BT_OK) return sst;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   // every launch starts from zeroed slots and counters: the array keeps
-  // whatever the last call on this device left in it
-  if (need > 0) {
-    const int64_t words = need / 16;
+  // whatever the last call on this device left in it.  The matrix-core
+  // kinds write every partial-sum region before it is read, so only their
+  // counters are cleared; the streaming kind accumulates into its slots.
+  const int64_t zero_from =
+      h.kind == bt::kKindDot4 ? 0 : h.scnt_off - h.sacc_off;
+  if (need > zero_from) {
+    const int64_t words = (need - zero_from) / 16;
     zero_kernel<<<dim3((unsigned)std::min<int64_t>((words + 255) / 256, 4096)),
-                  dim3(256), 0, s>>>(reinterpret_cast<uint4*>(scr), words);
+                  dim3(256), 0, s>>>(
+        reinterpret_cast<uint4*>(scr + zero_from), words);
     if (hipGetLastError() != hipSuccess) return BT_E_HIP;
   }
   return launch_plan(const_cast<void*>(plan_dev), h, scr,

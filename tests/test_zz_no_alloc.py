@@ -1,6 +1,6 @@
 """bt_gemm_grouped_static, the grouped product for callers that cannot
 allocate: through the C ABI, its outputs equal bt_gemm_grouped's bit for bit
-(and the oracle's) on plans of both kinds, on calls in a row that share the
+(and the oracle's) on plans of every kind, on calls in a row that share the
 library's static scratch array, the second with a smaller input."""
 import numpy as np
 import pytest
@@ -86,3 +86,10 @@ def test_static_scratch_matches_grouped():
     # 4. the first plan again, and m = 3 (three tokens per slot)
     check(*big, "full grid m=1 again")
     check(*make_case([(2560, 2560), (640, 6912)], 3, 123), "m=3")
+    # 5. skinny matrix-core plans (m = 8 and 40; no scratch), then the
+    #    split prefill plan again: its counters were left zero by the last
+    #    launch that used them, and only they are cleared
+    check(*make_case([(600, 16384), (2560, 2560), (640, 6912)], 8, 124),
+          "matrix cores m=8")
+    check(*make_case([(300, 4096), (640, 2560)], 40, 125), "matrix cores m=40")
+    check(*split, "split ranges m=130 again")
