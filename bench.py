@@ -636,6 +636,12 @@ def main():
         roof["measured_ceiling_gb_s"] = ceiling["gb_s"]
         roof["frac_of_measured_ceiling"] = round(
             roof["achieved"] / ceiling["gb_s"], 4)
+        # the same probe over as many bytes as one product launch moves: a
+        # launch of this size pays the same ramp and drain as the kernel
+        same = read_ceiling(torch, bt, nbytes=ws.product_bytes() // 1024 * 1024)
+        roof["measured_ceiling_same_bytes_gb_s"] = same["gb_s"]
+        roof["frac_of_ceiling_same_bytes"] = round(
+            roof["achieved"] / same["gb_s"], 4)
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": unit,
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
