@@ -46,7 +46,8 @@ static_assert(sizeof(Desc) == 128, "Desc is 128 bytes");
 
 // One work unit of a grouped launch: problem index and a sub-index whose
 // meaning depends on the kernel: for the matrix-core kinds,
-// (256-row tile * ntt + token tile) * nsplit + reduction range.
+// (256-row tile * ntt + token tile) * nsplit + reduction range.  Problem -1
+// marks padding that keeps an XCD-ordered unit list aligned.
 struct Unit {
   int32_t prob;
   int32_t sub;

@@ -629,12 +629,14 @@ __global__ __launch_bounds__(256, 2) void tiled_kernel(Desc d, int ntt) {
   run_tile<C>(d, u / ntt, u % ntt, 0, 0, d.k >> 6, nullptr, nullptr);
 }
 
-// Unit sub-index: (256-row tile * ntt + token tile) * nsplit + range.
+// Unit sub-index: (256-row tile * ntt + token tile) * nsplit + range; a
+// unit of problem -1 is padding and does nothing.
 template <class C>
 __global__ __launch_bounds__(256, 2) void tiled_grouped_kernel(
     const Desc* __restrict__ descs, const Unit* __restrict__ units,
     int32_t* sacc, int32_t* scnt) {
   const Unit u = units[blockIdx.x];
+  if (u.prob < 0) return;  // padding of an XCD-ordered plan
   const Desc d = descs[u.prob];
   const int ntt = (d.m + C::BM - 1) / C::BM;
   const int tile = u.sub / d.nsplit;

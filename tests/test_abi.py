@@ -239,6 +239,43 @@ def test_grouped_plan_layout_mfma(L):
     assert p["scnt_off"] == p["sacc_off"]  # no scratch for this kind
 
 
+@pytest.mark.parametrize("m", [8, 32, 64])
+def test_grouped_plan_xcd_order(L, m):
+    """Skinny matrix-core plans of the 2B-shaped decode set (30 layers x 7
+    projections): whole problems per XCD (workgroup i runs on XCD i mod 8),
+    longest reductions first within each XCD, every unit once, padding
+    (problem -1) only after an XCD's last unit, and the XCDs' work within a
+    few percent of each other."""
+    shapes = [(2560, 2560), (640, 2560), (640, 2560), (2560, 2560),
+              (6912, 2560), (6912, 2560), (2560, 6912)]
+    specs = [(n, k, m) for _ in range(30) for n, k in shapes]
+    arr = problems(specs)
+    nbytes = L.bt_grouped_plan_bytes(arr, len(specs))
+    img = np.zeros(nbytes, np.uint8)
+    assert L.bt_grouped_plan(arr, len(specs), img.ctypes.data, nbytes) == 0
+    p = parse_plan(img)
+    assert p["kind"] == 1 and p["units"] % 8 == 0
+    u = p["unit"]
+    tiles = [(n + 255) // 256 for n, _, _ in specs]
+    real = [tuple(x) for x in u.tolist() if x[0] >= 0]
+    assert sorted(real) == sorted((i, t) for i, n in enumerate(tiles)
+                                  for t in range(n))
+    work = [0] * 8
+    for x in range(8):
+        col = u[x::8]
+        live = col[:, 0] >= 0
+        nlive = int(live.sum())
+        assert live[:nlive].all() and not live[nlive:].any()
+        ks = [specs[i][1] for i in col[:nlive, 0]]
+        assert ks == sorted(ks, reverse=True)
+        work[x] = sum(k // 64 for k in ks)
+    owner = {}
+    for pos, (prob, _) in enumerate(u.tolist()):
+        if prob >= 0:
+            assert owner.setdefault(prob, pos % 8) == pos % 8
+    assert max(work) <= 1.05 * min(work)
+
+
 def test_grouped_plan_layout_prefill(L):
     # m >= 65: 256-row x 128-token tiles; the k=6912 problem's reduction is
     # cut into 3 ranges of 36 chunks (about the 40 chunks of k=2560, even)
