@@ -560,6 +560,15 @@ def cpu_baseline(work: wl.Workload, ps: PackedSet, seconds: float,
                        f"+ product; {timed:.1f} s timed)")
 
 
+def device_info(torch):
+    """The GPU the line was measured on (the rooflines assume an MI355X:
+    256 CUs at 2.4 GHz)."""
+    pr = torch.cuda.get_device_properties(0)
+    return {"name": pr.name, "arch": getattr(pr, "gcnArchName", None),
+            "compute_units": pr.multi_processor_count,
+            "memory_gib": round(pr.total_memory / 2**30, 1)}
+
+
 def load_profile(name: str, sha: str, key: str):
     """A figure from a counter summary in profiles/ (null once the kernel
     sources have changed since the counters were taken)."""
@@ -632,6 +641,14 @@ def main():
                     "mfma" if prefill else "hbm",
                     load_profile(f"traffic_{prof}.json", sha,
                                  "hbm_bytes_per_launch"))
+    if not prefill:
+        # the same kernel time over the packed weight bytes alone
+        wgbs = ws.weight_bytes() / (kern_avg * 1e-3) / 1e9
+        roof["weight_gb_s"] = round(wgbs, 1)
+        roof["weight_frac"] = round(wgbs / HBM_PEAK_GBS, 4)
+        if ceiling:
+            roof["weight_frac_of_measured_ceiling"] = round(
+                wgbs / ceiling["gb_s"], 4)
     if ceiling and not prefill:
         roof["measured_ceiling_gb_s"] = ceiling["gb_s"]
         roof["frac_of_measured_ceiling"] = round(
@@ -656,6 +673,7 @@ def main():
                    "tokens_per_s_equiv": round(work.m / (ms_step * 1e-3), 1),
                    "tops": round(ws.ops() / (kern_avg * 1e-3) / 1e12, 3)},
         "roofline": roof,
+        "device": device_info(torch),
     }
     if extra and args.mode == "grouped":
         pl = per_launch_ms(ws, torch)
