@@ -236,10 +236,16 @@ PlanHeader plan_layout(const bt_problem* probs, int32_t count, bool fused) {
   h.units = h.kind == bt::kKindDot4
                 ? units
                 : (int64_t)plan_units(probs, count, m, h.kind, split).size();
+  // streaming kind: a start entry per wave of a launch on the current
+  // device (none when no device answers)
+  const int cus = h.kind == bt::kKindDot4 ? cu_count() : 0;
+  h.start_waves = cus > 0 ? bt::stream_waves(chunks, cus) : 0;
   auto up = [](int64_t x) { return (x + 255) / 256 * 256; };
   h.desc_off = up(sizeof(PlanHeader));
   h.chunk_off = up(h.desc_off + (int64_t)count * sizeof(Desc));
-  h.unit_off = up(h.chunk_off + (int64_t)count * 8);
+  h.start_off = up(h.chunk_off + (int64_t)count * 8);
+  h.unit_off =
+      up(h.start_off + h.start_waves * (int64_t)sizeof(bt::WaveStart));
   h.sacc_off = up(h.unit_off + h.units * (int64_t)sizeof(Unit));
   // streaming kind: one 64-bit slot (arrival count and partial total) per
   // row, token and row block; matrix-core kinds: split-reduction regions
@@ -289,7 +295,10 @@ int32_t read_plan_header(const void* plan_host, PlanHeader* out) {
       h.kind != bt::group_kind(h.m, h.total_chunks, h.fused == 1) ||
       h.desc_off != 256 ||
       h.bytes < h.scnt_off || h.scnt_off < h.sacc_off ||
-      h.sacc_off < h.unit_off || h.unit_off < h.chunk_off ||
+      h.sacc_off < h.unit_off || h.start_off < h.chunk_off + 8 * h.count ||
+      h.start_waves < 0 || h.start_waves > h.total_chunks ||
+      (h.start_waves > 0 && h.kind != bt::kKindDot4) ||
+      h.unit_off < h.start_off + h.start_waves * (int64_t)sizeof(bt::WaveStart) ||
       h.chunk_off < h.desc_off + (int64_t)h.count * (int64_t)sizeof(Desc) ||
       (h.kind != bt::kKindDot4 && h.units < 1) ||
       (h.fused == 1 && h.kind != bt::kKindDot4) || h.sacc_off % 256 != 0 ||
@@ -313,15 +322,16 @@ int32_t launch_plan(void* plan_dev, const PlanHeader& h, unsigned char* sacc,
   }
   const int cus = cu_count();
   if (cus <= 0) return BT_E_HIP;
-  // at least a group of 4 chunks per wave (counted in workgroups of 4 waves;
-  // the launch may regroup the same waves): a wave's set-up and hand-offs
-  // cost about what streaming a few chunks does, so small plans (one phase
-  // of a chained decode) run on fewer, fuller waves
-  const int64_t wgs = std::min<int64_t>((int64_t)cus * bt::kStreamWgPerCu,
-                                        (h.total_chunks + 15) / 16);
+  // workgroups of 4 waves (the launch may regroup the same waves)
+  const int64_t wgs = bt::stream_workgroups(h.total_chunks, cus);
+  // the start table holds only if it was written for this wave count
+  const bt::WaveStart* starts =
+      h.start_waves > 0 && h.start_waves == bt::stream_waves(h.total_chunks, cus)
+          ? reinterpret_cast<const bt::WaveStart*>(base + h.start_off)
+          : nullptr;
   return hip_status(bt::launch_stream_grouped(
-      descs, reinterpret_cast<const int64_t*>(base + h.chunk_off), h.count,
-      h.total_chunks, h.m, reinterpret_cast<int32_t*>(sacc), (int)wgs,
+      descs, reinterpret_cast<const int64_t*>(base + h.chunk_off), starts,
+      h.count, h.total_chunks, h.m, reinterpret_cast<int32_t*>(sacc), (int)wgs,
       h.fused == 1, wgs == (int64_t)cus * bt::kStreamWgPerCu, s));
 }
 
@@ -551,6 +561,34 @@ static int32_t build_plan(const bt_problem* probs, int32_t count, void* plan,
     const std::vector<Unit> units =
         plan_units(probs, count, h.m, h.kind, split);
     memcpy(out + h.unit_off, units.data(), units.size() * sizeof(Unit));
+  }
+  // start table: wave w of W streams chunks [w T / W, (w + 1) T / W); its
+  // first chunk lies in the last problem whose first chunk is not past it
+  const int64_t W = h.start_waves, T = h.total_chunks;
+  int32_t p = 0;
+  int64_t p0 = 0;  // first chunk of problem p
+  int64_t next0 = (probs[0].n + 63) / 64 * (probs[0].k / 64);
+  for (int64_t w = 0; w < W; ++w) {
+    const int64_t lo = w * T / W;
+    while (p + 1 < count && next0 <= lo) {
+      ++p;
+      p0 = next0;
+      next0 += (probs[p].n + 63) / 64 * (probs[p].k / 64);
+    }
+    bt::WaveStart e;
+    memset(&e, 0, sizeof(e));
+    e.lo = lo;
+    e.hi = (w + 1) * T / W;
+    e.prev_lo = w > 0 ? (w - 1) * T / W : 0;
+    e.next_hi = w + 1 < W ? (w + 2) * T / W : T;
+    e.w = probs[p].packed;
+    e.x = xf ? static_cast<const void*>(xf[p])
+             : static_cast<const void*>(probs[p].x_q);
+    e.chunk0 = p0;
+    e.p = p;
+    e.kc = (int32_t)(probs[p].k / 64);
+    e.nblk = (int32_t)((probs[p].n + 63) / 64);
+    memcpy(out + h.start_off + w * (int64_t)sizeof(e), &e, sizeof(e));
   }
   return BT_OK;
 }

@@ -53,12 +53,38 @@ struct Unit {
   int32_t sub;
 };
 
+// Where one wave of a streaming launch starts: the wave's range of the
+// concatenated chunk stream (wave w of W streams chunks [w T / W,
+// (w + 1) T / W) of the T chunks), its neighbours' range ends, and the
+// problem that holds its first chunk with what the wave needs to issue its
+// first weight loads.  One entry is one cache line, read with scalar loads;
+// without the table every wave divides for its bounds and searches the
+// problems' first chunks, every lane gathering descriptors, at the start of
+// the launch: a median 2.5 us of the 2B set's M=1 launch went by before a
+// wave's first weight load.
+struct WaveStart {
+  const uint8_t* w;  // packed weights of problem p
+  const void* x;     // int8 (xq) or, for fused plans, fp32 (xf) activations
+  int64_t chunk0;    // first chunk of problem p in the stream
+  int64_t lo, hi;    // the wave's chunks [lo, hi)
+  int32_t p;
+  int32_t kc;        // chunks per row block of problem p
+  int32_t nblk;      // row blocks of problem p
+  int32_t pad0_;
+  int64_t prev_lo;   // first chunk of the previous wave (0 for wave 0)
+  int64_t next_hi;   // end of the next wave's range (T for the last wave)
+  int64_t pad_[7];
+};
+static_assert(sizeof(WaveStart) == 128, "WaveStart is 128 bytes");
+
 // Host-side header at the start of a grouped plan image.  Layout:
-//   PlanHeader | Desc[count] | int64 chunk0[count] | Unit[units] |
-//   int32 scratch_acc[...] | int32 scratch_cnt[...]
+//   PlanHeader | Desc[count] | int64 chunk0[count] | WaveStart[start_waves] |
+//   Unit[units] | int32 scratch_acc[...] | int32 scratch_cnt[...]
 // The streaming kind has units = 0, one slot of m * 64 int64 (arrival count
 // in the high half, partial total in the low half) per row block, and no
-// counters.
+// counters.  Its start table is written for the wave count of a launch on
+// the device that was current when the plan was built (start_waves = 0 if
+// none was); a launch with another wave count searches instead.
 // The matrix-core kinds have, for the problems whose reduction is split, one
 // region of 64 * token_tile ints per (row block, token tile, range) and one
 // counter per (row block, token tile); none otherwise.
@@ -77,7 +103,9 @@ struct PlanHeader {
   int64_t total_chunks;
   int64_t blocks;      // row blocks over all problems
   int64_t fused;       // 1: the problems give fp32 activations (Desc::xf)
-  int64_t pad[4];
+  int64_t start_off;   // byte offset of WaveStart[start_waves]
+  int64_t start_waves; // waves the start table is written for (0: none)
+  int64_t pad[2];
 };
 static_assert(sizeof(PlanHeader) == 128, "PlanHeader is 128 bytes");
 
@@ -126,6 +154,20 @@ inline int64_t split_region_ints(int64_t m) { return 64 * token_tile(m); }
 #define BT_STREAM_WG_PER_CU 2
 #endif
 constexpr int kStreamWgPerCu = BT_STREAM_WG_PER_CU;  // persistent grid: WGs/CU
+// Workgroups of 4 waves in a streaming launch over total_chunks on `cus`
+// compute units: a persistent grid, but at least a group of 4 chunks per
+// wave (a wave's set-up and hand-offs cost about what streaming a few chunks
+// does, so small plans, one phase of a chained decode, run on fewer, fuller
+// waves).  The kernel streams with min(4 * workgroups, total_chunks) waves.
+inline int64_t stream_workgroups(int64_t total_chunks, int cus) {
+  const int64_t full = (int64_t)cus * kStreamWgPerCu;
+  const int64_t need = (total_chunks + 15) / 16;
+  return full < need ? full : need;
+}
+inline int64_t stream_waves(int64_t total_chunks, int cus) {
+  const int64_t w = 4 * stream_workgroups(total_chunks, cus);
+  return w < total_chunks ? w : total_chunks;
+}
 
 // Launchers (host code in the kernels' translation units).
 hipError_t launch_pack(const int8_t* t, int64_t n, int64_t k, uint8_t* packed,
@@ -146,10 +188,12 @@ inline int row_block_waves(int64_t nblk, int kc) {
 hipError_t launch_dot4(const Desc& d, hipStream_t s);
 hipError_t launch_lut(const Desc& d, hipStream_t s);  // m = 1 only
 // full: the grid fills every CU (workgroups == CUs * kStreamWgPerCu)
+// starts: the plan's start table for this launch's wave count, or null
 hipError_t launch_stream_grouped(const Desc* descs, const int64_t* chunk0,
-                                 int32_t count, int64_t total_chunks, int m,
-                                 int32_t* sacc, int workgroups, bool fused,
-                                 bool full, hipStream_t s);
+                                 const WaveStart* starts, int32_t count,
+                                 int64_t total_chunks, int m, int32_t* sacc,
+                                 int workgroups, bool fused, bool full,
+                                 hipStream_t s);
 
 // One phase of a persistent chained launch: a fused plan's descriptors,
 // chunk offsets and scratch slots in device memory.

@@ -47,6 +47,7 @@ namespace {
 typedef unsigned v4u __attribute__((ext_vector_type(4)));
 typedef const __attribute__((address_space(4))) int* const_iptr;
 typedef const __attribute__((address_space(4))) float* const_fptr;
+typedef const __attribute__((address_space(4))) WaveStart* const_start_ptr;
 typedef const __attribute__((address_space(1))) v4u* gv4u_ptr;
 typedef __attribute__((address_space(1))) float* gfloat_ptr;
 typedef __attribute__((address_space(1))) int32_t* gint_ptr;
@@ -835,16 +836,31 @@ struct Stream {
 };
 
 // Chunks [lo, hi) of the concatenated stream, problem by problem.
+// `start`: the wave's entry of the plan's start table (problem p holds chunk
+// lo), or null: then the wave searches the problems' first chunks.
 template <int TOK, bool FUSED>
 __device__ __forceinline__ void stream_range(Stream<TOK, FUSED>& st,
                                              const Desc* __restrict__ descs,
                                              const int64_t* __restrict__ chunk0s,
-                                             int count, int64_t lo,
-                                             int64_t hi) {
+                                             const WaveStart* start, int count,
+                                             int64_t lo, int64_t hi) {
   if (lo >= hi) return;
   st.lo = lo;
   st.hi = hi;
-  const ProbStart ps = find_problem<FUSED>(descs, chunk0s, count, lo);
+  ProbStart ps;
+  if (start) {
+    // scalar loads of the entry (a wave-uniform address)
+    const const_start_ptr e = (const_start_ptr)start;
+    ps.p = e->p;
+    ps.have = true;
+    ps.kc = e->kc;
+    ps.nblk = e->nblk;
+    ps.chunk0 = e->chunk0;
+    ps.w = e->w;
+    ps.x = e->x;
+  } else {
+    ps = find_problem<FUSED>(descs, chunk0s, count, lo);
+  }
   int p = ps.p;
   int64_t pos = lo;
   bool first = ps.have;
@@ -909,7 +925,8 @@ __device__ __forceinline__ void stream_range(Stream<TOK, FUSED>& st,
 template <int TOK, bool FUSED, int WPW>
 __global__ __launch_bounds__(64 * WPW) void stream_kernel(
     const Desc* __restrict__ descs, const int64_t* __restrict__ chunk0s,
-    int count, int64_t total, int32_t* sacc) {
+    const WaveStart* __restrict__ starts, int count, int64_t total,
+    int32_t* sacc) {
   static_assert(WPW == 4 || (WPW == 8 && !FUSED), "workgroup shape");
   // With fewer chunks than waves, only the first `total` waves take part.
   const int64_t W = min((int64_t)gridDim.x * WPW, total);
@@ -926,12 +943,23 @@ __global__ __launch_bounds__(64 * WPW) void stream_kernel(
   st.tail_local = false;
   if (wv < W) {
     // the neighbours share this workgroup only if they take part too
-    st.prev_lo = wv > 0 ? (wv - 1) * total / W : 0;
-    st.next_hi = wv + 1 < W ? (wv + 2) * total / W : total;
     st.prev_in_wg = wave > 0;
     st.next_in_wg = wave < WPW - 1 && wv + 1 < W;
-    stream_range(st, descs, chunk0s, count, wv * total / W,
-                 (wv + 1) * total / W);
+    int64_t lo, hi;
+    if (starts) {  // the plan's entry for this wave (scalar loads)
+      const const_start_ptr e = (const_start_ptr)(starts + wv);
+      lo = e->lo;
+      hi = e->hi;
+      st.prev_lo = e->prev_lo;
+      st.next_hi = e->next_hi;
+    } else {
+      lo = wv * total / W;
+      hi = (wv + 1) * total / W;
+      st.prev_lo = wv > 0 ? (wv - 1) * total / W : 0;
+      st.next_hi = wv + 1 < W ? (wv + 2) * total / W : total;
+    }
+    stream_range(st, descs, chunk0s, starts ? starts + wv : nullptr, count,
+                 lo, hi);
   }
   // Cut blocks shared by two waves of this workgroup only: the wave that
   // holds the block's last chunks leaves its partial sums in its (now
@@ -1193,31 +1221,34 @@ hipError_t launch_chain(const ChainPhase* phases, int nphase, int m,
 // regrouped in half as many.
 template <bool FUSED, int WPW>
 hipError_t launch_stream(const Desc* descs, const int64_t* chunk0,
-                         int32_t count, int64_t total_chunks, int m,
-                         int32_t* sacc, int workgroups, hipStream_t s) {
+                         const WaveStart* starts, int32_t count,
+                         int64_t total_chunks, int m, int32_t* sacc,
+                         int workgroups, hipStream_t s) {
   const dim3 grid((unsigned)((workgroups * 4 + WPW - 1) / WPW)), block(64 * WPW);
   switch (m) {
-    case 1: stream_kernel<1, FUSED, WPW><<<grid, block, 0, s>>>(descs, chunk0, count, total_chunks, sacc); break;
-    case 2: stream_kernel<2, FUSED, WPW><<<grid, block, 0, s>>>(descs, chunk0, count, total_chunks, sacc); break;
-    case 3: stream_kernel<3, FUSED, WPW><<<grid, block, 0, s>>>(descs, chunk0, count, total_chunks, sacc); break;
-    case 4: stream_kernel<4, FUSED, WPW><<<grid, block, 0, s>>>(descs, chunk0, count, total_chunks, sacc); break;
+    case 1: stream_kernel<1, FUSED, WPW><<<grid, block, 0, s>>>(descs, chunk0, starts, count, total_chunks, sacc); break;
+    case 2: stream_kernel<2, FUSED, WPW><<<grid, block, 0, s>>>(descs, chunk0, starts, count, total_chunks, sacc); break;
+    case 3: stream_kernel<3, FUSED, WPW><<<grid, block, 0, s>>>(descs, chunk0, starts, count, total_chunks, sacc); break;
+    case 4: stream_kernel<4, FUSED, WPW><<<grid, block, 0, s>>>(descs, chunk0, starts, count, total_chunks, sacc); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
 hipError_t launch_stream_grouped(const Desc* descs, const int64_t* chunk0,
-                                 int32_t count, int64_t total_chunks, int m,
-                                 int32_t* sacc, int workgroups, bool fused,
-                                 bool full, hipStream_t s) {
+                                 const WaveStart* starts, int32_t count,
+                                 int64_t total_chunks, int m, int32_t* sacc,
+                                 int workgroups, bool fused, bool full,
+                                 hipStream_t s) {
   if (fused)
-    return launch_stream<true, 4>(descs, chunk0, count, total_chunks, m, sacc,
-                                  workgroups, s);
+    return launch_stream<true, 4>(descs, chunk0, starts, count, total_chunks,
+                                  m, sacc, workgroups, s);
   // a full grid runs one workgroup per CU (all of the CU's waves)
   return full ? launch_stream<false, 4 * kStreamWgPerCu>(
-                    descs, chunk0, count, total_chunks, m, sacc, workgroups, s)
-              : launch_stream<false, 4>(descs, chunk0, count, total_chunks, m,
-                                        sacc, workgroups, s);
+                    descs, chunk0, starts, count, total_chunks, m, sacc,
+                    workgroups, s)
+              : launch_stream<false, 4>(descs, chunk0, starts, count,
+                                        total_chunks, m, sacc, workgroups, s);
 }
 
 }  // namespace bt

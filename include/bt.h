@@ -155,7 +155,9 @@ typedef struct bt_problem {
 /* Grouped product: many independent bt_gemm problems in one launch, for a
  * decode step whose projections are each too small to fill the GPU.
  * Use: bytes = bt_grouped_plan_bytes(probs, count); fill a host buffer of that
- * size with bt_grouped_plan (pure host code, no HIP call); copy it to device
+ * size with bt_grouped_plan (host code: it launches nothing and reads no
+ * device memory, and asks the HIP runtime only for the current device's
+ * compute-unit count); copy it to device
  * memory the caller owns (256-byte aligned, writable: every launch writes
  * the plan's scratch area); then call bt_gemm_grouped(plan_dev, plan_host, s)
  * as often as wanted.  The plan holds
@@ -169,6 +171,11 @@ typedef struct bt_problem {
  * stream); rebuild the plan when any pointer, shape or scale changes.
  * plan_host must stay a byte-identical copy of the host image written by
  * bt_grouped_plan (only its header is read by bt_gemm_grouped).
+ * With packed dot products the plan also records where each wave of a
+ * launch on the device that was current when it was built starts streaming
+ * (a table sized by that device's compute units; bytes and image must come
+ * from calls with the same device current).  A launch on a device with
+ * another count gives the same results and finds its starts by a search.
  * Kernel choice: m = 1 streams the weights through packed dot products; so
  * do m = 2 in plans of fewer than 131072 chunks (128 MiB of packed weights)
  * and m = 3, 4 in plans of fewer than 32768 chunks (32 MiB), while larger

@@ -155,7 +155,8 @@ def problems(specs):
 
 
 HDR_FIELDS = ["units", "desc_off", "chunk_off", "unit_off", "sacc_off",
-              "scnt_off", "bytes", "total_chunks", "blocks", "fused"]
+              "scnt_off", "bytes", "total_chunks", "blocks", "fused",
+              "start_off", "start_waves"]
 DESC_BYTES = 128
 
 
@@ -203,9 +204,15 @@ def test_grouped_plan_layout_stream(L):
     assert p["blocks"] == sum(nblk)
     assert p["total_chunks"] == sum(b * c for b, c in zip(nblk, kc))
     assert p["desc_off"] == 256 and nbytes == p["bytes"]
-    for off in ("desc_off", "chunk_off", "unit_off", "sacc_off", "scnt_off",
-                "bytes"):
+    for off in ("desc_off", "chunk_off", "start_off", "unit_off", "sacc_off",
+                "scnt_off", "bytes"):
         assert p[off] % 256 == 0
+    # the start table (one 128-byte entry per wave of a launch on the
+    # current device; none without a device) sits between the first-chunk
+    # offsets and the units
+    assert p["start_off"] >= p["chunk_off"] + 8 * p["count"]
+    assert 0 <= p["start_waves"] <= p["total_chunks"]
+    assert p["unit_off"] >= p["start_off"] + 128 * p["start_waves"]
     # scratch: one 64-bit slot (chunk count, partial total) per row of every
     # row block and token
     assert p["scnt_off"] - p["sacc_off"] >= sum(nblk) * 64 * 8
@@ -237,6 +244,7 @@ def test_grouped_plan_layout_mfma(L):
     assert p["unit"][0].tolist() == [1, 0]
     assert p["unit"][1:].tolist() == [[0, 0], [0, 1], [0, 2]]
     assert p["scnt_off"] == p["sacc_off"]  # no scratch for this kind
+    assert p["start_waves"] == 0  # the tiles need no start table
 
 
 @pytest.mark.parametrize("m", [8, 32, 64])

@@ -539,6 +539,34 @@ def grouped_plan(probs, fused=False):
             else bt.bt_grouped_plan(probs))
 
 
+# Plan header fields (int64 at byte 16 on) and the start-table entry layout.
+HDR = ["units", "desc_off", "chunk_off", "unit_off", "sacc_off", "scnt_off",
+       "bytes", "total_chunks", "blocks", "fused", "start_off", "start_waves"]
+START_BYTES = 128
+
+
+def plan_header(host):
+    vals = host[16:16 + 8 * len(HDR)].view(np.int64)
+    return dict(zip(HDR, (int(v) for v in vals)))
+
+
+def without_start_table(plan):
+    """The same plan with its header's start-table wave count set to 0: the
+    launch then finds every wave's range and first problem by itself."""
+    host = plan.host.copy()
+    host[16 + 8 * HDR.index("start_waves"):][:8].view(np.int64)[0] = 0
+    return bt.GroupedPlan(host, plan.dev, plan._tensors)
+
+
+def expected_waves(total_chunks):
+    """Waves of a streaming launch on this GPU: workgroups of 4 waves, at
+    most 2 per CU, and at least 16 chunks per workgroup; no more waves than
+    chunks."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    wgs = min(cus * 2, (total_chunks + 15) // 16)
+    return min(4 * wgs, total_chunks)
+
+
 @pytest.mark.parametrize("m,layers", [(1, 2), (3, 2), (8, 2), (16, 2),
                                       (32, 2), (40, 1), (64, 1), (130, 1)])
 def test_grouped_layers_match_oracle(m, layers):
@@ -617,8 +645,12 @@ def test_grouped_full_grid_cuts(m):
               np.float32(rng.uniform(0.01, 0.05)))
              for n, k in ((640, 65536), (4096, 256))]
     probs, outs, refs = grouped_problems(cases, m)
-    launch_and_check(bt.bt_grouped_plan(probs), probs, outs, refs,
-                     launches=3)
+    plan = bt.bt_grouped_plan(probs)
+    assert plan_header(plan.host)["start_waves"] > 0
+    launch_and_check(plan, probs, outs, refs, launches=3)
+    # the same plan with the waves finding their starts themselves
+    launch_and_check(without_start_table(plan), probs, outs, refs,
+                     launches=2, label="search")
 
 
 @pytest.mark.parametrize("m,fused", [(1, False), (2, False), (1, True),
@@ -641,8 +673,43 @@ def test_grouped_many_problems(m, fused):
     chunks = sum((t.shape[0] + 63) // 64 * t.shape[1] // 64
                  for t, _, _ in cases)
     assert chunks >= 512 * 16, "the plan must fill every CU"
-    launch_and_check(grouped_plan(probs, fused), probs, outs, refs,
-                     launches=3)
+    plan = grouped_plan(probs, fused)
+    check_start_table(plan, probs, fused)
+    launch_and_check(plan, probs, outs, refs, launches=3)
+    launch_and_check(without_start_table(plan), probs, outs, refs,
+                     launches=2, label="search")
+
+
+def check_start_table(plan, probs, fused):
+    """The plan's start table against the waves' ranges and first problems
+    computed here: wave w of W streams chunks [w T / W, (w + 1) T / W), and
+    its first chunk lies in the last problem whose first chunk is not past
+    it."""
+    h = plan_header(plan.host)
+    T = h["total_chunks"]
+    W = expected_waves(T)
+    assert h["start_waves"] == W
+    assert h["start_off"] % 256 == 0
+    assert h["unit_off"] >= h["start_off"] + W * START_BYTES
+    sizes = [(p["n"] + 63) // 64 * (p["k"] // 64) for p in probs]
+    assert sum(sizes) == T
+    first = np.concatenate([[0], np.cumsum(sizes)[:-1]])
+    tab = plan.host[h["start_off"]:h["start_off"] + W * START_BYTES]
+    tab = tab.reshape(W, START_BYTES)
+    q = tab.view(np.int64)   # 16 int64 per entry
+    d = tab.view(np.int32)   # 32 int32 per entry
+    for w in range(W):
+        lo, hi = w * T // W, (w + 1) * T // W
+        p = int(np.searchsorted(first, lo, side="right")) - 1
+        prob = probs[p]
+        x = prob["x"] if fused else prob["x_q"]
+        assert q[w, 0] == prob["packed"].data_ptr(), w
+        assert q[w, 1] == x.data_ptr(), w
+        assert q[w, 2] == first[p] and (q[w, 3], q[w, 4]) == (lo, hi), w
+        assert d[w, 10] == p and d[w, 11] == prob["k"] // 64, w
+        assert d[w, 12] == (prob["n"] + 63) // 64, w
+        assert q[w, 7] == (0 if w == 0 else (w - 1) * T // W), w
+        assert q[w, 8] == (T if w == W - 1 else (w + 2) * T // W), w
 
 
 @pytest.mark.parametrize("m", [1, 2, 3, 4])
