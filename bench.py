@@ -201,9 +201,30 @@ def capture(torch, fn):
     return g
 
 
+# Untimed run-in before each timed section.  Launches that follow an idle
+# GPU (bench.py packs weights and times the CPU oracle between sections)
+# run slower while the GPU's clocks come up: the M=1 product took 92-96 us
+# 5-10 ms after three idle seconds, 88-89 us at 10-20 ms and 87 us from
+# 20 ms on (per-launch events, 3000 back-to-back launches).  A serving loop
+# runs in the settled state, so every section first runs its own kernels,
+# untimed, for SETTLE_MS of wall time; then its W warmup and K timed steps.
+SETTLE_MS = 100.0
+
+
+def settle(torch, fn, ms=SETTLE_MS):
+    """Call fn back to back, untimed, for about `ms` of wall time."""
+    t0 = time.perf_counter()
+    while (time.perf_counter() - t0) * 1e3 < ms:
+        for _ in range(8):
+            fn()
+        torch.cuda.synchronize()
+
+
 def time_graph(torch, g, reps):
     """Average ms per replay of graph g over `reps` back-to-back replays
-    (HIP events on the current stream, after two untimed replays)."""
+    (HIP events on the current stream, after the run-in and two untimed
+    replays)."""
+    settle(torch, g.replay)
     g.replay()
     g.replay()
     e0 = torch.cuda.Event(enable_timing=True)
@@ -222,7 +243,13 @@ def run_timed(ws: WorkSet, steps: int, warmup: int, torch):
     stream the kernels run on), so that its average matches a kernel trace
     (no gap after the quantization kernels).  Two untimed launches go
     first, so that the stream is busy when the start event is reached and
-    the host's time to submit the first timed launch is not counted."""
+    the host's time to submit the first timed launch is not counted.
+    The run-in (settle) goes before the warmup steps."""
+
+    def step():
+        ws.quant()
+        ws.product()
+    settle(torch, step)
     for _ in range(warmup):
         ws.quant()
         ws.product()
@@ -391,7 +418,8 @@ class ChainSet:
 
 def run_chain(cs: ChainSet, tokens: int, warmup: int, torch):
     """Per-token wall time of the chained decode, eager and graph-replayed
-    (ms)."""
+    (ms), each after the run-in (settle) and `warmup` untimed tokens."""
+    settle(torch, cs.step)
     for _ in range(warmup):
         cs.step()
     torch.cuda.synchronize()
@@ -403,6 +431,7 @@ def run_chain(cs: ChainSet, tokens: int, warmup: int, torch):
     if cs.persistent:  # one cooperative launch per token: no graph
         return eager, eager
     g = cs.capture()
+    settle(torch, g.replay)
     for _ in range(warmup):
         g.replay()
     torch.cuda.synchronize()
@@ -501,6 +530,7 @@ def read_ceiling(torch, bt, nbytes=1 << 30, reps=20):
     buf = torch.ones(nbytes, dtype=torch.uint8, device=dev)
     sink = torch.empty(1 << 16, dtype=torch.int32, device=dev)
     out = {"bytes": nbytes, "sweep": {}}
+    settle(torch, lambda: bt.bt_read_probe(buf, sink, 8, 2))
     for wpc in (4, 8):
         for groups in (1, 2, 3, 4):
             for _ in range(3):
@@ -669,6 +699,7 @@ def main():
                    "layers": work.layers, "projections": len(work.projs),
                    "weight_bytes": ws.weight_bytes(),
                    "launch": args.mode,
+                   "settle_ms": SETTLE_MS,
                    "product_kernel_ms": round(kern_avg, 5),
                    "tokens_per_s_equiv": round(work.m / (ms_step * 1e-3), 1),
                    "tops": round(ws.ops() / (kern_avg * 1e-3) / 1e12, 3)},

@@ -18,6 +18,7 @@ namespace {
 constexpr int kMaxDevices = 64;
 std::atomic<int> g_arch[kMaxDevices];  // 0 unknown, 1 gfx950, 2 other
 std::atomic<int> g_cus[kMaxDevices];   // compute units, 0 = unknown
+std::atomic<int> g_xccs[kMaxDevices];  // XCDs, 0 = unknown
 
 bool aligned(const void* p, uintptr_t a) {
   return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0;
@@ -59,6 +60,22 @@ int cu_count() {
     g_cus[dev].store(cus, std::memory_order_relaxed);
   }
   return cus;
+}
+
+// XCDs (accelerator complex dies) of the current device (cached); 0 on
+// error.
+int xcc_count() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+    return 0;
+  int x = g_xccs[dev].load(std::memory_order_relaxed);
+  if (x == 0) {
+    if (hipDeviceGetAttribute(&x, hipDeviceAttributeNumberOfXccs, dev) !=
+        hipSuccess)
+      return 0;
+    g_xccs[dev].store(x, std::memory_order_relaxed);
+  }
+  return x;
 }
 
 // Checks shared by bt_gemm and the grouped plan.
@@ -505,6 +522,35 @@ int64_t bt_grouped_plan_bytes(const bt_problem* probs, int32_t count) {
   return plan_bytes_of(probs, count, false);
 }
 
+// Range ends of a streaming launch's W waves over T chunks: wave w streams
+// chunks [b[w], b[w + 1]).  Equal ranges (w T / W), except on a full grid of
+// 8-wave workgroups (one per CU), where the shares follow two service rates
+// measured with per-wave timestamps (2B and 8B decode sets at M=1):
+//  - each SIMD runs two waves of a workgroup, j and j + 4, and the older
+//    one's loads go first: with equal ranges waves 4-7 took 9-13 % longer
+//    than waves 0-3, so they take 0.87 of a share;
+//  - workgroup g runs on XCD g mod (XCDs), and with 8 XCDs the odd ones
+//    streamed 7-10 % slower, so their workgroups take 0.9 of a share.
+// The waves then end together instead of the slow ones streaming on alone
+// at a fraction of the bandwidth: 81 against 84.6 us on the 2B set and 262
+// against 275 us on the 8B set (both weights swept over 0.82-0.92).  The
+// outputs do not depend on the split.
+std::vector<int64_t> wave_bounds(int64_t T, int64_t W, bool weighted,
+                                 int xccs) {
+  if (W <= 0) return {};
+  std::vector<int64_t> c(W + 1, 0);
+  for (int64_t w = 0; w < W; ++w) {
+    int64_t wt = 1000;
+    if (weighted && w % 8 >= 4) wt = wt * 87 / 100;
+    if (weighted && xccs == 8 && (w / 8) % 2 == 1) wt = wt * 9 / 10;
+    c[w + 1] = c[w] + wt;
+  }
+  std::vector<int64_t> b(W + 1);
+  for (int64_t w = 0; w <= W; ++w)
+    b[w] = (int64_t)((__int128)c[w] * T / c[W]);
+  return b;
+}
+
 // Builds a grouped plan image; with xf, the problems give fp32 activations
 // (xf[i]) that the launch quantizes itself, after an RMSNorm with gain g[i]
 // and eps[i] when g is given.
@@ -562,14 +608,19 @@ static int32_t build_plan(const bt_problem* probs, int32_t count, void* plan,
         plan_units(probs, count, h.m, h.kind, split);
     memcpy(out + h.unit_off, units.data(), units.size() * sizeof(Unit));
   }
-  // start table: wave w of W streams chunks [w T / W, (w + 1) T / W); its
-  // first chunk lies in the last problem whose first chunk is not past it
+  // start table: contiguous ranges, wave w streaming chunks [b[w], b[w+1]);
+  // its first chunk lies in the last problem whose first chunk is not past
+  // it
   const int64_t W = h.start_waves, T = h.total_chunks;
+  const int cus = W > 0 ? cu_count() : 0;
+  const std::vector<int64_t> b =
+      wave_bounds(T, W, !fused && cus > 0 && W == 8 * (int64_t)cus,
+                  xcc_count());
   int32_t p = 0;
   int64_t p0 = 0;  // first chunk of problem p
   int64_t next0 = (probs[0].n + 63) / 64 * (probs[0].k / 64);
   for (int64_t w = 0; w < W; ++w) {
-    const int64_t lo = w * T / W;
+    const int64_t lo = b[w];
     while (p + 1 < count && next0 <= lo) {
       ++p;
       p0 = next0;
@@ -578,9 +629,9 @@ static int32_t build_plan(const bt_problem* probs, int32_t count, void* plan,
     bt::WaveStart e;
     memset(&e, 0, sizeof(e));
     e.lo = lo;
-    e.hi = (w + 1) * T / W;
-    e.prev_lo = w > 0 ? (w - 1) * T / W : 0;
-    e.next_hi = w + 1 < W ? (w + 2) * T / W : T;
+    e.hi = b[w + 1];
+    e.prev_lo = w > 0 ? b[w - 1] : 0;
+    e.next_hi = w + 1 < W ? b[w + 2] : T;
     e.w = probs[p].packed;
     e.x = xf ? static_cast<const void*>(xf[p])
              : static_cast<const void*>(probs[p].x_q);
