@@ -590,6 +590,215 @@ def cpu_baseline(work: wl.Workload, ps: PackedSet, seconds: float,
                        f"+ product; {timed:.1f} s timed)")
 
 
+def _bin_rates(lo_ns, hi_ns, nbytes, end_ns, bin_ns=250.0):
+    """Aggregate read rate (GB/s, i.e. bytes per ns) in bins of bin_ns, each
+    wave's bytes spread evenly over its [lo, hi) interval."""
+    nb = int(np.ceil(end_ns / bin_ns)) + 1
+    rate = np.zeros(nb)
+    for a, b, by in zip(lo_ns, hi_ns, nbytes):
+        if b <= a:
+            continue
+        r = by / (b - a)
+        i0, i1 = int(a // bin_ns), int(b // bin_ns)
+        for i in range(i0, min(i1, nb - 1) + 1):
+            ov = min(b, (i + 1) * bin_ns) - max(a, i * bin_ns)
+            if ov > 0:
+                rate[i] += r * ov / bin_ns
+    return rate
+
+
+def _phases(lo_ns, hi_ns, nbytes, end_ns, bin_ns=250.0):
+    """Ramp / steady / drain of one launch from its per-wave streaming
+    intervals: the steady rate is the median of the middle half of the
+    window; ramp and drain losses are the time lost against that rate in the
+    first and second half (so that window = bytes / steady + ramp + drain)."""
+    rate = _bin_rates(lo_ns, hi_ns, nbytes, end_ns, bin_ns)
+    n = len(rate)
+    steady = float(np.median(rate[n // 4:3 * n // 4]))
+    loss = np.clip(1.0 - rate / steady, 0.0, None) * bin_ns
+    return {"steady_gb_s": steady,
+            "bytes_over_steady_us": float(np.sum(nbytes)) / steady / 1e3,
+            "ramp_loss_us": float(loss[:n // 2].sum()) / 1e3,
+            "drain_loss_us": float(loss[n // 2:].sum()) / 1e3,
+            "rate_gb_s_per_us": [int(rate[i:i + 4].mean())
+                                 for i in range(0, n, 4)]}
+
+
+def _hw_xcd(hw):
+    return (hw[:, 1] & 0xF).astype(np.int64)
+
+
+def wave_timeline(ws: WorkSet, torch, bt, launches=8):
+    """Per-wave timestamps of the streaming product launch and of the read
+    probe over the same bytes, from the timing build (libbt_timing.so,
+    include/bt_timing.h): where a launch's time goes (start, ramp, steady
+    streaming, drain), per launch and summarized as medians."""
+    import ctypes
+    V = ctypes.c_void_p
+    T = ctypes.CDLL(os.path.join(os.path.dirname(bt.LIB_PATH),
+                                 "libbt_timing.so"))
+    T.bt_gemm_grouped.argtypes = [V, V, V]
+    T.bt_gemm_grouped.restype = ctypes.c_int32
+    T.bt_read_probe.argtypes = [V, ctypes.c_int64, V, ctypes.c_int64,
+                                ctypes.c_int32, ctypes.c_int32, V]
+    T.bt_read_probe.restype = ctypes.c_int32
+    for f in (T.bt_wave_timestamps, T.bt_probe_timestamps):
+        f.argtypes = [V, V]
+        f.restype = ctypes.c_int32
+    host = ws.plan.host
+    hdr = host[16:16 + 8 * 12].view(np.int64)
+    kind = int(host[12:16].view(np.int32)[0])
+    if kind != 0:
+        raise SystemExit("--wave-timestamps needs a streaming plan (m <= 4 "
+                         "with packed dot products)")
+    total, start_off, W = int(hdr[7]), int(hdr[10]), int(hdr[11])
+    if W > 0:  # the plan's own ranges
+        tab = host[start_off:start_off + W * 128].reshape(W, 128)
+        lo_c, hi_c = tab.view(np.int64)[:, 3], tab.view(np.int64)[:, 4]
+    else:
+        cus = torch.cuda.get_device_properties(0).multi_processor_count
+        W = min(4 * min(2 * cus, (total + 15) // 16), total)
+        lo_c = np.arange(W) * total // W
+        hi_c = (np.arange(W) + 1) * total // W
+    wpw = 8 if W == 8 * torch.cuda.get_device_properties(0).multi_processor_count else 4
+    stream = torch.cuda.current_stream().cuda_stream
+    nbytes = ws.product_bytes()
+
+    def launch():
+        rc = T.bt_gemm_grouped(ws.plan.dev.data_ptr(), host.ctypes.data,
+                               stream)
+        if rc != 0:
+            raise RuntimeError(f"timing build: status {rc}")
+    # the timing build computes what the product library does, bit for bit
+    outs = [p["y"] for p in ws.problems]
+    for y in outs:
+        y.fill_(float("nan"))
+    ws.product()
+    torch.cuda.synchronize()
+    ref = torch.cat([y.flatten() for y in outs]).clone()
+    for y in outs:
+        y.fill_(float("nan"))
+    launch()
+    torch.cuda.synchronize()
+    same = bool(torch.equal(ref, torch.cat([y.flatten() for y in outs])))
+
+    def events(fn, reps=20):
+        for _ in range(2):
+            fn()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps * 1e3
+    settle(torch, launch)
+    ev = {"product_library_us": [], "timing_build_us": []}
+    for _ in range(3):
+        ev["product_library_us"].append(round(events(ws.product), 2))
+        ev["timing_build_us"].append(round(events(launch), 2))
+
+    def med(rows, key):
+        return round(float(np.median([r[key] for r in rows])), 2)
+    kern = []
+    for _ in range(launches):
+        launch()
+        launch()
+        launch()
+        torch.cuda.synchronize()
+        ts = np.zeros((4096, 8), np.uint64)
+        hw = np.zeros((4096, 2), np.uint32)
+        if T.bt_wave_timestamps(ts.ctypes.data, hw.ctypes.data) != 0:
+            raise RuntimeError("bt_wave_timestamps failed")
+        ts = ts[:W].astype(np.int64)
+        hw = hw[:W]
+        t = (ts[:, :7] - ts[:, 0].min()) * 10.0  # ns
+        by = (hi_c - lo_c) * 1024.0
+        ph = _phases(t[:, 1], t[:, 3], by, t[:, 6].max())
+        loop = (t[:, 3] - t[:, 1]) / 1e3
+        slot = np.arange(W) % wpw
+        xcd = _hw_xcd(hw)
+        kern.append({
+            "window_us": t[:, 6].max() / 1e3,
+            "last_wave_start_us": t[:, 0].max() / 1e3,
+            "start_us": float(np.median(t[:, 1] - t[:, 0])) / 1e3,
+            "first_data_us": float(np.median(t[:, 2] - t[:, 1])) / 1e3,
+            "loop_end_p10_us": float(np.percentile(t[:, 3], 10)) / 1e3,
+            "loop_end_p50_us": float(np.median(t[:, 3])) / 1e3,
+            "loop_end_max_us": t[:, 3].max() / 1e3,
+            "handoff_us": float(np.median(t[:, 4] - t[:, 3])) / 1e3,
+            "barrier_wait_us": float(np.median(t[:, 5] - t[:, 4])) / 1e3,
+            "steady_gb_s": ph["steady_gb_s"],
+            "bytes_over_steady_us": ph["bytes_over_steady_us"],
+            "ramp_loss_us": ph["ramp_loss_us"],
+            "drain_loss_us": ph["drain_loss_us"],
+            "loop_us_by_slot": [float(loop[slot == j].mean())
+                                for j in range(wpw)],
+            "loop_us_by_xcd": [float(loop[xcd == x].mean()) if (xcd == x).any()
+                               else None for x in range(8)],
+            "rate": ph["rate_gb_s_per_us"]})
+    # the read probe over the same bytes, best of its configurations
+    pbytes = nbytes // 1024 * 1024
+    buf = torch.ones(pbytes, dtype=torch.uint8, device="cuda:0")
+    sink = torch.empty(1 << 16, dtype=torch.int32, device="cuda:0")
+
+    def probe(wpc, g):
+        rc = T.bt_read_probe(buf.data_ptr(), pbytes, sink.data_ptr(),
+                             sink.numel(), wpc, g, stream)
+        if rc != 0:
+            raise RuntimeError(f"read probe: status {rc}")
+    settle(torch, lambda: probe(8, 2))
+    sweep = {(wpc, g): events(lambda wpc=wpc, g=g: probe(wpc, g))
+             for wpc in (4, 8) for g in (1, 2, 3, 4)}
+    best = min(sweep, key=sweep.get)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    PW = cus * best[0]
+    steps = pbytes // 1024
+    plo = np.arange(PW) * steps // PW
+    phi = (np.arange(PW) + 1) * steps // PW
+    prob = []
+    for _ in range(launches):
+        for _ in range(3):
+            probe(*best)
+        torch.cuda.synchronize()
+        ts = np.zeros((4096, 4), np.uint64)
+        hw = np.zeros((4096, 2), np.uint32)
+        if T.bt_probe_timestamps(ts.ctypes.data, hw.ctypes.data) != 0:
+            raise RuntimeError("bt_probe_timestamps failed")
+        ts = ts[:PW].astype(np.int64)
+        t = (ts[:, :3] - ts[:, 0].min()) * 10.0
+        ph = _phases(t[:, 0], t[:, 2], (phi - plo) * 1024.0, t[:, 2].max())
+        prob.append({
+            "window_us": t[:, 2].max() / 1e3,
+            "first_data_us": float(np.median(t[:, 1] - t[:, 0])) / 1e3,
+            "loop_end_p10_us": float(np.percentile(t[:, 2], 10)) / 1e3,
+            "loop_end_p50_us": float(np.median(t[:, 2])) / 1e3,
+            "loop_end_max_us": t[:, 2].max() / 1e3,
+            "steady_gb_s": ph["steady_gb_s"],
+            "bytes_over_steady_us": ph["bytes_over_steady_us"],
+            "ramp_loss_us": ph["ramp_loss_us"],
+            "drain_loss_us": ph["drain_loss_us"]})
+    keys_k = [k for k in kern[0] if not isinstance(kern[0][k], list)]
+    keys_p = list(prob[0])
+    return {
+        "metric": "wave_timeline", "workload": ws.work.name,
+        "bytes_per_launch": nbytes, "waves": W, "waves_per_workgroup": wpw,
+        "launches": launches, "outputs_identical": same,
+        "events_us": ev,
+        "probe_config": {"waves_per_cu": best[0], "groups": best[1],
+                         "events_us": round(sweep[best], 2)},
+        "kernel": {k: med(kern, k) for k in keys_k},
+        "kernel_loop_us_by_slot": [round(float(np.median(
+            [r["loop_us_by_slot"][j] for r in kern])), 2) for j in range(wpw)],
+        "kernel_loop_us_by_xcd": [round(float(np.median(
+            [r["loop_us_by_xcd"][x] for r in kern])), 2)
+            if kern[0]["loop_us_by_xcd"][x] is not None else None
+            for x in range(8)],
+        "kernel_rate_gb_s_per_us_first_launch": kern[0]["rate"],
+        "probe": {k: med(prob, k) for k in keys_p}}
+
+
 def device_info(torch):
     """The GPU the line was measured on (the rooflines assume an MI355X:
     256 CUs at 2.4 GHz)."""
@@ -628,6 +837,10 @@ def main():
     ap.add_argument("--no-8b", action="store_true",
                     help="skip the 8B-shaped set")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--wave-timestamps", action="store_true",
+                    help="instead of the benchmark line, print where a "
+                         "streaming launch's time goes (ramp, steady, drain) "
+                         "from the timing build's per-wave timestamps")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one plain 256 MiB device copy, so that a "
                          "counter run can scale FETCH_SIZE / WRITE_SIZE")
@@ -650,6 +863,16 @@ def main():
     extra = not args.no_extra
     cpu = not args.no_cpu_baseline
 
+    if args.wave_timestamps:
+        if args.mode != "grouped":
+            raise SystemExit("--wave-timestamps times the grouped launch "
+                             "with int8 inputs (--mode grouped)")
+        work = WORKLOADS[args.workload]()
+        ps = PackedSet(work, torch, bt)
+        ws = WorkSet(work, ps, torch, bt, args.mode)
+        ws.quant()
+        print(json.dumps(wave_timeline(ws, torch, bt)), flush=True)
+        return
     ceiling = read_ceiling(torch, bt) if extra else None
     work = WORKLOADS[args.workload]()
     log(f"[bench] workload {work.name}: {len(work.problems())} products, "

@@ -14,6 +14,10 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OBJDIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libbt.so")
+# timing build: the same library with per-wave timestamps in the streaming
+# kernel and the read probe (BT_WAVE_TIMESTAMPS; include/bt_timing.h)
+TIMING_LIB = os.path.join(HERE, "libbt_timing.so")
+TIMED_SOURCES = ("gemv_stream.hip", "probe.hip")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 ARCH = "gfx950"
@@ -35,14 +39,27 @@ def sources():
 
 
 def build(verbose: bool = False) -> str:
-    """Compile every .hip source (in parallel) and link libbt.so."""
+    """Compile every .hip source (in parallel) and link libbt.so, and the
+    timing build libbt_timing.so (the timed sources compiled a second time
+    with BT_WAVE_TIMESTAMPS, linked with the other objects)."""
     os.makedirs(OBJDIR, exist_ok=True)
     procs = []
     objs = []
+    timed_objs = []
+    jobs = []
     for src in sources():
-        obj = os.path.join(OBJDIR, os.path.basename(src)[:-4] + ".o")
+        base = os.path.basename(src)[:-4]
+        obj = os.path.join(OBJDIR, base + ".o")
         objs.append(obj)
-        cmd = [HIPCC, *DEVICE_FLAGS, "-c", src, "-o", obj]
+        jobs.append((src, [HIPCC, *DEVICE_FLAGS, "-c", src, "-o", obj]))
+        if os.path.basename(src) in TIMED_SOURCES:
+            tobj = os.path.join(OBJDIR, "timed_" + base + ".o")
+            timed_objs.append(tobj)
+            jobs.append((src, [HIPCC, *DEVICE_FLAGS, "-DBT_WAVE_TIMESTAMPS",
+                               "-c", src, "-o", tobj]))
+        else:
+            timed_objs.append(obj)
+    for src, cmd in jobs:
         if verbose:
             print(" ".join(cmd), flush=True)
         procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE,
@@ -59,10 +76,11 @@ def build(verbose: bool = False) -> str:
             print(text)
     if failed:
         raise RuntimeError(f"hipcc failed for {failed}")
-    tmp = LIB + ".tmp"
-    subprocess.check_call([HIPCC, f"--offload-arch={ARCH}", "-shared",
-                           "-fPIC", *objs, "-o", tmp])
-    os.replace(tmp, LIB)
+    for lib, lib_objs in ((LIB, objs), (TIMING_LIB, timed_objs)):
+        tmp = lib + ".tmp"
+        subprocess.check_call([HIPCC, f"--offload-arch={ARCH}", "-shared",
+                               "-fPIC", *lib_objs, "-o", tmp])
+        os.replace(tmp, lib)
     return LIB
 
 

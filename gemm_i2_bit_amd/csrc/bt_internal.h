@@ -169,6 +169,11 @@ inline int64_t stream_waves(int64_t total_chunks, int cus) {
   return w < total_chunks ? w : total_chunks;
 }
 
+// Timing build (BT_WAVE_TIMESTAMPS): waves recorded per launch and
+// timestamp slots per wave.
+constexpr int kTimedWaves = 4096;
+constexpr int kTimedSlots = 8;
+
 // Launchers (host code in the kernels' translation units).
 hipError_t launch_pack(const int8_t* t, int64_t n, int64_t k, uint8_t* packed,
                        int32_t* n_invalid, hipStream_t s);

@@ -42,6 +42,26 @@
 #include "bt_internal.h"
 
 namespace bt {
+
+#ifdef BT_WAVE_TIMESTAMPS
+// Timing build only (libbt_timing.so): each wave of a streaming launch
+// writes the chip's 100 MHz real-time counter at fixed points of its work,
+// and its hardware position, for the last launch.  Slots: 0 entry, 1 range
+// and first problem known, 2 first weight group and activation sums
+// arrived, 3 end of the last segment's loop, 4 hand-offs done, 5 after the
+// workgroup barrier, 6 exit, 7 segments streamed.
+__device__ unsigned long long g_wave_ts[kTimedWaves * kTimedSlots];
+__device__ unsigned int g_wave_hw[kTimedWaves * 2];
+__device__ __forceinline__ void wave_stamp(int slot) {
+  const int64_t w = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  const unsigned long long t = __builtin_amdgcn_s_memrealtime();
+  if ((threadIdx.x & 63) == 0 && w < kTimedWaves)
+    g_wave_ts[w * kTimedSlots + slot] = t;
+}
+#define BT_STAMP(slot) wave_stamp(slot)
+#else
+#define BT_STAMP(slot) ((void)0)
+#endif
 namespace {
 
 typedef unsigned v4u __attribute__((ext_vector_type(4)));
@@ -240,6 +260,10 @@ struct Stream {
   // cut blocks shared with a neighbour of this workgroup and no one else:
   // their partial sums meet in LDS after the stream (see stream_kernel)
   bool head_local, tail_local;
+#ifdef BT_WAVE_TIMESTAMPS
+  bool ts_first = true;
+  int ts_segments = 0;
+#endif
   int tail_rb_local;
   int head_keep[TOK], tail_keep[TOK];
   int32_t* sacc;
@@ -743,6 +767,11 @@ struct Stream {
       load_group(ring[i], pg);
     }
     finish_act(pre);
+#ifdef BT_WAVE_TIMESTAMPS
+    if (ts_first) BT_STAMP(2);
+    ts_first = false;
+    ++ts_segments;
+#endif
 #pragma unroll
     for (int t = 0; t < TOK; ++t) sav[t] = sa[t];
     stream_rest(ring, g, pg, s0, s1, head_rb, head_cut, head_sum, a);
@@ -771,6 +800,7 @@ struct Stream {
         }
       }
     }
+    BT_STAMP(3);
     // The staged blocks go first; then both hand-offs are issued, and only
     // then are the atomics' results looked at.  The cut head block's sums
     // were stashed only if it also ended here; otherwise it is the last
@@ -861,6 +891,7 @@ __device__ __forceinline__ void stream_range(Stream<TOK, FUSED>& st,
   } else {
     ps = find_problem<FUSED>(descs, chunk0s, count, lo);
   }
+  BT_STAMP(1);
   int p = ps.p;
   int64_t pos = lo;
   bool first = ps.have;
@@ -905,6 +936,7 @@ __device__ __forceinline__ void stream_range(Stream<TOK, FUSED>& st,
     pos = st.chunk0 + s1;
     ++p;
   }
+  BT_STAMP(4);
 }
 
 // Wave wv of W streams chunks [wv T / W, (wv + 1) T / W) of the T chunks.
@@ -932,6 +964,14 @@ __global__ __launch_bounds__(64 * WPW) void stream_kernel(
   const int64_t W = min((int64_t)gridDim.x * WPW, total);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t wv = (int64_t)blockIdx.x * WPW + wave;
+  BT_STAMP(0);
+#ifdef BT_WAVE_TIMESTAMPS
+  if ((threadIdx.x & 63) == 0 && wv < kTimedWaves) {
+    g_wave_hw[wv * 2] = __builtin_amdgcn_s_getreg((4) | (0 << 6) | (31 << 11));
+    g_wave_hw[wv * 2 + 1] =
+        __builtin_amdgcn_s_getreg((20) | (0 << 6) | (31 << 11));
+  }
+#endif
   Stream<TOK, FUSED> st;
   __shared__ int obuf_all[WPW][16 * 64];
   st.obuf = obuf_all[wave];
@@ -972,12 +1012,18 @@ __global__ __launch_bounds__(64 * WPW) void stream_kernel(
     for (int t = 0; t < TOK; ++t) st.obuf[t * 64 + lane] = st.head_keep[t];
   }
   __syncthreads();
+  BT_STAMP(5);
   if (st.tail_local) {
     const int* other = obuf_all[wave + 1];
 #pragma unroll
     for (int t = 0; t < TOK; ++t)
       st.write_one(st.tail_rb_local, t, st.tail_keep[t] + other[t * 64 + lane]);
   }
+  BT_STAMP(6);
+#ifdef BT_WAVE_TIMESTAMPS
+  if (lane == 0 && wv < kTimedWaves)
+    g_wave_ts[wv * kTimedSlots + 7] = st.ts_segments;
+#endif
 }
 
 // ---------------------------------------------------------------------------
@@ -1252,3 +1298,15 @@ hipError_t launch_stream_grouped(const Desc* descs, const int64_t* chunk0,
 }
 
 }  // namespace bt
+
+#ifdef BT_WAVE_TIMESTAMPS
+extern "C" int32_t bt_wave_timestamps(uint64_t* ts, uint32_t* hw) {
+  if (!ts || !hw) return BT_E_NULL;
+  if (hipMemcpyFromSymbol(ts, HIP_SYMBOL(bt::g_wave_ts),
+                          sizeof(bt::g_wave_ts)) != hipSuccess ||
+      hipMemcpyFromSymbol(hw, HIP_SYMBOL(bt::g_wave_hw),
+                          sizeof(bt::g_wave_hw)) != hipSuccess)
+    return BT_E_HIP;
+  return BT_OK;
+}
+#endif

@@ -10,6 +10,24 @@
 #include "bt_internal.h"
 
 namespace bt {
+#ifdef BT_WAVE_TIMESTAMPS
+// Timing build only: per wave of the last probe launch, the real-time
+// counter at entry (slot 0), when its first load group has arrived (1) and
+// at the end of its loop (2), and its hardware position.
+__device__ unsigned long long g_probe_ts[kTimedWaves * 4];
+__device__ unsigned int g_probe_hw[kTimedWaves * 2];
+__device__ __forceinline__ void probe_stamp(int64_t wv, int slot) {
+  const unsigned long long t = __builtin_amdgcn_s_memrealtime();
+  if ((threadIdx.x & 63) == 0 && wv < kTimedWaves) {
+    g_probe_ts[wv * 4 + slot] = t;
+    if (slot == 0) {
+      g_probe_hw[wv * 2] = __builtin_amdgcn_s_getreg((4) | (0 << 6) | (31 << 11));
+      g_probe_hw[wv * 2 + 1] =
+          __builtin_amdgcn_s_getreg((20) | (0 << 6) | (31 << 11));
+    }
+  }
+}
+#endif
 namespace {
 
 typedef unsigned v4u __attribute__((ext_vector_type(4)));
@@ -50,11 +68,22 @@ __global__ __launch_bounds__(64 * WPW) void read_probe_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t wv = (int64_t)blockIdx.x * WPW + wave;
   const int64_t lo = wv * total / W, hi = (wv + 1) * total / W;
+#ifdef BT_WAVE_TIMESTAMPS
+  probe_stamp(wv, 0);
+#endif
   uint32_t x = 0;
   v4u ring[G][D];
 #pragma unroll
   for (int g = 0; g < G; ++g) load_group(ring[g], buf, lo + g * D,
                                          group_cnt(lo + g * D, hi));
+#ifdef BT_WAVE_TIMESTAMPS
+  {  // the first group's loads have arrived (the wait the first fold makes)
+    constexpr int n = (G - 1) * D;
+    __builtin_amdgcn_s_waitcnt((n & 0xF) | (0x7 << 4) | (0xF << 8) |
+                               ((n >> 4) << 14));
+    probe_stamp(wv, 1);
+  }
+#endif
   for (int64_t pos = lo; pos < hi; pos += G * D) {
 #pragma unroll
     for (int g = 0; g < G; ++g) {
@@ -65,6 +94,9 @@ __global__ __launch_bounds__(64 * WPW) void read_probe_kernel(
       load_group(ring[g], buf, next, group_cnt(next, hi));
     }
   }
+#ifdef BT_WAVE_TIMESTAMPS
+  probe_stamp(wv, 2);
+#endif
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) x ^= __shfl_xor(x, off, 64);
   if ((threadIdx.x & 63) == 0) sink[wv] = x;
@@ -95,3 +127,15 @@ hipError_t launch_read_probe(const void* buf, int64_t bytes, uint32_t* sink,
 }
 
 }  // namespace bt
+
+#ifdef BT_WAVE_TIMESTAMPS
+extern "C" int32_t bt_probe_timestamps(uint64_t* ts, uint32_t* hw) {
+  if (!ts || !hw) return BT_E_NULL;
+  if (hipMemcpyFromSymbol(ts, HIP_SYMBOL(bt::g_probe_ts),
+                          sizeof(bt::g_probe_ts)) != hipSuccess ||
+      hipMemcpyFromSymbol(hw, HIP_SYMBOL(bt::g_probe_hw),
+                          sizeof(bt::g_probe_hw)) != hipSuccess)
+    return BT_E_HIP;
+  return BT_OK;
+}
+#endif

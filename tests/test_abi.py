@@ -19,8 +19,8 @@ HEADER = os.path.join(ROOT, "include", "bt.h")
 P = 0x10000  # a 16-byte aligned fake address; never dereferenced here
 
 
-def declared_functions():
-    text = open(HEADER).read()
+def declared_functions(header=HEADER):
+    text = open(header).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(bt_\w+)\s*\(", text)))
 
@@ -41,6 +41,25 @@ def test_exports_every_declared_symbol(L):
             "bt_gemm_grouped", "bt_grouped_plan"} <= set(names)
     for name in names:
         assert hasattr(L, name), name
+
+
+def test_timing_build_exports(L):
+    """The timing build (per-wave timestamps) exports what bt.h declares
+    and the two calls of bt_timing.h; the product library has neither of
+    the latter."""
+    path = os.path.join(os.path.dirname(bt.LIB_PATH), "libbt_timing.so")
+    assert os.path.exists(path), "libbt_timing.so is built with libbt.so"
+    T = ctypes.CDLL(path)
+    timing = declared_functions(os.path.join(ROOT, "include", "bt_timing.h"))
+    assert timing == ["bt_probe_timestamps", "bt_wave_timestamps"]
+    for name in declared_functions() + timing:
+        assert hasattr(T, name), name
+    for name in timing:
+        assert not hasattr(L, name), name
+        fn = getattr(T, name)
+        fn.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        fn.restype = ctypes.c_int32
+        assert fn(None, None) == bt.BT_E_NULL  # checked before any HIP call
 
 
 def test_status_strings(L):
