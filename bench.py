@@ -14,8 +14,10 @@ one JSON line (rank 0, one GPU).  Unless --no-extra is given the line also
 carries the other configurations: the single small GEMV (latency), batched
 decode at M = 8/16/32 over the same weights, the M=512 prefill layer, the
 8B-shaped set at M = 1 and 64, one launch per product beside the grouped
-launch, the measured streaming-read ceiling, the layer-chained decode and the
-lookup-table comparison.
+launch, the step as one launch that quantizes its own activations
+(fused_step, 2B and 8B sets at M=1), the measured streaming-read ceiling,
+the layer-chained decode and the format comparison.
+--wave-timestamps prints instead where a streaming launch's time goes.
 """
 from __future__ import annotations
 
@@ -270,6 +272,25 @@ def run_timed(ws: WorkSet, steps: int, warmup: int, torch):
     e1.record()
     torch.cuda.synchronize()
     return wall, e0.elapsed_time(e1) / steps
+
+
+def fused_entry(work: wl.Workload, ps: PackedSet, torch, bt, steps, warmup,
+                two_launch_ms):
+    """The same step as one launch that quantizes its own activations
+    (bt_grouped_plan_f32): ms per step beside the two-launch step's, and the
+    fused kernel's rate over its own algorithmic bytes (packed weights, fp32
+    activations, fp32 outputs)."""
+    fws = WorkSet(work, ps, torch, bt, "fused")
+    wall, kern = run_timed(fws, steps, warmup, torch)
+    ms = wall / steps * 1e3
+    out = {"ms_per_step": round(ms, 4),
+           "two_launch_ms_per_step": round(two_launch_ms, 4),
+           "speedup_vs_two_launch": round(two_launch_ms / ms, 4),
+           "kernel_ms": round(kern, 5),
+           "kernel_gb_s": round(fws.product_bytes() / (kern * 1e-3) / 1e9, 1)}
+    del fws
+    torch.cuda.empty_cache()
+    return out
 
 
 def per_launch_ms(ws: WorkSet, torch, reps=10):
@@ -660,7 +681,8 @@ def wave_timeline(ws: WorkSet, torch, bt, launches=8):
         W = min(4 * min(2 * cus, (total + 15) // 16), total)
         lo_c = np.arange(W) * total // W
         hi_c = (np.arange(W) + 1) * total // W
-    wpw = 8 if W == 8 * torch.cuda.get_device_properties(0).multi_processor_count else 4
+    wpw = (8 if ws.mode == "grouped" and W == 8 *
+           torch.cuda.get_device_properties(0).multi_processor_count else 4)
     stream = torch.cuda.current_stream().cuda_stream
     nbytes = ws.product_bytes()
 
@@ -783,6 +805,7 @@ def wave_timeline(ws: WorkSet, torch, bt, launches=8):
     keys_p = list(prob[0])
     return {
         "metric": "wave_timeline", "workload": ws.work.name,
+        "mode": ws.mode,
         "bytes_per_launch": nbytes, "waves": W, "waves_per_workgroup": wpw,
         "launches": launches, "outputs_identical": same,
         "events_us": ev,
@@ -864,9 +887,6 @@ def main():
     cpu = not args.no_cpu_baseline
 
     if args.wave_timestamps:
-        if args.mode != "grouped":
-            raise SystemExit("--wave-timestamps times the grouped launch "
-                             "with int8 inputs (--mode grouped)")
         work = WORKLOADS[args.workload]()
         ps = PackedSet(work, torch, bt)
         ws = WorkSet(work, ps, torch, bt, args.mode)
@@ -936,6 +956,9 @@ def main():
             "gb_s": round(ws.product_bytes() / (pl * 1e-3) / 1e9, 1),
             "frac": round(ws.product_bytes() / (pl * 1e-3) / 1e9
                           / HBM_PEAK_GBS, 4)}
+        if work.m <= 4:
+            out["fused_step"] = fused_entry(work, ps, torch, bt, args.steps,
+                                            args.warmup, ms_step)
     if cpu:
         log("[bench] timing the CPU oracle on a sample")
         cb = cpu_baseline(work, ps, args.cpu_seconds, host_threads())
@@ -1004,6 +1027,10 @@ def main():
                 ws8 = WorkSet(wl.decode_8b(m), ps8, torch, bt)
                 d8[f"m{m}"] = config_entry(ws8, torch, 20, 3, ceiling["gb_s"],
                                            cpu_seconds=cpu_s, ps=ps8)
+                if m == 1:
+                    d8["m1"]["fused_step"] = fused_entry(
+                        wl.decode_8b(1), ps8, torch, bt, 20, 3,
+                        d8["m1"]["ms_per_step"])
                 del ws8
                 torch.cuda.empty_cache()
             out["decode_8b"] = d8

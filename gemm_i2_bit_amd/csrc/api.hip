@@ -522,32 +522,130 @@ int64_t bt_grouped_plan_bytes(const bt_problem* probs, int32_t count) {
   return plan_bytes_of(probs, count, false);
 }
 
-// Range ends of a streaming launch's W waves over T chunks: wave w streams
-// chunks [b[w], b[w + 1]).  Equal ranges (w T / W), except on a full grid of
-// 8-wave workgroups (one per CU), where the shares follow two service rates
-// measured with per-wave timestamps (2B and 8B decode sets at M=1):
-//  - each SIMD runs two waves of a workgroup, j and j + 4, and the older
-//    one's loads go first: with equal ranges waves 4-7 took 9-13 % longer
-//    than waves 0-3, so they take 0.87 of a share;
+// Shares of the waves of a streaming launch (integers, 1000 = one equal
+// share).  Equal, except on a grid that fills the GPU (8 waves per CU),
+// where they follow service rates measured with per-wave timestamps (2B
+// and 8B decode sets at M=1):
+//  - each SIMD runs two waves, and the older one's loads go first.  With
+//    8-wave workgroups (one per CU) those are waves j and j + 4 of the
+//    workgroup: with equal ranges waves 4-7 took 9-13 % longer than waves
+//    0-3, so they take 0.87 of a share.  With 4-wave workgroups (two per
+//    CU, fused plans) the younger waves are those of the workgroups
+//    dispatched second, the upper half of the grid: 0.9 of a share;
 //  - workgroup g runs on XCD g mod (XCDs), and with 8 XCDs the odd ones
-//    streamed 7-10 % slower, so their workgroups take 0.9 of a share.
+//    streamed 7-10 % slower on most boxes, so their workgroups take 0.9 of
+//    a share.
 // The waves then end together instead of the slow ones streaming on alone
 // at a fraction of the bandwidth: 81 against 84.6 us on the 2B set and 262
-// against 275 us on the 8B set (both weights swept over 0.82-0.92).  The
-// outputs do not depend on the split.
-std::vector<int64_t> wave_bounds(int64_t T, int64_t W, bool weighted,
-                                 int xccs) {
-  if (W <= 0) return {};
-  std::vector<int64_t> c(W + 1, 0);
+// against 275 us on the 8B set (both weights swept over 0.82-0.92; fused
+// plans 88.2 against 90.4 us and 269.9 against 276.8 us).  The outputs do
+// not depend on the split.
+std::vector<int64_t> wave_shares(int64_t W, int wpw, bool full, int xccs) {
+  std::vector<int64_t> wt(W, 1000);
+  if (!full) return wt;
   for (int64_t w = 0; w < W; ++w) {
-    int64_t wt = 1000;
-    if (weighted && w % 8 >= 4) wt = wt * 87 / 100;
-    if (weighted && xccs == 8 && (w / 8) % 2 == 1) wt = wt * 9 / 10;
-    c[w + 1] = c[w] + wt;
+    if (wpw == 8 && w % 8 >= 4) wt[w] = wt[w] * 87 / 100;
+    if (wpw == 4 && w >= W / 2) wt[w] = wt[w] * 9 / 10;
+    if (xccs == 8 && (w / wpw) % 2 == 1) wt[w] = wt[w] * 9 / 10;
   }
-  std::vector<int64_t> b(W + 1);
+  return wt;
+}
+
+// Range ends by share: wave w streams chunks [b[w], b[w + 1]), b[w] =
+// floor(T x (shares of waves before w) / (all shares)).
+std::vector<int64_t> bounds_by_share(int64_t T,
+                                     const std::vector<int64_t>& wt) {
+  const int64_t W = (int64_t)wt.size();
+  std::vector<int64_t> c(W + 1, 0), b(W + 1);
+  for (int64_t w = 0; w < W; ++w) c[w + 1] = c[w] + wt[w];
   for (int64_t w = 0; w <= W; ++w)
     b[w] = (int64_t)((__int128)c[w] * T / c[W]);
+  return b;
+}
+
+// Range ends of a launch that quantizes its own activations: every segment
+// (the part of a wave's range inside one problem) starts by quantizing that
+// problem's m rows, so a wave whose range crosses a problem boundary does
+// that work twice.  With ranges by share, those waves finished last (per-
+// wave timestamps: the fused launch's drain was 14 us on the 2B set).
+// Here the ends are placed by cost instead: a chunk costs 10 units and a
+// segment of problem p 4 m (k / 64) units (swept: 0.1 to 1.0 chunk per 64
+// inputs of a row, best at 0.4 on both sets: 2B 84.1-84.6 against 86.8-88.0
+// us, 8B 260.9-263.1 against 269.6-270.4 us; the two-launch step takes
+// 85.2-85.8 and 270.9-271.1 us).  Wave w's range ends where the running cost
+// first reaches C x (shares of waves up to w) / (all shares); a wave moves
+// on to the next problem only if at least half of that problem's
+// quantization fits its share.  C, the total cost, is set by bisection so
+// that the last wave's cost matches its share.  Ranges may come out empty
+// (the wave then does nothing).
+constexpr int64_t kChunkCost = 10;
+constexpr int64_t kQuantCostPer64 = 4;  // per 64 inputs of a token row
+std::vector<int64_t> bounds_by_cost(const bt_problem* probs, int32_t count,
+                                    int64_t T,
+                                    const std::vector<int64_t>& wt) {
+  const int64_t W = (int64_t)wt.size();
+  std::vector<int64_t> ends(count), q(count), qtail(count + 1, 0);
+  int64_t e = 0, qmax = 0;
+  for (int32_t i = 0; i < count; ++i) {
+    e += (probs[i].n + 63) / 64 * (probs[i].k / 64);
+    ends[i] = e;
+    q[i] = kQuantCostPer64 * probs[i].m * (probs[i].k / 64);
+    qmax = std::max(qmax, q[i]);
+  }
+  for (int32_t i = count - 1; i >= 0; --i) qtail[i] = qtail[i + 1] + q[i];
+  std::vector<int64_t> cw(W + 1, 0);
+  for (int64_t w = 0; w < W; ++w) cw[w + 1] = cw[w] + wt[w];
+  std::vector<int64_t> b(W + 1);
+  // places the ends for total cost C; returns the last wave's cost minus
+  // its share
+  auto place = [&](int64_t C) -> int64_t {
+    int64_t pos = 0, A = 0;
+    int32_t p = 0;
+    b[0] = 0;
+    for (int64_t w = 0; w + 1 < W; ++w) {
+      const int64_t target = (int64_t)((__int128)C * cw[w + 1] / cw[W]);
+      if (pos < T) {
+        while (p + 1 < count && ends[p] <= pos) ++p;
+        A += q[p];  // the wave's first segment
+        for (;;) {
+          const int64_t left = ends[p] - pos;
+          if (A + kChunkCost * left <= target && p + 1 < count) {
+            A += kChunkCost * left;
+            pos = ends[p];
+            ++p;
+            if (2 * A + q[p] > 2 * target) break;  // next wave's problem
+            A += q[p];
+          } else {
+            const int64_t room = target - A + kChunkCost / 2;
+            const int64_t step =
+                std::max<int64_t>(0, std::min(left, room / kChunkCost));
+            A += kChunkCost * step;
+            pos += step;
+            break;
+          }
+        }
+      }
+      b[w + 1] = pos;
+    }
+    b[W] = T;
+    int64_t last = 0;
+    if (pos < T) {
+      while (p + 1 < count && ends[p] <= pos) ++p;
+      last = qtail[p] + kChunkCost * (T - pos);
+    }
+    const int64_t share =
+        (int64_t)((__int128)C * (cw[W] - cw[W - 1]) / cw[W]);
+    return last - share;
+  };
+  int64_t lo = 0, hi = kChunkCost * T + W * qmax + kChunkCost;
+  while (lo < hi) {
+    const int64_t mid = lo + (hi - lo) / 2;
+    if (place(mid) > 0)
+      lo = mid + 1;
+    else
+      hi = mid;
+  }
+  place(hi);
   return b;
 }
 
@@ -613,9 +711,15 @@ static int32_t build_plan(const bt_problem* probs, int32_t count, void* plan,
   // it
   const int64_t W = h.start_waves, T = h.total_chunks;
   const int cus = W > 0 ? cu_count() : 0;
-  const std::vector<int64_t> b =
-      wave_bounds(T, W, !fused && cus > 0 && W == 8 * (int64_t)cus,
-                  xcc_count());
+  // a full grid has 8 waves per CU: one 8-wave workgroup per CU, or two
+  // of 4 for fused plans
+  const bool full = cus > 0 && W == 8 * (int64_t)cus;
+  const std::vector<int64_t> wt =
+      wave_shares(W, fused ? 4 : 8, full, xcc_count());
+  const std::vector<int64_t> b = W <= 0 ? std::vector<int64_t>()
+                                 : fused && full
+                                     ? bounds_by_cost(probs, count, T, wt)
+                                     : bounds_by_share(T, wt);
   int32_t p = 0;
   int64_t p0 = 0;  // first chunk of problem p
   int64_t next0 = (probs[0].n + 63) / 64 * (probs[0].k / 64);

@@ -48,8 +48,9 @@ namespace bt {
 // writes the chip's 100 MHz real-time counter at fixed points of its work,
 // and its hardware position, for the last launch.  Slots: 0 entry, 1 range
 // and first problem known, 2 first weight group and activation sums
-// arrived, 3 end of the last segment's loop, 4 hand-offs done, 5 after the
-// workgroup barrier, 6 exit, 7 segments streamed.
+// arrived (fused plans: the first segment's rows quantized), 3 end of the
+// last segment's loop, 4 hand-offs done, 5 after the workgroup barrier, 6
+// exit, 7 segments streamed.
 __device__ unsigned long long g_wave_ts[kTimedWaves * kTimedSlots];
 __device__ unsigned int g_wave_hw[kTimedWaves * 2];
 __device__ __forceinline__ void wave_stamp(int slot) {
@@ -719,6 +720,11 @@ struct Stream {
     ocnt = 0;
     orb0 = sg.head_rb + (sg.head_cut ? 1 : 0);  // first block finished whole
     quantize_rows();
+#ifdef BT_WAVE_TIMESTAMPS
+    if (ts_first) BT_STAMP(2);
+    ts_first = false;
+    ++ts_segments;
+#endif
     stream_rest(sg.ring, sg.g, sg.pg, sg.s0, sg.s1, sg.head_rb, sg.head_cut,
                 head_sum, a);
   }

@@ -21,7 +21,8 @@ extern "C" {
 
 /* Copies the records of the last streaming grouped launch to host memory:
  * ts [BT_TIMED_WAVES][8] uint64, slots 0 wave entry, 1 range and first
- * problem known, 2 first weight group and activation sums arrived, 3 end of
+ * problem known, 2 first weight group and activation sums arrived (plans
+ * that quantize their own activations: the first segment's rows quantized), 3 end of
  * the last segment's loop, 4 hand-offs done, 5 after the workgroup barrier,
  * 6 exit, 7 segments streamed (a count, not a time); hw [BT_TIMED_WAVES][2]
  * uint32, the wave's HW_ID and XCC_ID registers.  Global wave w is wave

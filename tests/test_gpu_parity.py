@@ -5,6 +5,7 @@ oracle's float64 rescale (exactly 0 where the accumulator is 0).
 
 Inputs come from workloads.py (random numbers only).  Expected values come
 only from the oracle."""
+import itertools
 import os
 
 import numpy as np
@@ -680,23 +681,93 @@ def test_grouped_many_problems(m, fused):
                      launches=2, label="search")
 
 
-def expected_bounds(T, W, fused):
-    """Range ends of the waves of a streaming launch on this GPU: equal
-    ranges, except on a full grid of 8-wave workgroups (non-fused plans),
-    where waves 4-7 of each workgroup take 0.87 of a share and, on a GPU of
-    8 XCDs (the 256-CU gfx950 parts), the workgroups of the odd XCDs 0.9."""
+def expected_shares(W, fused):
+    """Shares of the waves of a streaming launch on this GPU (1000 = one
+    equal share): equal, except on a grid of 8 waves per CU, where the
+    younger wave of each SIMD takes less (waves 4-7 of each 8-wave
+    workgroup 0.87 of a share for unfused plans, the upper half of the
+    grid's 4-wave workgroups 0.9 for fused plans) and, on a GPU of 8 XCDs
+    (the 256-CU gfx950 parts), the workgroups of the odd XCDs 0.9."""
     props = torch.cuda.get_device_properties(0)
     cus = props.multi_processor_count
-    weighted = not fused and W == 8 * cus
+    full = W == 8 * cus
     eight_xcds = cus == 256 and props.gcnArchName.startswith("gfx950")
-    wt = np.full(W, 1000, np.int64)
-    w = np.arange(W)
-    if weighted:
-        wt[w % 8 >= 4] = 870
-        if eight_xcds:
-            odd = (w // 8) % 2 == 1
-            wt[odd] = wt[odd] * 9 // 10
-    c = np.concatenate([[0], np.cumsum(wt)])
+    wpw = 4 if fused else 8
+    wt = [1000] * W
+    if full:
+        for w in range(W):
+            if fused and w >= W // 2:
+                wt[w] = wt[w] * 9 // 10
+            if not fused and w % 8 >= 4:
+                wt[w] = wt[w] * 87 // 100
+            if eight_xcds and (w // wpw) % 2 == 1:
+                wt[w] = wt[w] * 9 // 10
+    return wt, full
+
+
+def cost_bounds(sizes, q, T, wt):
+    """Range ends placed by cost (plans that quantize their own
+    activations): a chunk costs 10 and a segment of problem p costs q[p];
+    wave w's range ends where the running cost first reaches C x (shares up
+    to w) / (all shares), moving on to the next problem only if at least
+    half of its quantization fits; C is the least total cost for which the
+    last wave's cost does not exceed its share."""
+    W = len(wt)
+    ends = list(itertools.accumulate(sizes))
+    cw = [0] + list(itertools.accumulate(wt))
+
+    def place(C):
+        b = [0]
+        pos = A = p = 0
+        for w in range(W - 1):
+            target = C * cw[w + 1] // cw[W]
+            if pos < T:
+                while p + 1 < len(sizes) and ends[p] <= pos:
+                    p += 1
+                A += q[p]
+                while True:
+                    left = ends[p] - pos
+                    if A + 10 * left <= target and p + 1 < len(sizes):
+                        A += 10 * left
+                        pos = ends[p]
+                        p += 1
+                        if 2 * A + q[p] > 2 * target:
+                            break
+                        A += q[p]
+                    else:
+                        step = max(0, min(left, (target - A + 5) // 10))
+                        A += 10 * step
+                        pos += step
+                        break
+            b.append(pos)
+        b.append(T)
+        last = 0
+        if pos < T:
+            while p + 1 < len(sizes) and ends[p] <= pos:
+                p += 1
+            last = sum(q[p:]) + 10 * (T - pos)
+        return b, last - C * (cw[W] - cw[W - 1]) // cw[W]
+
+    lo, hi = 0, 10 * T + W * max(q) + 10
+    while lo < hi:
+        mid = (lo + hi) // 2
+        if place(mid)[1] > 0:
+            lo = mid + 1
+        else:
+            hi = mid
+    return np.array(place(hi)[0], np.int64)
+
+
+def expected_bounds(T, W, fused, probs):
+    """Range ends of the waves: by share, or by cost for fused plans on a
+    grid of 8 waves per CU."""
+    wt, full = expected_shares(W, fused)
+    if fused and full:
+        sizes = [(p["n"] + 63) // 64 * (p["k"] // 64) for p in probs]
+        m = probs[0]["x"].shape[0] if probs[0]["x"].dim() == 2 else 1
+        q = [4 * m * (p["k"] // 64) for p in probs]
+        return cost_bounds(sizes, q, T, wt)
+    c = np.concatenate([[0], np.cumsum(np.array(wt, np.int64))])
     return c * T // c[-1]
 
 
@@ -714,7 +785,7 @@ def check_start_table(plan, probs, fused):
     sizes = [(p["n"] + 63) // 64 * (p["k"] // 64) for p in probs]
     assert sum(sizes) == T
     first = np.concatenate([[0], np.cumsum(sizes)[:-1]])
-    b = expected_bounds(T, W, fused)
+    b = expected_bounds(T, W, fused, probs)
     assert b[0] == 0 and b[-1] == T and (np.diff(b) >= 0).all()
     tab = plan.host[h["start_off"]:h["start_off"] + W * START_BYTES]
     tab = tab.reshape(W, START_BYTES)
@@ -722,7 +793,8 @@ def check_start_table(plan, probs, fused):
     d = tab.view(np.int32)   # 32 int32 per entry
     for w in range(W):
         lo, hi = b[w], b[w + 1]
-        p = int(np.searchsorted(first, lo, side="right")) - 1
+        p = min(int(np.searchsorted(first, lo, side="right")) - 1,
+                len(probs) - 1)
         prob = probs[p]
         x = prob["x"] if fused else prob["x_q"]
         assert q[w, 0] == prob["packed"].data_ptr(), w
