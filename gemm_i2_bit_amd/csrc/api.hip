@@ -411,117 +411,6 @@ __global__ __launch_bounds__(256) void zero_kernel(uint4* p, int64_t words) {
     p[i] = make_uint4(0u, 0u, 0u, 0u);
 }
 
-}  // namespace
-
-extern "C" {
-
-const char* bt_status_str(int32_t status) {
-  switch (status) {
-    case BT_OK: return "ok";
-    case BT_E_NULL: return "a required pointer is NULL";
-    case BT_E_SHAPE: return "shape out of range (need k % 64 == 0, 64 <= k <= 65536, n, m >= 1)";
-    case BT_E_ALIGN: return "pointer not aligned as documented";
-    case BT_E_ARG: return "invalid argument (scale, count or plan)";
-    case BT_E_HIP: return "HIP runtime error";
-    case BT_E_ARCH: return "current device is not gfx950";
-    default: return "unknown status";
-  }
-}
-
-int64_t bt_packed_bytes(int64_t n, int64_t k) {
-  if (!n_ok(n) || !k_ok(k)) return BT_E_SHAPE;
-  return (n + 63) / 64 * 64 * (k / 4);
-}
-
-int32_t bt_pack_i2s(const int8_t* t, int64_t n, int64_t k, uint8_t* packed,
-                    int32_t* n_invalid, void* stream) {
-  if (!t || !packed) return BT_E_NULL;
-  if (!n_ok(n) || !k_ok(k)) return BT_E_SHAPE;
-  if (!aligned(t, 16) || !aligned(packed, 16) ||
-      (n_invalid && !aligned(n_invalid, 4)))
-    return BT_E_ALIGN;
-  const int32_t arch = check_arch();
-  if (arch != BT_OK) return arch;
-  return hip_status(bt::launch_pack(t, n, k, packed, n_invalid,
-                                    static_cast<hipStream_t>(stream)));
-}
-
-int32_t bt_quant_act(const float* x, int64_t m, int64_t k, int8_t* x_q,
-                     float* s_a, void* stream) {
-  if (!x || !x_q || !s_a) return BT_E_NULL;
-  if (!m_ok(m) || !k_ok(k)) return BT_E_SHAPE;
-  if (!aligned(x, 16) || !aligned(x_q, 16) || !aligned(s_a, 4))
-    return BT_E_ALIGN;
-  const int32_t arch = check_arch();
-  if (arch != BT_OK) return arch;
-  return hip_status(
-      bt::launch_quant(x, m, k, x_q, s_a, static_cast<hipStream_t>(stream)));
-}
-
-int32_t bt_quant_act_many(const bt_quant_job* jobs, int32_t count,
-                          void* stream) {
-  if (!jobs) return BT_E_NULL;
-  if (count < 1 || count > BT_MAX_QUANT_JOBS) return BT_E_ARG;
-  int64_t rows = 0;
-  for (int32_t j = 0; j < count; ++j) {
-    const bt_quant_job& q = jobs[j];
-    if (!q.x || !q.x_q || !q.s_a) return BT_E_NULL;
-    if (!m_ok(q.m) || !k_ok(q.k)) return BT_E_SHAPE;
-    if (!aligned(q.x, 16) || !aligned(q.x_q, 16) || !aligned(q.s_a, 4))
-      return BT_E_ALIGN;
-    rows += q.m;
-  }
-  if (rows > BT_MAX_M) return BT_E_SHAPE;
-  const int32_t arch = check_arch();
-  if (arch != BT_OK) return arch;
-  return hip_status(
-      bt::launch_quant_many(jobs, count, static_cast<hipStream_t>(stream)));
-}
-
-int32_t bt_gemm(const uint8_t* packed, float s_w, int64_t n, int64_t k,
-                int64_t m, const int8_t* x_q, const float* s_a, float* y,
-                int32_t* acc, void* stream) {
-  const int32_t st = check_problem(packed, s_w, n, k, m, x_q, s_a, y, acc);
-  if (st != BT_OK) return st;
-  const int32_t arch = check_arch();
-  if (arch != BT_OK) return arch;
-  const Desc d = make_desc(packed, s_w, n, k, m, x_q, s_a, y, acc);
-  const hipStream_t s = static_cast<hipStream_t>(stream);
-  if (bt::plan_kind(m) == bt::kKindDot4)
-    return hip_status(bt::launch_dot4(d, s));
-  return hip_status(bt::launch_tiled(d, s));
-}
-
-int32_t bt_gemv(const uint8_t* packed, float s_w, int64_t n, int64_t k,
-                const int8_t* x_q, const float* s_a, float* y, int32_t* acc,
-                void* stream) {
-  return bt_gemm(packed, s_w, n, k, 1, x_q, s_a, y, acc, stream);
-}
-
-int32_t bt_gemv_lut(const uint8_t* packed, float s_w, int64_t n, int64_t k,
-                    const int8_t* x_q, const float* s_a, float* y,
-                    int32_t* acc, void* stream) {
-  const int32_t st = check_problem(packed, s_w, n, k, 1, x_q, s_a, y, acc);
-  if (st != BT_OK) return st;
-  const int32_t arch = check_arch();
-  if (arch != BT_OK) return arch;
-  const Desc d = make_desc(packed, s_w, n, k, 1, x_q, s_a, y, acc);
-  return hip_status(bt::launch_lut(d, static_cast<hipStream_t>(stream)));
-}
-
-// Size of the plan image of a group (fused: the problems give fp32
-// activations), or a negative status.
-static int64_t plan_bytes_of(const bt_problem* probs, int32_t count,
-                             bool fused) {
-  const int32_t st = check_group(probs, count, fused);
-  if (st != BT_OK) return st;
-  return plan_layout(probs, count, fused).bytes;
-}
-
-int64_t bt_grouped_plan_bytes(const bt_problem* probs, int32_t count) {
-  return plan_bytes_of(probs, count, false);
-}
-
 // Shares of the waves of a streaming launch (integers, 1000 = one equal
 // share).  Equal, except on a grid that fills the GPU (8 waves per CU),
 // where they follow service rates measured with per-wave timestamps (2B
@@ -647,6 +536,117 @@ std::vector<int64_t> bounds_by_cost(const bt_problem* probs, int32_t count,
   }
   place(hi);
   return b;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* bt_status_str(int32_t status) {
+  switch (status) {
+    case BT_OK: return "ok";
+    case BT_E_NULL: return "a required pointer is NULL";
+    case BT_E_SHAPE: return "shape out of range (need k % 64 == 0, 64 <= k <= 65536, n, m >= 1)";
+    case BT_E_ALIGN: return "pointer not aligned as documented";
+    case BT_E_ARG: return "invalid argument (scale, count or plan)";
+    case BT_E_HIP: return "HIP runtime error";
+    case BT_E_ARCH: return "current device is not gfx950";
+    default: return "unknown status";
+  }
+}
+
+int64_t bt_packed_bytes(int64_t n, int64_t k) {
+  if (!n_ok(n) || !k_ok(k)) return BT_E_SHAPE;
+  return (n + 63) / 64 * 64 * (k / 4);
+}
+
+int32_t bt_pack_i2s(const int8_t* t, int64_t n, int64_t k, uint8_t* packed,
+                    int32_t* n_invalid, void* stream) {
+  if (!t || !packed) return BT_E_NULL;
+  if (!n_ok(n) || !k_ok(k)) return BT_E_SHAPE;
+  if (!aligned(t, 16) || !aligned(packed, 16) ||
+      (n_invalid && !aligned(n_invalid, 4)))
+    return BT_E_ALIGN;
+  const int32_t arch = check_arch();
+  if (arch != BT_OK) return arch;
+  return hip_status(bt::launch_pack(t, n, k, packed, n_invalid,
+                                    static_cast<hipStream_t>(stream)));
+}
+
+int32_t bt_quant_act(const float* x, int64_t m, int64_t k, int8_t* x_q,
+                     float* s_a, void* stream) {
+  if (!x || !x_q || !s_a) return BT_E_NULL;
+  if (!m_ok(m) || !k_ok(k)) return BT_E_SHAPE;
+  if (!aligned(x, 16) || !aligned(x_q, 16) || !aligned(s_a, 4))
+    return BT_E_ALIGN;
+  const int32_t arch = check_arch();
+  if (arch != BT_OK) return arch;
+  return hip_status(
+      bt::launch_quant(x, m, k, x_q, s_a, static_cast<hipStream_t>(stream)));
+}
+
+int32_t bt_quant_act_many(const bt_quant_job* jobs, int32_t count,
+                          void* stream) {
+  if (!jobs) return BT_E_NULL;
+  if (count < 1 || count > BT_MAX_QUANT_JOBS) return BT_E_ARG;
+  int64_t rows = 0;
+  for (int32_t j = 0; j < count; ++j) {
+    const bt_quant_job& q = jobs[j];
+    if (!q.x || !q.x_q || !q.s_a) return BT_E_NULL;
+    if (!m_ok(q.m) || !k_ok(q.k)) return BT_E_SHAPE;
+    if (!aligned(q.x, 16) || !aligned(q.x_q, 16) || !aligned(q.s_a, 4))
+      return BT_E_ALIGN;
+    rows += q.m;
+  }
+  if (rows > BT_MAX_M) return BT_E_SHAPE;
+  const int32_t arch = check_arch();
+  if (arch != BT_OK) return arch;
+  return hip_status(
+      bt::launch_quant_many(jobs, count, static_cast<hipStream_t>(stream)));
+}
+
+int32_t bt_gemm(const uint8_t* packed, float s_w, int64_t n, int64_t k,
+                int64_t m, const int8_t* x_q, const float* s_a, float* y,
+                int32_t* acc, void* stream) {
+  const int32_t st = check_problem(packed, s_w, n, k, m, x_q, s_a, y, acc);
+  if (st != BT_OK) return st;
+  const int32_t arch = check_arch();
+  if (arch != BT_OK) return arch;
+  const Desc d = make_desc(packed, s_w, n, k, m, x_q, s_a, y, acc);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (bt::plan_kind(m) == bt::kKindDot4)
+    return hip_status(bt::launch_dot4(d, s));
+  return hip_status(bt::launch_tiled(d, s));
+}
+
+int32_t bt_gemv(const uint8_t* packed, float s_w, int64_t n, int64_t k,
+                const int8_t* x_q, const float* s_a, float* y, int32_t* acc,
+                void* stream) {
+  return bt_gemm(packed, s_w, n, k, 1, x_q, s_a, y, acc, stream);
+}
+
+int32_t bt_gemv_lut(const uint8_t* packed, float s_w, int64_t n, int64_t k,
+                    const int8_t* x_q, const float* s_a, float* y,
+                    int32_t* acc, void* stream) {
+  const int32_t st = check_problem(packed, s_w, n, k, 1, x_q, s_a, y, acc);
+  if (st != BT_OK) return st;
+  const int32_t arch = check_arch();
+  if (arch != BT_OK) return arch;
+  const Desc d = make_desc(packed, s_w, n, k, 1, x_q, s_a, y, acc);
+  return hip_status(bt::launch_lut(d, static_cast<hipStream_t>(stream)));
+}
+
+// Size of the plan image of a group (fused: the problems give fp32
+// activations), or a negative status.
+static int64_t plan_bytes_of(const bt_problem* probs, int32_t count,
+                             bool fused) {
+  const int32_t st = check_group(probs, count, fused);
+  if (st != BT_OK) return st;
+  return plan_layout(probs, count, fused).bytes;
+}
+
+int64_t bt_grouped_plan_bytes(const bt_problem* probs, int32_t count) {
+  return plan_bytes_of(probs, count, false);
 }
 
 // Builds a grouped plan image; with xf, the problems give fp32 activations

@@ -422,7 +422,6 @@ __device__ __forceinline__ void store_tile(const Desc& d, const TileState<C>& x,
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
       const int tl0 = 32 * ((i + wave) % NB);  // first token of this tile
-      const int tok = tok0 + tl0 + li;
       const float sa = x.sav[i];
 #pragma unroll
       for (int p = 0; p < 32 / TP; ++p) {
