@@ -325,7 +325,12 @@ def config_entry(ws: WorkSet, torch, steps, warmup, ceiling=None,
     ms_step = wall / steps * 1e3
     prefill = ws.m >= 128
     nbytes = ws.product_bytes()
-    roof = roofline(nbytes, ws.ops(), kern, "mfma" if prefill else "hbm")
+    # counted HBM bytes per launch where profiles/ holds them for this
+    # workload and the current kernel sources
+    traffic = load_profile(f"traffic_{ws.work.name}.json",
+                           kernel_sources_sha(), "hbm_bytes_per_launch")
+    roof = roofline(nbytes, ws.ops(), kern, "mfma" if prefill else "hbm",
+                    traffic)
     if ceiling and not prefill:
         roof["frac_of_measured_ceiling"] = round(
             roof["achieved"] / ceiling, 4)

@@ -510,8 +510,16 @@ def launch_and_check(plan, probs, outs, refs, launches=2, label=""):
             acc = prob["acc"].cpu().numpy()
             y = prob["y"].cpu().numpy()
             for r0, r1, acc_r, y_r in spans:
-                assert np.array_equal(acc[:, r0:r1], acc_r), \
-                    f"{label} launch {launch} problem {i} rows {r0}..{r1}"
+                got = acc[:, r0:r1]
+                if not np.array_equal(got, acc_r):
+                    bad = np.argwhere(got != acc_r)
+                    detail = [(int(t), r0 + int(c), int(acc_r[t, c]),
+                               int(got[t, c])) for t, c in bad[:8]]
+                    raise AssertionError(
+                        f"{label} launch {launch} problem {i} rows {r0}..{r1}:"
+                        f" {len(bad)} of {got.size} accumulators differ"
+                        f" (token, row, expected, got): {detail}; unwritten"
+                        f" (guard fill) {int((got == 0x7EADBEEF).sum())}")
                 check_y(y[:, r0:r1], y_r, acc_r)
         outs.check()
 
