@@ -949,27 +949,28 @@ def decode_2b_distinct():
 
 
 @pytest.mark.parametrize("m,fused", [(1, False), (1, True), (2, False),
-                                     (4, False), (8, False), (16, False),
-                                     (32, False)])
+                                     (2, True), (4, False), (8, False),
+                                     (16, False), (32, False)])
 def test_decode_set_distinct_full_size(decode_2b_distinct, m, fused):
     """The whole 2B-shaped decode set with distinct weights per layer in one
     grouped launch, as the benchmark runs it, three times in a row; every
     output of every launch against the oracle.  M=1 streams with dot
-    products (fused: the launch quantizes the fp32 activations itself); M=2
-    and 4 (sets this large) and the batched decode sizes M=8, 16 and 32 run
-    on the matrix cores."""
+    products (fused: the launch quantizes the fp32 activations itself, with
+    range ends placed by cost, also at M=2); M=2 and 4 (sets this large) and
+    the batched decode sizes M=8, 16 and 32 run on the matrix cores."""
     run_weight_set(decode_2b_distinct, wl.decode_2b(m), fused)
 
 
-@pytest.mark.parametrize("m", [1, 64])
-def test_decode_8b_set_grouped_full_size(m):
+@pytest.mark.parametrize("m,fused", [(1, False), (1, True), (64, False)])
+def test_decode_8b_set_grouped_full_size(m, fused):
     """The 8B-shaped set (32 layers x 7 projections, 1.74 GB of packed
     weights, every layer reusing layer 0's tensors) in one grouped launch:
-    every output at M=1; at M=64 every output of layer 0 and sampled rows of
-    the other layers."""
+    every output at M=1 (also with the launch quantizing its fp32
+    activations); at M=64 every output of layer 0 and sampled rows of the
+    other layers."""
     ws = WeightSet(wl.decode_8b(m), shared=True)
-    run_weight_set(ws, wl.decode_8b(m), full_layers=None if m == 1 else {0},
-                   launches=2)
+    run_weight_set(ws, wl.decode_8b(m), fused,
+                   full_layers=None if m == 1 else {0}, launches=2)
 
 
 @pytest.fixture(scope="module")
