@@ -1012,8 +1012,31 @@ def test_prefill_layer_grouped(prefill_layer):
                           n=t.shape[0], k=t.shape[1], x_q=x_q, s_a=s_a, y=y,
                           acc=acc))
         refs.append([(0, t.shape[0], acc_r, y_r)])
-    launch_and_check(bt.bt_grouped_plan(probs), probs, outs, refs,
-                     launches=3)
+    plan = bt.bt_grouped_plan(probs)
+    check_prefill_order(plan)
+    launch_and_check(plan, probs, outs, refs, launches=3)
+
+
+def check_prefill_order(plan):
+    """A prefill plan with more units than CUs but at most two per CU puts
+    the ranges of split reductions at the end of the first round (the units
+    [cus - ranges, cus)), every other unit in the plain order around them,
+    and lists every unit once."""
+    host = plan.host
+    h = plan_header(host)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    U = h["units"]
+    units = host[h["unit_off"]:h["unit_off"] + 8 * U].view(np.int32)
+    units = units.reshape(U, 2)
+    count = int(host[4:8].view(np.int32)[0])
+    desc = host[h["desc_off"]:h["desc_off"] + 128 * count].reshape(count, 128)
+    nsplit = desc[:, 80:84].copy().view(np.int32)[:, 0]
+    is_range = nsplit[units[:, 0]] > 1
+    n = int(is_range.sum())
+    assert cus < U <= 2 * cus and 0 < n <= cus
+    assert is_range[cus - n:cus].all() and not is_range[:cus - n].any()
+    assert not is_range[cus:].any()
+    assert len({(int(p), int(q)) for p, q in units}) == U
 
 
 # ------------------------------------------------------ read-ceiling probe
