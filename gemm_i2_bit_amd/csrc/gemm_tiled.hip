@@ -279,6 +279,10 @@ __device__ __forceinline__ void issue(TileState<C>& x, int st) {
   for (int r = 0; r < C::kActDma; ++r)
     load_lds16(x.abase, x.abytes, act + x.aq[r] * 1024, x.av[r] + c0 * 64);
   if constexpr (C::kRegW) {
+    // the wait at the top of a stage counts the loads younger than the
+    // stage's activation loads, so the scheduler must not move the weight
+    // loads (plain loads, free to pass the direct-to-LDS ones) above them
+    __builtin_amdgcn_sched_barrier(0);
     const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<void*>(x.wbase), 0, x.wbytes, kRsrcFlags);
     // streamed once: non-temporal
@@ -295,11 +299,22 @@ __device__ __forceinline__ void issue(TileState<C>& x, int st) {
   }
 }
 
+// Loads younger than the activation loads of the stage in slot S, at its
+// wait.  In the last, partial pass around the ring every stage issued is past
+// the end: its weight loads into registers are never read, so the compiler
+// drops them, and stage S finds S * kWLoads fewer younger loads than a full
+// pass has (the count is exact then, and stricter than needed if they stay).
+template <class C, int S, bool Last>
+constexpr int younger() {
+  return Last && C::kRegW ? C::kYounger - S * C::kWLoads : C::kYounger;
+}
+
 // Stage st from slot S; stage st + NS - 1 goes into slot S - 1 (mod NS),
 // whose previous stage every wave finished before the barrier.
-template <class C, int S>
+template <class C, int S, bool Last>
 __device__ __forceinline__ void run_stage(TileState<C>& x, int st) {
-  __builtin_amdgcn_s_waitcnt(waitcnt_vm(C::kYounger));
+  static_assert(younger<C, S, Last>() >= 0, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(younger<C, S, Last>()));
   __builtin_amdgcn_s_barrier();
   issue<C, (S + C::NS - 1) % C::NS>(x, st + C::NS - 1);
   // keep register-bound weight loads at the top of the stage: the scheduler
@@ -315,18 +330,19 @@ __device__ __forceinline__ void run_stage(TileState<C>& x, int st) {
                      st < x.nfull ? 0x01010101 : 0, x.acc, x.tsum_part);
 }
 
-// Slots S .. NS-1 of one pass around the ring, starting at stage st0; with
-// `bounded`, only the stages below nst.
-template <class C, int S>
-__device__ __forceinline__ void ring_pass(TileState<C>& x, int st0,
-                                          bool bounded, int nst) {
+// Slots S .. NS-1 of one pass around the ring, starting at stage st0; the
+// Last (partial) pass runs only the stages below nst.
+template <class C, int S, bool Last>
+__device__ __forceinline__ void ring_pass(TileState<C>& x, int st0, int nst) {
   if constexpr (S < C::NS) {
-    if (!bounded || st0 + S < nst) run_stage<C, S>(x, st0 + S);
-    ring_pass<C, S + 1>(x, st0, bounded, nst);
+    if (!Last || st0 + S < nst) run_stage<C, S, Last>(x, st0 + S);
+    ring_pass<C, S + 1, Last>(x, st0, nst);
   }
 }
 
-// Loads of stages S .. NS-2 into their slots.
+// Loads of stages S .. NS-2 into their slots.  The scheduler may mix a
+// stage's weight loads with the next stage's loads: that only adds loads
+// younger than a stage's activation loads, so the waits stay sufficient.
 template <class C, int S>
 __device__ __forceinline__ void prologue(TileState<C>& x) {
   if constexpr (S < C::NS - 1) {
@@ -595,8 +611,8 @@ __device__ __forceinline__ void run_tile(const Desc& d, int rt, int tt,
   // so exactly NS-2 stages are younger than the one awaited.
   prologue<C, 0>(x);
   int st = 0;
-  for (; st + C::NS <= nst; st += C::NS) ring_pass<C, 0>(x, st, false, nst);
-  ring_pass<C, 0>(x, st, true, nst);
+  for (; st + C::NS <= nst; st += C::NS) ring_pass<C, 0, false>(x, st, nst);
+  ring_pass<C, 0, true>(x, st, nst);
   // drain the loads issued past the end before LDS is reused
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
 
@@ -625,7 +641,13 @@ __device__ __forceinline__ void run_tile(const Desc& d, int rt, int tt,
 template <class C>
 __global__ __launch_bounds__(256, 2) void tiled_kernel(Desc d, int ntt) {
   const int u = blockIdx.x;
-  run_tile<C>(d, u / ntt, u % ntt, 0, 0, d.k >> 6, nullptr, nullptr);
+  // the division runs on the vector unit: copied to SGPRs (the compiler
+  // drops a readfirstlane of a value it knows is uniform), the buffer
+  // descriptors built from the tile indices need no per-lane loop
+  int rt, tt;
+  asm("s_mov_b32 %0, %1" : "=s"(rt) : "s"(u / ntt));
+  asm("s_mov_b32 %0, %1" : "=s"(tt) : "s"(u % ntt));
+  run_tile<C>(d, rt, tt, 0, 0, d.k >> 6, nullptr, nullptr);
 }
 
 // Unit sub-index: (256-row tile * ntt + token tile) * nsplit + range; a

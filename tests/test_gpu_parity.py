@@ -973,6 +973,58 @@ def test_decode_8b_set_grouped_full_size(m, fused):
                    full_layers=None if m == 1 else {0}, launches=2)
 
 
+@pytest.mark.parametrize("which,m", [("8b", 64), ("2b", 64), ("2b", 48),
+                                     ("2b", 32)])
+def test_skinny_launches_repeat(decode_2b_distinct, which, m):
+    """The matrix-core decode plans launched 40 times in a row: every launch
+    writes the same bits as the first to every output.  The tiles count
+    their outstanding loads to know when a ring slot has arrived; a load
+    the count misses races with the reads of the slot, and a race shows up
+    as launches that differ.  Covers token tiles of 32 and 64 (48: a ragged
+    tile), reductions of 20, 32, 54 and 112 stages (54: the ring's last pass
+    is partial) and split reductions."""
+    if which == "8b":
+        ws = WeightSet(wl.decode_8b(m), shared=True)
+        work = wl.decode_8b(m)
+    else:
+        ws, work = decode_2b_distinct, wl.decode_2b(m)
+    plist = work.problems()
+    outs = OutSet([(m, p.n) for p in plist])
+    probs = []
+    for i, p in enumerate(plist):
+        key = ws.key(p)
+        y, acc = outs.out(i)
+        x_q, s_a = bt.bt_quant_act(dev(work.activations(p.layer, p.proj)))
+        probs.append(dict(packed=ws.gpu[key], s_w=ws.s_w[key], n=p.n, k=p.k,
+                          x_q=x_q, s_a=s_a, y=y, acc=acc))
+    plan = bt.bt_grouped_plan(probs)
+    bt.bt_gemm_grouped(plan)
+    torch.cuda.synchronize()
+    first_acc = outs.acc.buf.clone()
+    first_y = outs.y.buf.view(torch.int32).clone()
+    assert not bool((first_acc[torch.from_numpy(outs.acc.mask).cuda()]
+                     == 0x7EADBEEF).any()), "an output was not written"
+    for launch in range(1, 40):
+        outs.reset()
+        bt.bt_gemm_grouped(plan)
+        torch.cuda.synchronize()
+        same_acc = torch.equal(outs.acc.buf, first_acc)
+        same_y = torch.equal(outs.y.buf.view(torch.int32), first_y)
+        if not (same_acc and same_y):
+            base = outs.acc.buf.data_ptr()
+            where = []
+            for i, v in enumerate(outs.acc.views):
+                o = (v.data_ptr() - base) // 4
+                bad = int((v != first_acc[o:o + v.numel()]).sum())
+                if bad:
+                    where.append((i, bad))
+            raise AssertionError(
+                f"{work.name} launch {launch} differs from launch 0 (acc "
+                f"equal {same_acc}, y equal {same_y}); (problem, elements): "
+                f"{where[:8]}")
+    outs.check()
+
+
 @pytest.fixture(scope="module")
 def prefill_layer():
     """The M=512 prefill layer: host inputs and the oracle's outputs of all
