@@ -353,8 +353,11 @@ __device__ __forceinline__ void prologue(TileState<C>& x) {
 
 // Direct stores of the wave's final sums (no staging): lane (h, i) writes
 // its token's rows as four 16-byte pieces per register set.  Used for
-// 32-token tiles holding at most 16 tokens, where the staging passes cost
-// more than the scattered pieces.
+// 32-token tiles holding at most kDirectTokens tokens: over the 2B-shaped
+// decode set the two ways tie at 5 to 7 tokens, direct stores are ahead
+// below that (90.0 against 93.4 us at 4), and the staged whole segments
+// from 8 tokens on (95.5 against 99.2 us at 8, 102.6 against 108.5 at 16).
+constexpr int kDirectTokens = 6;
 template <class C>
 __device__ __forceinline__ void store_direct(const Desc& d,
                                              const TileState<C>& x,
@@ -424,7 +427,7 @@ __device__ __forceinline__ void store_tile(const Desc& d, const TileState<C>& x,
   constexpr int NB = C::NB;
   constexpr int TP = Staging<C>::TP;
   if constexpr (NB == 1) {
-    if (d.m - tok0 <= 16) {  // few tokens in this tile: store directly
+    if (d.m - tok0 <= kDirectTokens) {  // few tokens: store directly
       store_direct<C>(d, x, fin, blk, tok0);
       return;
     }
