@@ -46,7 +46,8 @@ static_assert(sizeof(Desc) == 128, "Desc is 128 bytes");
 
 // One work unit of a grouped launch: problem index and a sub-index whose
 // meaning depends on the kernel: for the matrix-core kinds,
-// (256-row tile * ntt + token tile) * nsplit + reduction range.  Problem -1
+// (row tile * ntt + token tile) * nsplit + reduction range (row tiles of
+// tile_rows(token tile) rows).  Problem -1
 // marks padding that keeps an XCD-ordered unit list aligned.
 struct Unit {
   int32_t prob;
@@ -141,12 +142,16 @@ inline int group_kind(int64_t m, int64_t total_chunks, bool fused) {
 }
 // tokens per workgroup tile of the matrix-core kernels
 inline int token_tile(int64_t m) { return m <= 32 ? 32 : (m <= 64 ? 64 : 128); }
-// work units (256-row x token-tile workgroups) of one problem for the
+// weight rows per workgroup tile for a token tile: 64-token tiles give each
+// of the 4 waves two 64-row blocks, the others one
+constexpr int tile_rows(int token_tile) { return token_tile == 64 ? 512 : 256; }
+// work units (tile_rows x token-tile workgroups) of one problem for the
 // matrix-core kinds, before any split of the reduction
 inline int64_t kind_units(int kind, int64_t n, int64_t m) {
   if (kind == kKindDot4) return 0;
   const int bm = token_tile(m);
-  return (n + 255) / 256 * ((m + bm - 1) / bm);
+  const int rows = tile_rows(bm);
+  return (n + rows - 1) / rows * ((m + bm - 1) / bm);
 }
 // int32 entries of one split-reduction scratch region (64 rows x token tile)
 inline int64_t split_region_ints(int64_t m) { return 64 * token_tile(m); }

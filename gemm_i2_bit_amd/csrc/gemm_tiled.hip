@@ -66,13 +66,19 @@ constexpr int kWSlot = BLK * CPS * 1024;  // 8 KiB
 // Buffer resource word 3 for raw (untyped, unswizzled) gfx9 buffer loads.
 constexpr int kRsrcFlags = 0x00020000;
 
-template <int BM_, int NS_, bool RegW_>
+template <int BM_, int NS_, bool RegW_, int BPW_ = 1>
 struct Cfg {
   static constexpr int BM = BM_;       // tokens per workgroup tile
   static constexpr int NB = BM / 32;   // 32-token MFMA tiles per wave
   static constexpr int NS = NS_;       // LDS ring slots
   // weight words go from memory straight to registers (else through LDS)
   static constexpr bool kRegW = RegW_;
+  // 64-row blocks per wave: the workgroup tile covers kRows weight rows, and
+  // each activation byte brought into LDS serves BPW blocks of every wave
+  static constexpr int BPW = BPW_;
+  static constexpr int kRows = 64 * BLK * BPW;
+  static_assert(BPW == 1 || kRegW, "several blocks per wave: weights in "
+                                   "registers");
   // activation slot, rounded up to whole 1 KiB loads
   static constexpr int kActSlot = (BM * kRow + 1023) / 1024 * 1024;
   // direct loads filling one activation slot, 64 granules each, spread over
@@ -81,7 +87,7 @@ struct Cfg {
   static constexpr int kActDma = (kActLoads + BLK - 1) / BLK;
   // memory instructions per wave per stage, in issue order: activation
   // loads, then weight loads (into LDS, or into registers)
-  static constexpr int kWLoads = kRegW ? 2 : CPS;
+  static constexpr int kWLoads = kRegW ? 2 * BPW : CPS;
   static constexpr int kPerStage = kActDma + kWLoads;
   // at the start of a stage, the loads younger than its activation loads:
   // its own weight loads when they go to registers (the compiler waits for
@@ -91,8 +97,12 @@ struct Cfg {
   static_assert(kYounger < 64, "vmcnt range");
 };
 using CfgS32 = Cfg<32, 4, true>;
-using CfgS64 = Cfg<64, 4, true>;
+using CfgS64 = Cfg<64, 4, true, 2>;
 using CfgP128 = Cfg<128, 3, false>;
+// the plans count work units with the same tile heights
+static_assert(CfgS32::kRows == tile_rows(32) && CfgS64::kRows == tile_rows(64) &&
+                  CfgP128::kRows == tile_rows(128),
+              "tile rows of the plans");
 
 // s_waitcnt immediate: vmcnt(v) and lgkmcnt(0); expcnt not waited on
 constexpr int waitcnt_vm(int v) {
@@ -217,16 +227,18 @@ __device__ __forceinline__ void compute_stage(const int8_t* act,
   }
 }
 
-// One stage with weight words in registers: lane (h, i) holds the 16-byte
-// chunk 2 p + h of rows i and 32 + i (w[0], w[1]); word s gives the A
-// operands of step s, inputs 64 h + 16 s + [0, 16) of the stage.  `ones` is
-// 0 for lanes whose chunk lies past the row (odd kc), else 0x01010101.
+// One stage with weight words in registers: for each of the wave's blocks
+// lane (h, i) holds the 16-byte chunk 2 p + h of rows i and 32 + i (w[.][0],
+// w[.][1]); word s gives the A operands of step s, inputs 64 h + 16 s +
+// [0, 16) of the stage, and one B operand read from LDS serves every block.
+// `ones` is 0 for lanes whose chunk lies past the row (odd kc), else
+// 0x01010101.
 template <class C>
 __device__ __forceinline__ void compute_stage_reg(const int8_t* act,
-                                                  const v4i (&w)[2],
+                                                  const v4i (&w)[C::BPW][2],
                                                   const int (&bread)[C::NB],
                                                   int ones,
-                                                  v16i (&acc)[2][C::NB],
+                                                  v16i (&acc)[C::BPW][2][C::NB],
                                                   int& tsum_part) {
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
@@ -234,14 +246,17 @@ __device__ __forceinline__ void compute_stage_reg(const int8_t* act,
 #pragma unroll
     for (int i = 0; i < C::NB; ++i)
       b[i] = *reinterpret_cast<const v4i*>(act + bread[i] + 16 * s);
-    const v4i a0 = expand((uint32_t)w[0][s]);
-    const v4i a1 = expand((uint32_t)w[1][s]);
 #pragma unroll
-    for (int i = 0; i < C::NB; ++i) {
-      acc[0][i] =
-          __builtin_amdgcn_mfma_i32_32x32x32_i8(a0, b[i], acc[0][i], 0, 0, 0);
-      acc[1][i] =
-          __builtin_amdgcn_mfma_i32_32x32x32_i8(a1, b[i], acc[1][i], 0, 0, 0);
+    for (int bb = 0; bb < C::BPW; ++bb) {
+      const v4i a0 = expand((uint32_t)w[bb][0][s]);
+      const v4i a1 = expand((uint32_t)w[bb][1][s]);
+#pragma unroll
+      for (int i = 0; i < C::NB; ++i) {
+        acc[bb][0][i] = __builtin_amdgcn_mfma_i32_32x32x32_i8(
+            a0, b[i], acc[bb][0][i], 0, 0, 0);
+        acc[bb][1][i] = __builtin_amdgcn_mfma_i32_32x32x32_i8(
+            a1, b[i], acc[bb][1][i], 0, 0, 0);
+      }
     }
     tsum_part = sdot4(b[0].x, ones, tsum_part);
     tsum_part = sdot4(b[0].y, ones, tsum_part);
@@ -253,8 +268,8 @@ __device__ __forceinline__ void compute_stage_reg(const int8_t* act,
 // Per-wave state of one workgroup tile.
 template <class C>
 struct TileState {
-  const void* wbase;  // the wave's weight block
-  int wbytes;
+  const void* wbase[C::BPW];  // the wave's weight blocks
+  int wbytes[C::BPW];
   const void* abase;  // the tile's activation rows
   int abytes;
   int av[C::kActDma];         // per-lane source offsets of the activation loads
@@ -263,8 +278,8 @@ struct TileState {
   int wread;                  // LDS offset (or source offset) of the A words
   int wave, lane, h, nfull;
   int c_begin;  // first chunk of the tile's reduction range
-  v4i wreg[C::kRegW ? C::NS : 1][2];  // register ring of weight words
-  v16i acc[2][C::NB];
+  v4i wreg[C::kRegW ? C::NS : 1][C::BPW][2];  // register ring of weights
+  v16i acc[C::BPW][2][C::NB];
   int tsum_part;
   float sav[C::NB];  // activation scale of the lane's token in each tile
 };
@@ -283,18 +298,21 @@ __device__ __forceinline__ void issue(TileState<C>& x, int st) {
     // stage's activation loads, so the scheduler must not move the weight
     // loads (plain loads, free to pass the direct-to-LDS ones) above them
     __builtin_amdgcn_sched_barrier(0);
-    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<void*>(x.wbase), 0, x.wbytes, kRsrcFlags);
-    // streamed once: non-temporal
 #pragma unroll
-    for (int r2 = 0; r2 < 2; ++r2)
-      x.wreg[S][r2] = __builtin_amdgcn_raw_buffer_load_b128(
-          r, x.wread + c0 * 1024 + r2 * 512, 0, 2);
+    for (int b = 0; b < C::BPW; ++b) {
+      const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<void*>(x.wbase[b]), 0, x.wbytes[b], kRsrcFlags);
+      // streamed once: non-temporal
+#pragma unroll
+      for (int r2 = 0; r2 < 2; ++r2)
+        x.wreg[S][b][r2] = __builtin_amdgcn_raw_buffer_load_b128(
+            r, x.wread + c0 * 1024 + r2 * 512, 0, 2);
+    }
   } else {
     int8_t* wts = wts_slot<C, S>();
 #pragma unroll
     for (int j = 0; j < CPS; ++j)
-      load_lds16(x.wbase, x.wbytes, wts + (x.wave * CPS + j) * 1024,
+      load_lds16(x.wbase[0], x.wbytes[0], wts + (x.wave * CPS + j) * 1024,
                  x.lane * 16 + (c0 + j) * 1024);
   }
 }
@@ -327,7 +345,7 @@ __device__ __forceinline__ void run_stage(TileState<C>& x, int st) {
                          x.tsum_part);
   else
     compute_stage<C>(act_slot<C, S>(), wts_slot<C, S>(), x.bread, x.wread,
-                     st < x.nfull ? 0x01010101 : 0, x.acc, x.tsum_part);
+                     st < x.nfull ? 0x01010101 : 0, x.acc[0], x.tsum_part);
 }
 
 // Slots S .. NS-1 of one pass around the ring, starting at stage st0; the
@@ -535,7 +553,7 @@ __device__ __forceinline__ void combine_split(const Desc& d, TileState<C>& x,
   }
 }
 
-// One workgroup tile: weight rows [256 rt, 256 rt + 256) x tokens
+// One workgroup tile: weight rows [kRows rt, kRows rt + kRows) x tokens
 // [BM tt, BM tt + BM), reduction over chunks [c_begin, c_end) (range ks of
 // the problem's split).
 template <class C>
@@ -556,12 +574,17 @@ __device__ __forceinline__ void run_tile(const Desc& d, int rt, int tt,
   const int nst = (nc + CPS - 1) / CPS;
   x.nfull = nc / CPS;  // full stages; an odd count (last range) adds one
   x.c_begin = c_begin;
-  const int blk = rt * BLK + wave;
-  const bool blk_ok = blk < d.nblk;  // wave-uniform
+  const int blk0 = (rt * BLK + wave) * C::BPW;  // the wave's first block
+  const bool blk_ok = blk0 < d.nblk;            // wave-uniform
 
-  // weight loads: the wave's block, 1 KiB per chunk, lane = 16-byte row piece
-  x.wbase = d.w + (size_t)(blk_ok ? blk : 0) * 16 * (size_t)k;
-  x.wbytes = blk_ok ? 16 * k : 0;
+  // weight loads: each of the wave's blocks, 1 KiB per chunk, lane = 16-byte
+  // row piece; a block past the problem's rows reads as zero
+#pragma unroll
+  for (int b = 0; b < C::BPW; ++b) {
+    const bool ok = blk0 + b < d.nblk;
+    x.wbase[b] = d.w + (size_t)(ok ? blk0 + b : 0) * 16 * (size_t)k;
+    x.wbytes[b] = ok ? 16 * k : 0;
+  }
   // activation loads: load q fills slot granules 64 q + lane, granule g of
   // the slot being byte 16 (g % 9) of token g / 9 (the ninth is padding and
   // gets a copy of the eighth; granules past the tile's tokens are out of
@@ -596,9 +619,11 @@ __device__ __forceinline__ void run_tile(const Desc& d, int rt, int tt,
     x.wread = wave * CPS * 1024 + li * 16 + 8 * h;
   }
 #pragma unroll
-  for (int r2 = 0; r2 < 2; ++r2)
+  for (int b = 0; b < C::BPW; ++b)
 #pragma unroll
-    for (int i = 0; i < NB; ++i) x.acc[r2][i] = v16i{0};
+    for (int r2 = 0; r2 < 2; ++r2)
+#pragma unroll
+      for (int i = 0; i < NB; ++i) x.acc[b][r2][i] = v16i{0};
   x.tsum_part = 0;
   // the epilogue's activation scales, requested now so that the end of the
   // tile does not wait for them (older than every load of the ring, so the
@@ -626,19 +651,27 @@ __device__ __forceinline__ void run_tile(const Desc& d, int rt, int tt,
   __syncthreads();
 
   if (!blk_ok) return;
-  // sums net of the activation sums, in place
+  int qs[NB];
 #pragma unroll
-  for (int i = 0; i < NB; ++i) {
-    const int qs = tsum[32 * ((i + wave) % NB) + li];
+  for (int i = 0; i < NB; ++i) qs[i] = tsum[32 * ((i + wave) % NB) + li];
+  // every block unrolled with its own accumulators (a loop with an exit
+  // would index them at run time and put them in scratch)
 #pragma unroll
-    for (int r2 = 0; r2 < 2; ++r2)
+  for (int b = 0; b < C::BPW; ++b) {
+    if (blk0 + b < d.nblk) {  // wave-uniform
+      // sums net of the activation sums, in place
 #pragma unroll
-      for (int g = 0; g < 16; ++g) x.acc[r2][i][g] -= qs;
+      for (int i = 0; i < NB; ++i)
+#pragma unroll
+        for (int r2 = 0; r2 < 2; ++r2)
+#pragma unroll
+          for (int g = 0; g < 16; ++g) x.acc[b][r2][i][g] -= qs[i];
+      if (d.nsplit > 1)
+        combine_split<C>(d, x, x.acc[b], blk0 + b, tt, ks, tok0, sacc, scnt);
+      else
+        store_tile<C>(d, x, x.acc[b], blk0 + b, tok0);
+    }
   }
-  if (d.nsplit > 1)
-    combine_split<C>(d, x, x.acc, blk, tt, ks, tok0, sacc, scnt);
-  else
-    store_tile<C>(d, x, x.acc, blk, tok0);
 }
 
 template <class C>
@@ -653,8 +686,8 @@ __global__ __launch_bounds__(256, 2) void tiled_kernel(Desc d, int ntt) {
   run_tile<C>(d, rt, tt, 0, 0, d.k >> 6, nullptr, nullptr);
 }
 
-// Unit sub-index: (256-row tile * ntt + token tile) * nsplit + range; a
-// unit of problem -1 is padding and does nothing.
+// Unit sub-index: (row tile * ntt + token tile) * nsplit + range, row tiles
+// of C::kRows rows; a unit of problem -1 is padding and does nothing.
 template <class C>
 __global__ __launch_bounds__(256, 2) void tiled_grouped_kernel(
     const Desc* __restrict__ descs, const Unit* __restrict__ units,
@@ -673,7 +706,7 @@ __global__ __launch_bounds__(256, 2) void tiled_grouped_kernel(
 template <class C>
 hipError_t launch_one(const Desc& d, hipStream_t s) {
   const int ntt = (d.m + C::BM - 1) / C::BM;
-  const int64_t units = (int64_t)((d.n + 255) / 256) * ntt;
+  const int64_t units = (int64_t)((d.n + C::kRows - 1) / C::kRows) * ntt;
   tiled_kernel<C><<<dim3((unsigned)units), dim3(256), 0, s>>>(d, ntt);
   return hipGetLastError();
 }

@@ -250,6 +250,12 @@ def test_grouped_plan_layout_stream(L):
         assert d["s_w"] == np.float32(0.25)
 
 
+def tile_rows(m):
+    """Weight rows per matrix-core workgroup tile: 512 for the 64-token
+    tiles (m = 33..64), else 256."""
+    return 512 if 32 < m <= 64 else 256
+
+
 def test_grouped_plan_layout_mfma(L):
     specs = [(640, 2560, 40), (96, 6912, 40)]
     arr = problems(specs)
@@ -257,11 +263,12 @@ def test_grouped_plan_layout_mfma(L):
     img = np.zeros(nbytes, np.uint8)
     assert L.bt_grouped_plan(arr, 2, img.ctypes.data, nbytes) == 0
     p = parse_plan(img)
-    # 256-row tiles, one 64-token tile
-    assert p["kind"] == 1 and p["units"] == 3 + 1
+    # one 64-token tile; its workgroups cover 512 rows (two 64-row blocks
+    # per wave): 640 rows in 2 tiles, 96 rows in 1
+    assert p["kind"] == 1 and p["units"] == 2 + 1
     # largest reduction length first
     assert p["unit"][0].tolist() == [1, 0]
-    assert p["unit"][1:].tolist() == [[0, 0], [0, 1], [0, 2]]
+    assert p["unit"][1:].tolist() == [[0, 0], [0, 1]]
     assert p["scnt_off"] == p["sacc_off"]  # no scratch for this kind
     assert p["start_waves"] == 0  # the tiles need no start table
 
@@ -283,7 +290,8 @@ def test_grouped_plan_xcd_order(L, m):
     p = parse_plan(img)
     assert p["kind"] == 1 and p["units"] % 8 == 0
     u = p["unit"]
-    tiles = [(n + 255) // 256 for n, _, _ in specs]
+    rows = tile_rows(m)
+    tiles = [(n + rows - 1) // rows for n, _, _ in specs]
     real = [tuple(x) for x in u.tolist() if x[0] >= 0]
     assert sorted(real) == sorted((i, t) for i, n in enumerate(tiles)
                                   for t in range(n))
