@@ -351,6 +351,13 @@ def config_entry(ws: WorkSet, torch, steps, warmup, ceiling=None,
             "frac": round((ws.ops() / (pl * 1e-3) / 1e12 / INT8_PEAK_TOPS)
                           if prefill else
                           (nbytes / (pl * 1e-3) / 1e9 / HBM_PEAK_GBS), 4)}
+    # matrix-core and vector-ALU busy fractions where profiles/ holds
+    # counters for this workload and the current kernel sources
+    for key in ("mfma_busy", "valu_busy"):
+        v = load_profile(f"counters_{ws.work.name}.json",
+                         kernel_sources_sha(), key)
+        if v is not None:
+            e[key] = v
     if cpu_seconds > 0 and ps is not None:
         e["cpu_baseline"] = cpu_baseline(ws.work, ps, cpu_seconds,
                                          host_threads())

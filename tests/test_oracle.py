@@ -131,16 +131,19 @@ def test_pack_single_plus_one_golden(orc):
 
 
 def test_pack_chunk_and_block_placement(orc):
-    # 16-byte chunk c of row r sits at (r // 64) * 16 k + c * 1024 + (r % 64)
-    # * 16: set one +1 at (r, 64 c) and find the only changed byte.
+    # single +1 entries of a 130 x 192 matrix: the one changed byte of the
+    # packed image and its value, worked out by hand (golden file)
+    _, rows = read_golden("pack_placement.txt")
+    assert len(rows) >= 8
     n, k = 130, 192
-    for r, c in [(0, 0), (1, 0), (63, 2), (64, 0), (65, 1), (129, 2)]:
+    for r, kk, off, val in rows:
         t = np.zeros((n, k), np.int8)
-        t[r, 64 * c] = 1
+        t[int(r), int(kk)] = 1
         p, _ = orc.pack_i2s(t)
+        assert p.shape == (3 * 16 * k,)
         changed = np.flatnonzero(p != 0x55)
-        assert changed.tolist() == [(r // 64) * 16 * k + c * 1024 + (r % 64) * 16]
-        assert p[changed[0]] == 0x56
+        assert changed.tolist() == [int(off)], (r, kk)
+        assert p[changed[0]] == int(val, 16), (r, kk)
 
 
 def test_pack_round_trip_all_81_bytes(orc):
