@@ -1057,7 +1057,13 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         out["calibration_copy_bytes"] = n
-        del src, dst
+        # a second reference for the read counter: the read probe reads the
+        # same 256 MiB once
+        sink = torch.empty(1 << 16, dtype=torch.int32, device="cuda:0")
+        bt.bt_read_probe(src, sink, 8, 2)
+        torch.cuda.synchronize()
+        out["calibration_read_probe_bytes"] = n
+        del src, dst, sink
 
     print(json.dumps(out), flush=True)
 
