@@ -334,6 +334,15 @@ def config_entry(ws: WorkSet, torch, steps, warmup, ceiling=None,
     if ceiling and not prefill:
         roof["frac_of_measured_ceiling"] = round(
             roof["achieved"] / ceiling, 4)
+    if not prefill:
+        # the same against a probe that writes the launch's share of output
+        # bytes between its reads
+        wbytes = sum(4 * ws.m * p["n"] for p in ws.problems)
+        mixed, shape = mixed_ceiling(torch, ws.bt, wbytes / (nbytes - wbytes))
+        roof["write_share"] = round(wbytes / nbytes, 4)
+        roof["measured_mixed_ceiling_gb_s"] = mixed
+        roof["mixed_ceiling_best"] = shape
+        roof["frac_of_mixed_ceiling"] = round(roof["achieved"] / mixed, 4)
     e = {"workload": ws.work.name, "m": ws.m,
          "ms_per_step": round(ms_step, 4),
          "product_kernel_ms": round(kern, 5),
@@ -583,6 +592,40 @@ def read_ceiling(torch, bt, nbytes=1 << 30, reps=20):
     out["best"] = best
     del buf, sink
     return out
+
+
+def mixed_ceiling(torch, bt, write_frac, nbytes=1 << 30, reps=20):
+    """The rate of a stream that writes `write_frac` of its bytes:
+    bt_mix_probe reading 1 GiB once and writing write_frac of that once
+    (1 KiB pieces spread through the reads in bursts of 1, 8 or 32),
+    back-to-back launches timed with HIP events; GB/s of bytes read plus
+    written, the best (and its shape) over 4 and 8 waves per compute unit
+    with 2 load groups in flight and the three burst sizes."""
+    dev = torch.device("cuda:0")
+    buf = torch.ones(nbytes, dtype=torch.uint8, device=dev)
+    out_bytes = int(nbytes * write_frac) // 1024 * 1024
+    out = torch.empty(max(out_bytes, 1024), dtype=torch.uint8,
+                      device=dev)[:out_bytes]
+    sink = torch.empty(1 << 16, dtype=torch.int32, device=dev)
+    settle(torch, lambda: bt.bt_mix_probe(buf, out, sink, 8, 2, 8))
+    best, shape = 0.0, None
+    for wpc in (4, 8):
+        for burst in (1, 8, 32):
+            for _ in range(3):
+                bt.bt_mix_probe(buf, out, sink, wpc, 2, burst)
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                bt.bt_mix_probe(buf, out, sink, wpc, 2, burst)
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / reps
+            gbs = (nbytes + out_bytes) / (ms * 1e-3) / 1e9
+            if gbs > best:
+                best, shape = gbs, f"{wpc}w_2g_burst{burst}"
+    del buf, out, sink
+    return round(best, 1), shape
 
 
 def cpu_baseline(work: wl.Workload, ps: PackedSet, seconds: float,

@@ -5,7 +5,7 @@ library's HIP kernels.  PyTorch supplies device memory and streams.
 Functions carry the C ABI's names (see include/bt.h for the contract):
 bt_pack_i2s, bt_quant_act, bt_quant_act_many, bt_gemv, bt_gemm,
 bt_grouped_plan, bt_grouped_plan_f32, bt_gemm_grouped, bt_packed_bytes,
-bt_status_str, and the measurement helper bt_read_probe.
+bt_status_str, and the measurement helpers bt_read_probe and bt_mix_probe.
 """
 from __future__ import annotations
 
@@ -127,6 +127,8 @@ def lib() -> ctypes.CDLL:
         L.bt_gemm_grouped_static.restype = i32
         L.bt_read_probe.argtypes = [p, i64, p, i64, i32, i32, p]
         L.bt_read_probe.restype = i32
+        L.bt_mix_probe.argtypes = [p, i64, p, i64, i32, p, i64, i32, i32, p]
+        L.bt_mix_probe.restype = i32
         _lib = L
     return _lib
 
@@ -508,6 +510,21 @@ def bt_read_probe(buf, sink, waves_per_cu: int = 8, groups: int = 2,
                                _dev(sink, torch.int32, "sink"), sink.numel(),
                                int(waves_per_cu), int(groups),
                                _stream(stream)), "bt_read_probe")
+
+
+def bt_mix_probe(buf, out, sink, waves_per_cu: int = 8, groups: int = 2,
+                 burst: int = 1, stream=None):
+    """Stream-read a uint8 GPU buffer once while writing the uint8 GPU
+    buffer `out` once in bursts of `burst` 1 KiB pieces (the mixed
+    read/write probe; out.numel() <= buf.numel(), both multiples of 1024);
+    sink as for bt_read_probe."""
+    torch = _torch()
+    _check(lib().bt_mix_probe(_dev(buf, torch.uint8, "buf"), buf.numel(),
+                              _dev(out, torch.uint8, "out"), out.numel(),
+                              int(burst),
+                              _dev(sink, torch.int32, "sink"), sink.numel(),
+                              int(waves_per_cu), int(groups),
+                              _stream(stream)), "bt_mix_probe")
 
 
 class ChainPlan:

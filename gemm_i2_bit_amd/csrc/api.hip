@@ -1041,4 +1041,28 @@ int32_t bt_read_probe(const void* buf, int64_t bytes, uint32_t* sink,
                                           static_cast<hipStream_t>(stream)));
 }
 
+int32_t bt_mix_probe(const void* buf, int64_t bytes, void* out,
+                     int64_t out_bytes, int32_t burst, uint32_t* sink,
+                     int64_t sink_words, int32_t waves_per_cu, int32_t groups,
+                     void* stream) {
+  if (!buf || !sink || (!out && out_bytes != 0)) return BT_E_NULL;
+  if (bytes < 1024 || bytes % 1024 != 0 || out_bytes < 0 ||
+      out_bytes % 1024 != 0 || out_bytes > bytes)
+    return BT_E_SHAPE;
+  if (!aligned(buf, 16) || !aligned(out, 16) || !aligned(sink, 4))
+    return BT_E_ALIGN;
+  if ((waves_per_cu != 4 && waves_per_cu != 8) || groups < 1 || groups > 4 ||
+      burst < 1 || burst > 64)
+    return BT_E_ARG;
+  const int32_t arch = check_arch();
+  if (arch != BT_OK) return arch;
+  const int cus = cu_count();
+  if (cus <= 0) return BT_E_HIP;
+  const int64_t waves = (int64_t)cus * waves_per_cu;
+  if (sink_words < waves) return BT_E_SHAPE;
+  return hip_status(bt::launch_mix_probe(
+      buf, bytes, out, out_bytes, burst, sink, (int)waves, waves_per_cu,
+      groups, static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

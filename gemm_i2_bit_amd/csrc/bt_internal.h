@@ -255,6 +255,9 @@ hipError_t launch_pack_b3(const int8_t* t, int64_t n, int64_t k,
 hipError_t launch_b3(const Desc& d, hipStream_t s);  // m = 1 only
 hipError_t launch_read_probe(const void* buf, int64_t bytes, uint32_t* sink,
                              int waves, int wpw, int groups, hipStream_t s);
+hipError_t launch_mix_probe(const void* buf, int64_t bytes, void* out,
+                            int64_t out_bytes, int burst, uint32_t* sink,
+                            int waves, int wpw, int groups, hipStream_t s);
 // RMSNorm before the quantization.  A row's sum of squares is taken by one
 // wave, in one fixed order, by every kernel that normalizes: lane l adds the
 // squares of float4 i = l, l + 64, l + 128, ... in increasing i (x, y, z, w

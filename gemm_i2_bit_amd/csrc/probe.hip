@@ -102,6 +102,73 @@ __global__ __launch_bounds__(64 * WPW) void read_probe_kernel(
   if ((threadIdx.x & 63) == 0) sink[wv] = x;
 }
 
+// The read probe with a write stream mixed in: wave w also writes its share
+// [w P / W, (w + 1) P / W) of the P 1 KiB pieces of `out`, spread evenly
+// through its reads in bursts of `burst` pieces (before a load group, once
+// that many pieces are due), with non-temporal 128-bit stores, each piece
+// filled with its own index.  Timing it gives the rate of a stream that
+// writes a given fraction of its bytes, as a skinny matrix product writes
+// its outputs between its weight reads (a tile's outputs in one burst).
+template <int WPW, int G>
+__global__ __launch_bounds__(64 * WPW) void mix_probe_kernel(
+    const uint8_t* __restrict__ buf, int64_t total, uint32_t* __restrict__ out,
+    int64_t pieces, int burst, uint32_t* sink) {
+  const int64_t W = (int64_t)gridDim.x * WPW;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t wv = (int64_t)blockIdx.x * WPW + wave;
+  const int64_t lo = wv * total / W, hi = (wv + 1) * total / W;
+  const int64_t wlo = wv * pieces / W, whi = (wv + 1) * pieces / W;
+  const int lane = threadIdx.x & 63;
+  int64_t wnext = wlo;
+  typedef __attribute__((address_space(1))) v4u* gv4u_ptr;
+  typedef __attribute__((address_space(1))) uint32_t* gu32_ptr;
+  uint32_t x = 0;
+  v4u ring[G][D];
+#pragma unroll
+  for (int g = 0; g < G; ++g) load_group(ring[g], buf, lo + g * D,
+                                         group_cnt(lo + g * D, hi));
+  for (int64_t pos = lo; pos < hi; pos += G * D) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      x ^= fold(ring[g]);
+      const int64_t next = pos + (g + G) * D;
+      load_group(ring[g], buf, next, group_cnt(next, hi));
+      // pieces due once steps [lo, pos + (g + 1) D) are read
+      const int64_t done = min(pos + (g + 1) * D, hi) - lo;
+      const int64_t due = wlo + (whi - wlo) * done / (hi - lo);
+      if (due - wnext < burst) continue;
+      for (; wnext < due; ++wnext) {
+        const uint32_t v = (uint32_t)wnext;
+        __builtin_nontemporal_store(
+            v4u{v, v, v, v},
+            reinterpret_cast<gv4u_ptr>((gu32_ptr)(out + wnext * 256 + lane * 4)));
+      }
+    }
+  }
+  for (; wnext < whi; ++wnext) {
+    const uint32_t v = (uint32_t)wnext;
+    __builtin_nontemporal_store(
+        v4u{v, v, v, v},
+        reinterpret_cast<gv4u_ptr>((gu32_ptr)(out + wnext * 256 + lane * 4)));
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) x ^= __shfl_xor(x, off, 64);
+  if (lane == 0) sink[wv] = x;
+}
+
+template <int WPW>
+void launch_mix_wpw(const uint8_t* b, int64_t steps, uint32_t* out,
+                    int64_t pieces, int burst, uint32_t* sink, int waves,
+                    int groups, hipStream_t s) {
+  const dim3 grid((unsigned)(waves / WPW)), block(64 * WPW);
+  switch (groups) {
+    case 1: mix_probe_kernel<WPW, 1><<<grid, block, 0, s>>>(b, steps, out, pieces, burst, sink); break;
+    case 2: mix_probe_kernel<WPW, 2><<<grid, block, 0, s>>>(b, steps, out, pieces, burst, sink); break;
+    case 3: mix_probe_kernel<WPW, 3><<<grid, block, 0, s>>>(b, steps, out, pieces, burst, sink); break;
+    default: mix_probe_kernel<WPW, 4><<<grid, block, 0, s>>>(b, steps, out, pieces, burst, sink); break;
+  }
+}
+
 template <int WPW>
 void launch_wpw(const uint8_t* b, int64_t steps, uint32_t* sink, int waves,
                 int groups, hipStream_t s) {
@@ -123,6 +190,20 @@ hipError_t launch_read_probe(const void* buf, int64_t bytes, uint32_t* sink,
     launch_wpw<8>(b, bytes / 1024, sink, waves, groups, s);
   else
     launch_wpw<4>(b, bytes / 1024, sink, waves, groups, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_mix_probe(const void* buf, int64_t bytes, void* out,
+                            int64_t out_bytes, int burst, uint32_t* sink,
+                            int waves, int wpw, int groups, hipStream_t s) {
+  const uint8_t* b = static_cast<const uint8_t*>(buf);
+  uint32_t* o = static_cast<uint32_t*>(out);
+  if (wpw == 8)
+    launch_mix_wpw<8>(b, bytes / 1024, o, out_bytes / 1024, burst, sink,
+                      waves, groups, s);
+  else
+    launch_mix_wpw<4>(b, bytes / 1024, o, out_bytes / 1024, burst, sink,
+                      waves, groups, s);
   return hipGetLastError();
 }
 

@@ -281,6 +281,26 @@ int32_t bt_read_probe(const void* buf, int64_t bytes, uint32_t* sink,
                       int64_t sink_words, int32_t waves_per_cu,
                       int32_t groups, void* stream);
 
+/* Measurement helper, not part of the product path: bt_read_probe with a
+ * write stream mixed in.  Besides reading `bytes` at buf once as
+ * bt_read_probe does, the waves write out_bytes at out once, in 1 KiB
+ * pieces with non-temporal 128-bit stores, each wave its contiguous share,
+ * spread evenly through its reads in bursts of `burst` consecutive pieces
+ * (the rest at the end of the wave's reads); every 32-bit word of piece i
+ * (bytes [1024 i, 1024 i + 1024) of out) receives the value i.  Timing it
+ * gives the rate of a memory stream that writes a given fraction of its
+ * bytes, as a skinny matrix product writes its outputs between its weight
+ * reads.
+ *  buf, sink, waves_per_cu, groups  as in bt_read_probe.
+ *  out        device, 16-byte aligned (may be NULL when out_bytes is 0);
+ *             out_bytes % 1024 == 0 and 0 <= out_bytes <= bytes, else
+ *             BT_E_SHAPE.
+ *  burst      1 to 64, else BT_E_ARG. */
+int32_t bt_mix_probe(const void* buf, int64_t bytes, void* out,
+                     int64_t out_bytes, int32_t burst, uint32_t* sink,
+                     int64_t sink_words, int32_t waves_per_cu, int32_t groups,
+                     void* stream);
+
 /* RMSNorm in front of the activation quantization: RMS normalization is one
  * of the GPU kernels of a ternary model's decode step ("1bit-systems：在AMD
  * Strix Halo上实现纯Rust本地三值权重LLM推理", section "技术架构：Rust在上，HIP

@@ -484,6 +484,28 @@ def test_read_probe_argument_errors(L):
         assert g(P, 1024, P, 4096, 4, groups, None) == bt.BT_E_ARG, groups
 
 
+def test_mix_probe_argument_errors(L):
+    g = L.bt_mix_probe
+    assert g(None, 1024, P, 1024, 1, P, 4096, 8, 2, None) == bt.BT_E_NULL
+    assert g(P, 1024, None, 1024, 1, P, 4096, 8, 2, None) == bt.BT_E_NULL
+    assert g(P, 1024, P, 1024, 1, None, 4096, 8, 2, None) == bt.BT_E_NULL
+    # no output pointer is needed for no writes (checks pass up to the device)
+    assert g(P, 1024, None, 0, 1, P, 4096, 0, 2, None) == bt.BT_E_ARG
+    for nbytes, obytes in [(0, 0), (512, 0), (1024 + 16, 1024), (1024, 512),
+                           (1024, -1024), (1024, 2048)]:
+        assert g(P, nbytes, P, obytes, 1, P, 4096, 8, 2,
+                 None) == bt.BT_E_SHAPE, (nbytes, obytes)
+    assert g(P + 8, 1024, P, 1024, 1, P, 4096, 8, 2, None) == bt.BT_E_ALIGN
+    assert g(P, 1024, P + 8, 1024, 1, P, 4096, 8, 2, None) == bt.BT_E_ALIGN
+    assert g(P, 1024, P, 1024, 1, P + 2, 4096, 8, 2, None) == bt.BT_E_ALIGN
+    for wpc in (0, 3, 16):
+        assert g(P, 1024, P, 0, 1, P, 4096, wpc, 2, None) == bt.BT_E_ARG, wpc
+    for groups in (0, 5):
+        assert g(P, 1024, P, 0, 1, P, 4096, 4, groups, None) == bt.BT_E_ARG
+    for burst in (0, -1, 65):
+        assert g(P, 1024, P, 0, burst, P, 4096, 4, 2, None) == bt.BT_E_ARG
+
+
 def test_b3_sizes_and_argument_errors(L):
     assert L.bt_b3_packed_bytes(64, 80 * 4) == 64 * 4 * 16
     assert L.bt_b3_packed_bytes(70, 64) == 128 * 16      # 64 inputs -> 80

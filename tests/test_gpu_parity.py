@@ -1109,6 +1109,37 @@ def test_read_probe_reads_every_word_once():
             assert got == np.bitwise_xor.reduce(words), (wpc, groups)
 
 
+def test_mix_probe_reads_and_writes_every_word_once():
+    """The mixed read/write probe: reads every word of its buffer once (XOR
+    of the per-wave results) and writes every 1 KiB piece of its output
+    once with the piece's index, for shares that do not divide evenly among
+    the waves, including no writes and as many bytes written as read, in
+    bursts of 1 to 64 pieces."""
+    rng = np.random.default_rng(115)
+    words = rng.integers(0, 1 << 32, size=(3 * 1024 * 1024 + 37 * 256),
+                         dtype=np.uint32)
+    buf = dev(words.view(np.uint8))
+    nbytes = words.size * 4
+    for frac in (0.0, 0.16, 1.0):
+        pieces = int(nbytes * frac) // 1024
+        for wpc, groups, burst in ((4, 2, 1), (8, 4, 1), (8, 1, 8),
+                                   (4, 3, 64)):
+            print(f"mix probe: {pieces} pieces, {wpc} waves/CU, {groups} "
+                  f"groups, bursts of {burst}", flush=True)
+            out = torch.full((pieces * 256 + 256,), -1, dtype=torch.int32,
+                             device="cuda:0")
+            sink = torch.zeros(1 << 16, dtype=torch.int32, device="cuda:0")
+            bt.bt_mix_probe(buf, out[:pieces * 256].view(torch.uint8), sink,
+                            wpc, groups, burst)
+            torch.cuda.synchronize()
+            got = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32))
+            assert got == np.bitwise_xor.reduce(words), (frac, wpc, groups)
+            o = out.cpu().numpy()
+            want = np.repeat(np.arange(pieces, dtype=np.int32), 256)
+            np.testing.assert_array_equal(o[:pieces * 256], want)
+            assert (o[pieces * 256:] == -1).all()  # guard past the end
+
+
 # ------------------------------------------------------- layer-chained decode
 def oracle_chain(work, layers, norm=False):
     """The chained decode on the CPU: every phase quantizes its input (O3;
