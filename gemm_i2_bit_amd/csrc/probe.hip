@@ -104,9 +104,9 @@ __global__ __launch_bounds__(64 * WPW) void read_probe_kernel(
 
 // The read probe with a write stream mixed in: wave w also writes its share
 // [w P / W, (w + 1) P / W) of the P 1 KiB pieces of `out`, spread evenly
-// through its reads in bursts of `burst` pieces (before a load group, once
-// that many pieces are due), with non-temporal 128-bit stores, each piece
-// filled with its own index.  Timing it gives the rate of a stream that
+// through its reads in bursts of `burst` pieces (after a load group is
+// issued, once that many pieces are due; the rest after its last reads),
+// with non-temporal 128-bit stores, each piece filled with its own index.  Timing it gives the rate of a stream that
 // writes a given fraction of its bytes, as a skinny matrix product writes
 // its outputs between its weight reads (a tile's outputs in one burst).
 template <int WPW, int G>
