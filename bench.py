@@ -704,6 +704,62 @@ def _hw_xcd(hw):
     return (hw[:, 1] & 0xF).astype(np.int64)
 
 
+def calibrate_xcd_shares(ws: WorkSet, torch, bt, rounds=2, launches=4):
+    """Per-XCD shares for a streaming plan on a full grid, measured on this
+    GPU: the plan is launched through the timing build (libbt_timing.so,
+    include/bt_timing.h), each XCD's mean wave loop time is read from the
+    per-wave timestamps, and each XCD's share is scaled by the mean loop
+    time over its own (two rounds), so that the XCDs end their reads
+    together.  The plan is then rebuilt with those shares
+    (bt_grouped_plan_xcd); the outputs do not change.  Returns the shares
+    (permille per XCD), or None where this does not apply."""
+    import ctypes
+    path = os.path.join(os.path.dirname(bt.LIB_PATH), "libbt_timing.so")
+    host = ws.plan.host
+    hdr = host[16:16 + 8 * 12].view(np.int64)
+    kind = int(host[12:16].view(np.int32)[0])
+    W = int(hdr[11])
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    if ws.mode != "grouped" or kind != 0 or W != 8 * cus or \
+            not os.path.exists(path):
+        return None
+    V = ctypes.c_void_p
+    T = ctypes.CDLL(path)
+    T.bt_gemm_grouped.argtypes = [V, V, V]
+    T.bt_gemm_grouped.restype = ctypes.c_int32
+    T.bt_wave_timestamps.argtypes = [V, V]
+    T.bt_wave_timestamps.restype = ctypes.c_int32
+    stream = torch.cuda.current_stream().cuda_stream
+    nx = 8
+    shares = np.array([1000 if x % 2 == 0 else 900 for x in range(nx)],
+                      np.float64)
+    plan = ws.plan
+    for _ in range(rounds):
+        loops = []
+        settle(torch, ws.product, ms=20.0)
+        for _ in range(launches):
+            for _ in range(3):
+                if T.bt_gemm_grouped(plan.dev.data_ptr(), plan.host.ctypes.data,
+                                     stream) != 0:
+                    raise RuntimeError("timing build launch failed")
+            torch.cuda.synchronize()
+            ts = np.zeros((4096, 8), np.uint64)
+            hw = np.zeros((4096, 2), np.uint32)
+            if T.bt_wave_timestamps(ts.ctypes.data, hw.ctypes.data) != 0:
+                raise RuntimeError("bt_wave_timestamps failed")
+            ts = ts[:W].astype(np.int64)
+            xcd = _hw_xcd(hw[:W])
+            loop = (ts[:, 3] - ts[:, 1]).astype(np.float64)
+            if set(np.unique(xcd)) != set(range(nx)):
+                return None
+            loops.append([loop[xcd == x].mean() for x in range(nx)])
+        lx = np.median(np.array(loops), axis=0)
+        shares = np.clip(shares * lx.mean() / lx, 500, 2000)
+        plan = bt.bt_grouped_plan(ws.problems, xcd_shares=np.rint(shares))
+    ws.plan = plan
+    return [int(v) for v in np.rint(shares)]
+
+
 def wave_timeline(ws: WorkSet, torch, bt, launches=8):
     """Per-wave timestamps of the streaming product launch and of the read
     probe over the same bytes, from the timing build (libbt_timing.so,
@@ -919,6 +975,9 @@ def main():
                     help="instead of the benchmark line, print where a "
                          "streaming launch's time goes (ramp, steady, drain) "
                          "from the timing build's per-wave timestamps")
+    ap.add_argument("--calibrate-xcd", action="store_true",
+                    help="time the M=1 streaming plans with per-XCD shares "
+                         "measured on this GPU (bt_grouped_plan_xcd)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one plain 256 MiB device copy, so that a "
                          "counter run can scale FETCH_SIZE / WRITE_SIZE")
@@ -954,6 +1013,8 @@ def main():
         f"{work.weight_bytes() / 1e6:.1f} MB packed weights")
     ps = PackedSet(work, torch, bt, keep_layers=2 if work.layers > 1 else 1)
     ws = WorkSet(work, ps, torch, bt, args.mode)
+    xcd_shares = (calibrate_xcd_shares(ws, torch, bt) if args.calibrate_xcd
+                  else None)
     wall, kern_avg = run_timed(ws, args.steps, args.warmup, torch)
     ms_step = wall / args.steps * 1e3
     step_bytes = ws.product_bytes() + ws.quant_bytes()
@@ -998,6 +1059,7 @@ def main():
                    "weight_bytes": ws.weight_bytes(),
                    "launch": args.mode,
                    "settle_ms": SETTLE_MS,
+                   "xcd_shares": xcd_shares,
                    "product_kernel_ms": round(kern_avg, 5),
                    "tokens_per_s_equiv": round(work.m / (ms_step * 1e-3), 1),
                    "tops": round(ws.ops() / (kern_avg * 1e-3) / 1e12, 3)},
@@ -1080,8 +1142,12 @@ def main():
             d8 = {}
             for m in (1, 64):
                 ws8 = WorkSet(wl.decode_8b(m), ps8, torch, bt)
+                sh8 = (calibrate_xcd_shares(ws8, torch, bt)
+                       if args.calibrate_xcd else None)
                 d8[f"m{m}"] = config_entry(ws8, torch, 20, 3, ceiling["gb_s"],
                                            cpu_seconds=cpu_s, ps=ps8)
+                if sh8 is not None:
+                    d8[f"m{m}"]["xcd_shares"] = sh8
                 if m == 1:
                     d8["m1"]["fused_step"] = fused_entry(
                         wl.decode_8b(1), ps8, torch, bt, 20, 3,

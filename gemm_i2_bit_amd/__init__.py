@@ -4,7 +4,8 @@ library's HIP kernels.  PyTorch supplies device memory and streams.
 
 Functions carry the C ABI's names (see include/bt.h for the contract):
 bt_pack_i2s, bt_quant_act, bt_quant_act_many, bt_gemv, bt_gemm,
-bt_grouped_plan, bt_grouped_plan_f32, bt_gemm_grouped, bt_packed_bytes,
+bt_grouped_plan (and bt_grouped_plan_xcd through its xcd_shares argument),
+bt_grouped_plan_f32, bt_gemm_grouped, bt_packed_bytes,
 bt_status_str, and the measurement helpers bt_read_probe and bt_mix_probe.
 """
 from __future__ import annotations
@@ -99,6 +100,8 @@ def lib() -> ctypes.CDLL:
         L.bt_grouped_plan_bytes.restype = i64
         L.bt_grouped_plan.argtypes = [p, i32, p, i64]
         L.bt_grouped_plan.restype = i32
+        L.bt_grouped_plan_xcd.argtypes = [p, i32, p, i32, p, i64]
+        L.bt_grouped_plan_xcd.restype = i32
         L.bt_grouped_plan_f32_bytes.argtypes = [p, i32]
         L.bt_grouped_plan_f32_bytes.restype = i64
         L.bt_grouped_plan_f32.argtypes = [p, i32, p, i64]
@@ -380,9 +383,10 @@ class GroupedPlan:
         self._tensors = tensors
 
 
-def bt_grouped_plan(problems, device=None) -> GroupedPlan:
+def bt_grouped_plan(problems, device=None, xcd_shares=None) -> GroupedPlan:
     """problems: list of dicts with packed, s_w, n, k, x_q, s_a, y and
-    optionally acc (GPU tensors; every problem has the same m)."""
+    optionally acc (GPU tensors; every problem has the same m).  xcd_shares:
+    optional per-XCD shares in permille (bt_grouped_plan_xcd)."""
     torch = _torch()
     arr = (bt_problem * len(problems))()
     keep = []
@@ -405,8 +409,14 @@ def bt_grouped_plan(problems, device=None) -> GroupedPlan:
     if nbytes < 0:
         raise BtError(nbytes, "bt_grouped_plan_bytes")
     host = np.zeros(nbytes, np.uint8)
-    _check(lib().bt_grouped_plan(arr, len(problems), host.ctypes.data,
-                                 nbytes), "bt_grouped_plan")
+    if xcd_shares is None:
+        _check(lib().bt_grouped_plan(arr, len(problems), host.ctypes.data,
+                                     nbytes), "bt_grouped_plan")
+    else:
+        sh = np.ascontiguousarray(xcd_shares, dtype=np.int32)
+        _check(lib().bt_grouped_plan_xcd(arr, len(problems), sh.ctypes.data,
+                                         sh.size, host.ctypes.data, nbytes),
+               "bt_grouped_plan_xcd")
     if device is None:
         device = problems[0]["x_q"].device
     dev = torch.from_numpy(host).to(device)

@@ -178,6 +178,7 @@ std::vector<Split> plan_splits(const bt_problem* probs, int32_t count,
 // 41.1-44.5 us in the plain order; the ranges first or in the second round
 // were in between or slower.  Without a device the plain order stays.
 constexpr int kXcds = 8;
+constexpr int32_t kMaxXcdShares = 32;  // XCDs a share table may list
 constexpr int64_t kXcdOrderMinUnits = 1024;
 std::vector<Unit> plan_units(const bt_problem* probs, int32_t count, int m,
                              int kind, const std::vector<Split>& split,
@@ -454,13 +455,22 @@ __global__ __launch_bounds__(256) void zero_kernel(uint4* p, int64_t words) {
 // against 275 us on the 8B set (both weights swept over 0.82-0.92; fused
 // plans 88.2 against 90.4 us and 269.9 against 276.8 us).  The outputs do
 // not depend on the split.
-std::vector<int64_t> wave_shares(int64_t W, int wpw, bool full, int xccs) {
+// A caller may give its own per-XCD shares (permille, one per XCD of the
+// device, from a measurement on the GPU the plan runs on): they replace the
+// odd-XCD rule.
+std::vector<int64_t> wave_shares(int64_t W, int wpw, bool full, int xccs,
+                                 const int32_t* xcd_share = nullptr,
+                                 int32_t nxcd = 0) {
   std::vector<int64_t> wt(W, 1000);
   if (!full) return wt;
+  const bool own = xcd_share != nullptr && nxcd == xccs && xccs > 0;
   for (int64_t w = 0; w < W; ++w) {
     if (wpw == 8 && w % 8 >= 4) wt[w] = wt[w] * 87 / 100;
     if (wpw == 4 && w >= W / 2) wt[w] = wt[w] * 9 / 10;
-    if (xccs == 8 && (w / wpw) % 2 == 1) wt[w] = wt[w] * 9 / 10;
+    if (own)
+      wt[w] = wt[w] * xcd_share[(w / wpw) % xccs] / 1000;
+    else if (xccs == 8 && (w / wpw) % 2 == 1)
+      wt[w] = wt[w] * 9 / 10;
   }
   return wt;
 }
@@ -680,7 +690,9 @@ int64_t bt_grouped_plan_bytes(const bt_problem* probs, int32_t count) {
 static int32_t build_plan(const bt_problem* probs, int32_t count, void* plan,
                           int64_t plan_bytes, const float* const* xf,
                           const float* const* g = nullptr,
-                          const float* eps = nullptr) {
+                          const float* eps = nullptr,
+                          const int32_t* xcd_share = nullptr,
+                          int32_t nxcd = 0) {
   if (!plan) return BT_E_NULL;
   const bool fused = xf != nullptr;
   const int32_t st = check_group(probs, count, fused);
@@ -741,7 +753,7 @@ static int32_t build_plan(const bt_problem* probs, int32_t count, void* plan,
   // of 4 for fused plans
   const bool full = cus > 0 && W == 8 * (int64_t)cus;
   const std::vector<int64_t> wt =
-      wave_shares(W, fused ? 4 : 8, full, xcc_count());
+      wave_shares(W, fused ? 4 : 8, full, xcc_count(), xcd_share, nxcd);
   const std::vector<int64_t> b = W <= 0 ? std::vector<int64_t>()
                                  : fused && full
                                      ? bounds_by_cost(probs, count, T, wt)
@@ -777,6 +789,17 @@ static int32_t build_plan(const bt_problem* probs, int32_t count, void* plan,
 int32_t bt_grouped_plan(const bt_problem* probs, int32_t count, void* plan,
                         int64_t plan_bytes) {
   return build_plan(probs, count, plan, plan_bytes, nullptr);
+}
+
+int32_t bt_grouped_plan_xcd(const bt_problem* probs, int32_t count,
+                            const int32_t* xcd_permille, int32_t nxcd,
+                            void* plan, int64_t plan_bytes) {
+  if (!xcd_permille) return BT_E_NULL;
+  if (nxcd < 1 || nxcd > kMaxXcdShares) return BT_E_ARG;
+  for (int32_t x = 0; x < nxcd; ++x)
+    if (xcd_permille[x] < 500 || xcd_permille[x] > 2000) return BT_E_ARG;
+  return build_plan(probs, count, plan, plan_bytes, nullptr, nullptr, nullptr,
+                    xcd_permille, nxcd);
 }
 
 // The fp32-activation problems as bt_problem (x in the x_q and s_a slots,

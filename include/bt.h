@@ -189,6 +189,24 @@ int32_t bt_grouped_plan(const bt_problem* probs, int32_t count, void* plan,
 int32_t bt_gemm_grouped(void* plan_dev, const void* plan_host,
                         void* stream);
 
+/* bt_grouped_plan with the caller's own per-XCD shares.  A launch whose
+ * grid fills the GPU streams each wave's contiguous range of the weights,
+ * and the XCDs (each with its own L2 and path to memory; workgroup g runs
+ * on XCD g mod nxcd) do not stream equally fast: by default odd XCDs take
+ * 0.9 of a share.  Rates measured on the GPU the plan runs on (per-wave
+ * timestamps of the timing build, include/bt_timing.h) can be given
+ * instead: XCD x's waves then take xcd_permille[x] / 1000 of a share, so
+ * that every XCD ends its reads at the same time.  The split changes no
+ * output bit.  Shares apply to streaming plans on a full grid of a device
+ * with nxcd XCDs and are ignored otherwise (the plan is then that of
+ * bt_grouped_plan).  Sizes as bt_grouped_plan_bytes.
+ *  xcd_permille  host int32 [nxcd], each in [500, 2000], else BT_E_ARG;
+ *                NULL gives BT_E_NULL.
+ *  nxcd          1 to 32, else BT_E_ARG. */
+int32_t bt_grouped_plan_xcd(const bt_problem* probs, int32_t count,
+                            const int32_t* xcd_permille, int32_t nxcd,
+                            void* plan, int64_t plan_bytes);
+
 /* bt_gemm_grouped for callers that cannot allocate device memory (code
  * under HIP graph capture, tight serving loops, harnesses that forbid
  * hipMalloc): the same launch over the same plan, with the same results bit

@@ -371,6 +371,31 @@ def test_grouped_plan_errors(L):
     assert L.bt_gemm_grouped(P + 16, img.ctypes.data, None) == bt.BT_E_ALIGN
 
 
+def test_grouped_plan_xcd_errors_and_default(L):
+    good = problems([(2560, 2560, 1), (640, 2560, 1)])
+    nbytes = L.bt_grouped_plan_bytes(good, 2)
+    img = np.zeros(nbytes, np.uint8)
+    g = L.bt_grouped_plan_xcd
+    sh = np.full(8, 1000, np.int32)
+    assert g(good, 2, None, 8, img.ctypes.data, nbytes) == bt.BT_E_NULL
+    for n in (0, -1, 33):
+        assert g(good, 2, sh.ctypes.data, n, img.ctypes.data,
+                 nbytes) == bt.BT_E_ARG, n
+    for bad in (499, 2001, 0, -1000):
+        b = sh.copy()
+        b[5] = bad
+        assert g(good, 2, b.ctypes.data, 8, img.ctypes.data,
+                 nbytes) == bt.BT_E_ARG, bad
+    assert g(good, 2, sh.ctypes.data, 8, img.ctypes.data,
+             nbytes - 1) == bt.BT_E_ARG
+    # with no device (no full grid) the shares are ignored: the image is
+    # bt_grouped_plan's, byte for byte
+    assert g(good, 2, sh.ctypes.data, 8, img.ctypes.data, nbytes) == 0
+    ref = np.zeros(nbytes, np.uint8)
+    assert L.bt_grouped_plan(good, 2, ref.ctypes.data, nbytes) == 0
+    assert np.array_equal(img, ref)
+
+
 def test_binding_rejects_host_tensors(L):
     torch = pytest.importorskip("torch")
     t = torch.zeros((64, 64), dtype=torch.int8)

@@ -1069,6 +1069,48 @@ def test_prefill_layer_grouped(prefill_layer):
     launch_and_check(plan, probs, outs, refs, launches=3)
 
 
+def test_grouped_plan_xcd_shares_same_outputs():
+    """A full-grid streaming plan with the caller's per-XCD shares
+    (bt_grouped_plan_xcd): the waves' ranges follow the shares (each XCD's
+    chunks in proportion), and the outputs are bit-identical to the default
+    plan's."""
+    work = wl.decode_2b(1)
+    probs = []
+    rng = np.random.default_rng(116)
+    for pr in work.problems()[:4 * 7]:  # four layers, 69 MB of weights
+        n, k = pr.n, pr.k
+        t = rng.integers(-1, 2, size=(n, k), dtype=np.int8)
+        packed = bt.bt_pack_i2s(dev(t))
+        xq = dev(rng.integers(-127, 128, size=(1, k), dtype=np.int8))
+        sa = dev(np.array([0.01], np.float32))
+        y = torch.empty((1, n), dtype=torch.float32, device="cuda:0")
+        probs.append(dict(packed=packed, s_w=0.02, n=n, k=k, x_q=xq,
+                          s_a=sa, y=y))
+    base = bt.bt_grouped_plan(probs)
+    shares = [1100, 800, 1000, 950, 1000, 900, 1200, 850]
+    tuned = bt.bt_grouped_plan(probs, xcd_shares=shares)
+    h = plan_header(tuned.host)
+    W = h["start_waves"]
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    assert W == 8 * cus
+    tab = tuned.host[h["start_off"]:h["start_off"] + W * 128].reshape(W, 128)
+    lo, hi = tab.view(np.int64)[:, 3], tab.view(np.int64)[:, 4]
+    xcd = (np.arange(W) // 8) % 8
+    per = np.array([(hi - lo)[xcd == x].sum() for x in range(8)], np.float64)
+    want = np.array(shares, np.float64)
+    np.testing.assert_allclose(per / per.sum(), want / want.sum(), rtol=0.01)
+    ys = []
+    for plan in (base, tuned, base, tuned):
+        for p in probs:
+            p["y"].fill_(float("nan"))
+        bt.bt_gemm_grouped(plan)
+        torch.cuda.synchronize()
+        ys.append(torch.cat([p["y"].flatten() for p in probs]).clone())
+    for y in ys[1:]:
+        assert torch.equal(y.view(torch.int32), ys[0].view(torch.int32))
+    assert not torch.isnan(ys[0]).any()
+
+
 def check_prefill_order(plan):
     """A prefill plan with more units than CUs but at most two per CU puts
     the ranges of split reductions at the end of the first round (the units
